@@ -1,0 +1,1 @@
+"""LinearARD attention-relation KL on MI355X (gfx950): HIP kernels behind a C-ABI."""
