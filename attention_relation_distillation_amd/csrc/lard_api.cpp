@@ -1,0 +1,222 @@
+// C ABI of the relation-KL library: host-side validation, workspace sizing and launch
+// configuration.  Every check runs before the first HIP call, so an invalid request never
+// touches the device.  The operation itself is documented in include/lard.h.
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "lard.h"
+#include "relkl_internal.h"
+
+namespace {
+
+using namespace lard;
+
+constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+constexpr int kTargetWorkgroups = 512;  // two waves of workgroups over 256 CUs
+constexpr int kMaxSplits = 64;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int elem_size(int dtype) { return dtype == LARD_BF16 ? 2 : 4; }
+
+lard_status check_strides(int dtype, int64_t sb, int64_t sh, int64_t sn) {
+  const int64_t q = 16 / elem_size(dtype);
+  if (sb < 0 || sh < 0 || sn < 0) return LARD_ERR_INVALID_ARGUMENT;
+  if (sb % q || sh % q || sn % q) return LARD_ERR_INVALID_ARGUMENT;
+  return LARD_OK;
+}
+
+lard_status check_desc(const lard_relkl_desc* d) {
+  if (!d) return LARD_ERR_INVALID_ARGUMENT;
+  if (d->dtype != LARD_FP32 && d->dtype != LARD_BF16) return LARD_ERR_INVALID_ARGUMENT;
+  if (d->B < 1 || d->H_in < 1 || d->N < 1 || d->d < 1) return LARD_ERR_INVALID_ARGUMENT;
+  if (d->d != 64 && d->d != 128) return LARD_ERR_UNSUPPORTED;
+  if (d->causal != 0 && d->causal != 1) return LARD_ERR_INVALID_ARGUMENT;
+  if (!(d->scale > 0.0f) || !isfinite(d->scale)) return LARD_ERR_INVALID_ARGUMENT;
+  if (d->H < 1) return LARD_ERR_INVALID_ARGUMENT;
+  if (d->H > LARD_MAX_HEADS) return LARD_ERR_UNSUPPORTED;
+  lard_status s = check_strides(d->dtype, d->t_stride_b, d->t_stride_h, d->t_stride_n);
+  if (s != LARD_OK) return s;
+  s = check_strides(d->dtype, d->s_stride_b, d->s_stride_h, d->s_stride_n);
+  if (s != LARD_OK) return s;
+  // rows must not overlap inside one head (stride over n at least one row of d)
+  if (d->N > 1 && (d->t_stride_n < d->d || d->s_stride_n < d->d)) return LARD_ERR_INVALID_ARGUMENT;
+  if (d->head_map == nullptr) {
+    if (d->H != d->H_in) return LARD_ERR_INVALID_ARGUMENT;
+  } else {
+    bool seen[LARD_MAX_HEADS * 4];
+    if (d->H_in > LARD_MAX_HEADS * 4) return LARD_ERR_UNSUPPORTED;
+    memset(seen, 0, sizeof(seen));
+    for (int h = 0; h < d->H; ++h) {
+      const int32_t v = d->head_map[h];
+      if (v < 0 || v >= d->H_in) return LARD_ERR_INVALID_ARGUMENT;
+      if (seen[v]) return LARD_ERR_INVALID_ARGUMENT;
+      seen[v] = true;
+    }
+  }
+  // 32-bit work indices
+  const int64_t units = (int64_t)d->B * d->H;
+  const int64_t row_tiles = (d->N + kBR - 1) / kBR;
+  if (units * row_tiles * kMaxSplits > 0x7fffffffLL) return LARD_ERR_UNSUPPORTED;
+  if ((int64_t)units * d->N > 0x7fffffffLL * 4LL) return LARD_ERR_UNSUPPORTED;
+  return LARD_OK;
+}
+
+void fill_map(UnitMap& m, const lard_relkl_desc* d) {
+  for (int h = 0; h < d->H; ++h) m.head_map[h] = d->head_map ? d->head_map[h] : h;
+  for (int h = d->H; h < LARD_MAX_HEADS; ++h) m.head_map[h] = 0;
+}
+
+int row_tiles_of(const lard_relkl_desc* d) { return (d->N + kBR - 1) / kBR; }
+int key_tiles_of(const lard_relkl_desc* d) { return (d->N + kBC - 1) / kBC; }
+
+// Split the key range of the backward when the (unit, row tile) grid alone cannot fill
+// the chip.  Deterministic in the shape; LARD_SPLITK overrides it (clamped).
+int choose_splits(const lard_relkl_desc* d) {
+  const int64_t base = (int64_t)d->B * d->H * row_tiles_of(d);
+  const int kt = key_tiles_of(d);
+  int s = 1;
+  if (base < kTargetWorkgroups) s = (int)((kTargetWorkgroups + base - 1) / base);
+  const char* env = getenv("LARD_SPLITK");
+  if (env && env[0]) {
+    const int v = atoi(env);
+    if (v >= 1) s = v;
+  }
+  if (s > kt) s = kt;
+  if (s > kMaxSplits) s = kMaxSplits;
+  if (s < 1) s = 1;
+  return s;
+}
+
+size_t fwd_workspace(const lard_relkl_desc* d) {
+  const size_t n = (size_t)d->B * d->H * row_tiles_of(d);
+  return ((n * sizeof(double) + 255) / 256) * 256;
+}
+
+size_t bwd_workspace(const lard_relkl_desc* d) {
+  const int s = choose_splits(d);
+  if (s == 1) return 0;
+  return (size_t)s * d->B * d->H * (size_t)row_tiles_of(d) * kBR * d->d * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lard_status_string(lard_status status) {
+  switch (status) {
+    case LARD_OK: return "LARD_OK: success";
+    case LARD_ERR_INVALID_ARGUMENT: return "LARD_ERR_INVALID_ARGUMENT: invalid argument";
+    case LARD_ERR_UNSUPPORTED: return "LARD_ERR_UNSUPPORTED: unsupported configuration";
+    case LARD_ERR_WORKSPACE_TOO_SMALL: return "LARD_ERR_WORKSPACE_TOO_SMALL: workspace too small";
+    case LARD_ERR_HIP: return "LARD_ERR_HIP: HIP launch or runtime error";
+  }
+  return "unknown lard_status";
+}
+
+int lard_version(void) { return kVersion; }
+
+size_t lard_relkl_workspace_size(const lard_relkl_desc* desc, int pass, lard_status* status) {
+  lard_status s = check_desc(desc);
+  if (s == LARD_OK && pass != 0 && pass != 1) s = LARD_ERR_INVALID_ARGUMENT;
+  if (status) *status = s;
+  if (s != LARD_OK) return 0;
+  return pass == 0 ? fwd_workspace(desc) : bwd_workspace(desc);
+}
+
+lard_status lard_relkl_fwd(const lard_relkl_desc* desc, const void* x_teacher,
+                           const void* x_student, float* lse_teacher, float* lse_student,
+                           float* row_kl, float* loss, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  lard_status s = check_desc(desc);
+  if (s != LARD_OK) return s;
+  if (!x_teacher || !x_student || !lse_teacher || !lse_student || !loss || !workspace)
+    return LARD_ERR_INVALID_ARGUMENT;
+  if (!aligned(x_teacher, 16) || !aligned(x_student, 16) || !aligned(workspace, 8) ||
+      !aligned(lse_teacher, 4) || !aligned(lse_student, 4) || !aligned(loss, 4) ||
+      (row_kl && !aligned(row_kl, 4)))
+    return LARD_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < fwd_workspace(desc)) return LARD_ERR_WORKSPACE_TOO_SMALL;
+
+  FwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.x_t = x_teacher;
+  a.x_s = x_student;
+  a.t_sb = desc->t_stride_b; a.t_sh = desc->t_stride_h; a.t_sn = desc->t_stride_n;
+  a.s_sb = desc->s_stride_b; a.s_sh = desc->s_stride_h; a.s_sn = desc->s_stride_n;
+  a.B = desc->B; a.H = desc->H; a.N = desc->N;
+  a.row_tiles = row_tiles_of(desc);
+  a.scale = desc->scale;
+  a.c2 = desc->scale * 1.4426950408889634f;
+  a.lse_t = lse_teacher;
+  a.lse_s = lse_student;
+  a.row_kl = row_kl;
+  a.partial = static_cast<double*>(workspace);
+  fill_map(a.map, desc);
+  const int e = launch_fwd(a, desc->dtype == LARD_BF16, desc->d, desc->causal == 1, loss, stream);
+  return e == 0 ? LARD_OK : LARD_ERR_HIP;
+}
+
+lard_status lard_relkl_bwd(const lard_relkl_desc* desc, const void* x_teacher,
+                           const void* x_student, const float* lse_teacher,
+                           const float* lse_student, const float* grad_loss,
+                           const lard_grad_desc* grad, void* dx_student, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  lard_status s = check_desc(desc);
+  if (s != LARD_OK) return s;
+  if (!grad || !x_teacher || !x_student || !lse_teacher || !lse_student || !grad_loss ||
+      !dx_student)
+    return LARD_ERR_INVALID_ARGUMENT;
+  if (grad->dtype != LARD_FP32 && grad->dtype != LARD_BF16) return LARD_ERR_INVALID_ARGUMENT;
+  if (grad->dtype == LARD_BF16 && desc->dtype != LARD_BF16) return LARD_ERR_UNSUPPORTED;
+  s = check_strides(grad->dtype, grad->stride_b, grad->stride_h, grad->stride_n);
+  if (s != LARD_OK) return s;
+  if (desc->N > 1 && grad->stride_n < desc->d) return LARD_ERR_INVALID_ARGUMENT;
+  if (!aligned(x_teacher, 16) || !aligned(x_student, 16) || !aligned(dx_student, 16) ||
+      !aligned(lse_teacher, 4) || !aligned(lse_student, 4) || !aligned(grad_loss, 4))
+    return LARD_ERR_INVALID_ARGUMENT;
+  const size_t need = bwd_workspace(desc);
+  if (need > 0 && (!workspace || !aligned(workspace, 16))) return LARD_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < need) return LARD_ERR_WORKSPACE_TOO_SMALL;
+
+  BwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.x_t = x_teacher;
+  a.x_s = x_student;
+  a.t_sb = desc->t_stride_b; a.t_sh = desc->t_stride_h; a.t_sn = desc->t_stride_n;
+  a.s_sb = desc->s_stride_b; a.s_sh = desc->s_stride_h; a.s_sn = desc->s_stride_n;
+  a.g_sb = grad->stride_b; a.g_sh = grad->stride_h; a.g_sn = grad->stride_n;
+  a.B = desc->B; a.H = desc->H; a.N = desc->N;
+  a.row_tiles = row_tiles_of(desc);
+  a.key_tiles = key_tiles_of(desc);
+  a.splits = choose_splits(desc);
+  a.scale = desc->scale;
+  a.c2 = desc->scale * 1.4426950408889634f;
+  a.lse_t = lse_teacher;
+  a.lse_s = lse_student;
+  a.grad_loss = grad_loss;
+  a.dx = dx_student;
+  a.partial = static_cast<float*>(workspace);
+  fill_map(a.map, desc);
+  const bool out_f32 = grad->dtype == LARD_FP32;
+  int e = launch_bwd(a, desc->dtype == LARD_BF16, desc->d, desc->causal == 1, out_f32, stream);
+  if (e != 0) return LARD_ERR_HIP;
+  if (a.splits > 1) {
+    ReduceArgs r;
+    memset(&r, 0, sizeof(r));
+    r.partial = a.partial;
+    r.dx = dx_student;
+    r.g_sb = a.g_sb; r.g_sh = a.g_sh; r.g_sn = a.g_sn;
+    r.B = a.B; r.H = a.H; r.N = a.N; r.d = desc->d;
+    r.rows_pad = a.row_tiles * kBR;
+    r.splits = a.splits;
+    r.map = a.map;
+    e = launch_splitk_reduce(r, out_f32, true, stream);
+    if (e != 0) return LARD_ERR_HIP;
+  }
+  return LARD_OK;
+}
+
+}  // extern "C"

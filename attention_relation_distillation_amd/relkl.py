@@ -1,0 +1,246 @@
+"""Python binding of the relation-KL C ABI (include/lard.h).
+
+Argument marshalling only: output buffers and the workspace come from PyTorch's caching
+allocator, the stream is PyTorch's current stream, and every arithmetic step runs in the
+HIP kernels of liblard.so.  There is no CPU fallback: without the built library or a GPU
+these functions raise.
+
+    loss = relation_kl(x_t, x_s, causal=True)          # sum over rows, heads, batch
+    loss.backward()                                      # gradient reaches x_s only
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+__all__ = ["LardError", "library_path", "load_library", "relkl_fwd", "relkl_bwd",
+           "relation_kl", "workspace_size", "LARD_MAX_HEADS"]
+
+LARD_FP32 = 0
+LARD_BF16 = 1
+LARD_MAX_HEADS = 256
+_STATUS_NAMES = {0: "LARD_OK", 1: "LARD_ERR_INVALID_ARGUMENT", 2: "LARD_ERR_UNSUPPORTED",
+                 3: "LARD_ERR_WORKSPACE_TOO_SMALL", 4: "LARD_ERR_HIP"}
+
+
+class LardError(RuntimeError):
+    """A non-zero lard_status returned by the library."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class _Desc(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32),
+        ("B", ctypes.c_int32), ("H_in", ctypes.c_int32), ("N", ctypes.c_int32),
+        ("d", ctypes.c_int32),
+        ("t_stride_b", ctypes.c_int64), ("t_stride_h", ctypes.c_int64),
+        ("t_stride_n", ctypes.c_int64),
+        ("s_stride_b", ctypes.c_int64), ("s_stride_h", ctypes.c_int64),
+        ("s_stride_n", ctypes.c_int64),
+        ("H", ctypes.c_int32), ("causal", ctypes.c_int32),
+        ("head_map", ctypes.POINTER(ctypes.c_int32)),
+        ("scale", ctypes.c_float),
+    ]
+
+
+class _GradDesc(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64),
+        ("stride_n", ctypes.c_int64),
+    ]
+
+
+_LIB = None
+
+
+def library_path() -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblard.so")
+
+
+def load_library():
+    """Load liblard.so (built in-tree by ``__graft_entry__.build()``); raises if absent."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"HIP library {path} is not built; run __graft_entry__.build() "
+                           "(python -m attention_relation_distillation_amd.build)")
+    lib = ctypes.CDLL(path)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    lib.lard_relkl_workspace_size.restype = sz
+    lib.lard_relkl_workspace_size.argtypes = [ctypes.POINTER(_Desc), ctypes.c_int,
+                                              ctypes.POINTER(ctypes.c_int)]
+    lib.lard_relkl_fwd.restype = ctypes.c_int
+    lib.lard_relkl_fwd.argtypes = [ctypes.POINTER(_Desc), vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.lard_relkl_bwd.restype = ctypes.c_int
+    lib.lard_relkl_bwd.argtypes = [ctypes.POINTER(_Desc), vp, vp, vp, vp, vp,
+                                   ctypes.POINTER(_GradDesc), vp, vp, sz, vp]
+    lib.lard_status_string.restype = ctypes.c_char_p
+    lib.lard_status_string.argtypes = [ctypes.c_int]
+    lib.lard_version.restype = ctypes.c_int
+    lib.lard_version.argtypes = []
+    _LIB = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        msg = load_library().lard_status_string(status).decode()
+        raise LardError(status, msg)
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return LARD_BF16
+    if t == torch.float32:
+        return LARD_FP32
+    raise LardError(2, f"unsupported dtype {t} (bfloat16 or float32)")
+
+
+def _make_desc(x_t: torch.Tensor, x_s: torch.Tensor, causal: bool, scale: Optional[float],
+               head_map: Optional[Sequence[int]]):
+    if x_t.dim() != 4 or x_s.dim() != 4:
+        raise LardError(1, "inputs must be [B, H, N, d]")
+    if x_t.shape != x_s.shape or x_t.dtype != x_s.dtype:
+        raise LardError(1, "teacher and student must have the same shape and dtype")
+    if x_t.device != x_s.device:
+        raise LardError(1, "teacher and student must be on the same device")
+    if x_t.stride(-1) != 1 or x_s.stride(-1) != 1:
+        raise LardError(1, "the last dimension (d) must be contiguous")
+    b, h_in, n, d = x_t.shape
+    keep = []
+    if head_map is not None:
+        arr = (ctypes.c_int32 * len(head_map))(*[int(v) for v in head_map])
+        keep.append(arr)
+        hm_ptr = ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32))
+        h = len(head_map)
+    else:
+        hm_ptr = ctypes.POINTER(ctypes.c_int32)()
+        h = h_in
+    if scale is None:
+        scale = float(torch.tensor(d ** -0.5, dtype=torch.float32).item())
+    desc = _Desc(dtype=_dtype_code(x_t.dtype), B=b, H_in=h_in, N=n, d=d,
+                 t_stride_b=x_t.stride(0), t_stride_h=x_t.stride(1), t_stride_n=x_t.stride(2),
+                 s_stride_b=x_s.stride(0), s_stride_h=x_s.stride(1), s_stride_n=x_s.stride(2),
+                 H=h, causal=1 if causal else 0, head_map=hm_ptr, scale=scale)
+    return desc, keep
+
+
+def _stream_handle(dev: torch.device, stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream(dev) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _require_gpu(x: torch.Tensor):
+    if x.device.type != "cuda":
+        raise RuntimeError("the relation-KL library runs on a ROCm GPU only; got a tensor on "
+                           f"{x.device}")
+
+
+def workspace_size(x_t, x_s, *, causal=True, scale=None, head_map=None, pass_: int = 0) -> int:
+    lib = load_library()
+    desc, _keep = _make_desc(x_t, x_s, causal, scale, head_map)
+    st = ctypes.c_int(0)
+    n = lib.lard_relkl_workspace_size(ctypes.byref(desc), pass_, ctypes.byref(st))
+    _check(st.value)
+    return int(n)
+
+
+def relkl_fwd(x_t: torch.Tensor, x_s: torch.Tensor, *, causal: bool = True,
+              scale: Optional[float] = None, head_map: Optional[Sequence[int]] = None,
+              want_row_kl: bool = False, stream=None):
+    """Forward: returns dict(loss: 0-d fp32, lse_t, lse_s: fp32 [B, H, N], row_kl or None)."""
+    lib = load_library()
+    desc, keep = _make_desc(x_t, x_s, causal, scale, head_map)
+    _require_gpu(x_t)
+    b, n = desc.B, desc.N
+    dev = x_t.device
+    lse_t = torch.empty((b, desc.H, n), dtype=torch.float32, device=dev)
+    lse_s = torch.empty((b, desc.H, n), dtype=torch.float32, device=dev)
+    row_kl = torch.empty((b, desc.H, n), dtype=torch.float32, device=dev) if want_row_kl else None
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    st = ctypes.c_int(0)
+    ws_bytes = lib.lard_relkl_workspace_size(ctypes.byref(desc), 0, ctypes.byref(st))
+    _check(st.value)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    _check(lib.lard_relkl_fwd(ctypes.byref(desc), x_t.data_ptr(), x_s.data_ptr(),
+                              lse_t.data_ptr(), lse_s.data_ptr(),
+                              row_kl.data_ptr() if row_kl is not None else None,
+                              loss.data_ptr(), ws.data_ptr(), ws.numel(),
+                              _stream_handle(dev, stream)))
+    del keep
+    return {"loss": loss, "lse_t": lse_t, "lse_s": lse_s, "row_kl": row_kl}
+
+
+def relkl_bwd(x_t: torch.Tensor, x_s: torch.Tensor, lse_t: torch.Tensor, lse_s: torch.Tensor,
+              grad_loss: torch.Tensor, *, causal: bool = True, scale: Optional[float] = None,
+              head_map: Optional[Sequence[int]] = None, dx: Optional[torch.Tensor] = None,
+              dx_dtype: Optional[torch.dtype] = None, stream=None) -> torch.Tensor:
+    """Backward: gradient of grad_loss * loss with respect to x_s (teacher is frozen).
+
+    dx (optional) receives the result; heads outside head_map are left untouched.  A new
+    dx is zero-filled when head_map selects a subset of heads.
+    """
+    lib = load_library()
+    desc, keep = _make_desc(x_t, x_s, causal, scale, head_map)
+    _require_gpu(x_t)
+    dev = x_t.device
+    for t, name in ((lse_t, "lse_t"), (lse_s, "lse_s")):
+        if (t.dtype != torch.float32 or not t.is_contiguous() or t.device != dev
+                or tuple(t.shape) != (desc.B, desc.H, desc.N)):
+            raise LardError(1, f"{name} must be contiguous fp32 [B, H, N] on {dev}")
+    if (grad_loss.dtype != torch.float32 or grad_loss.numel() != 1 or grad_loss.device != dev):
+        raise LardError(1, "grad_loss must be a one-element fp32 tensor on the inputs' device")
+    grad_loss = grad_loss.contiguous()
+    if dx is None:
+        out_dtype = x_s.dtype if dx_dtype is None else dx_dtype
+        subset = head_map is not None and sorted(int(v) for v in head_map) != list(range(desc.H_in))
+        dx = (torch.zeros if subset else torch.empty)(x_s.shape, dtype=out_dtype, device=dev)
+    if dx.shape != x_s.shape or dx.stride(-1) != 1 or dx.device != dev:
+        raise LardError(1, "dx must match x_s in shape, with a contiguous last dimension")
+    gdesc = _GradDesc(dtype=_dtype_code(dx.dtype), reserved=0, stride_b=dx.stride(0),
+                      stride_h=dx.stride(1), stride_n=dx.stride(2))
+    st = ctypes.c_int(0)
+    ws_bytes = lib.lard_relkl_workspace_size(ctypes.byref(desc), 1, ctypes.byref(st))
+    _check(st.value)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    _check(lib.lard_relkl_bwd(ctypes.byref(desc), x_t.data_ptr(), x_s.data_ptr(),
+                              lse_t.data_ptr(), lse_s.data_ptr(), grad_loss.data_ptr(),
+                              ctypes.byref(gdesc), dx.data_ptr(), ws.data_ptr(), ws.numel(),
+                              _stream_handle(dev, stream)))
+    del keep
+    return dx
+
+
+class _RelationKL(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, x_t, x_s, causal, scale, head_map):
+        out = relkl_fwd(x_t, x_s, causal=causal, scale=scale, head_map=head_map)
+        ctx.save_for_backward(x_t, x_s, out["lse_t"], out["lse_s"])
+        ctx.causal, ctx.scale, ctx.head_map = causal, scale, head_map
+        return out["loss"]
+
+    @staticmethod
+    def backward(ctx, grad):
+        x_t, x_s, lse_t, lse_s = ctx.saved_tensors
+        g = grad if grad.dtype == torch.float32 else grad.float()
+        dx = relkl_bwd(x_t, x_s, lse_t, lse_s, g, causal=ctx.causal, scale=ctx.scale,
+                       head_map=ctx.head_map)
+        return None, dx, None, None, None
+
+
+def relation_kl(x_t: torch.Tensor, x_s: torch.Tensor, *, causal: bool = True,
+                scale: Optional[float] = None, head_map: Optional[Sequence[int]] = None):
+    """Sum over batch, relation heads and rows of KL(R_teacher || R_student) (a 0-d fp32
+    tensor).  Differentiable with respect to x_s; the teacher is treated as frozen."""
+    return _RelationKL.apply(x_t.detach(), x_s, causal, scale,
+                             None if head_map is None else tuple(int(v) for v in head_map))

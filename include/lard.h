@@ -1,0 +1,149 @@
+/*
+ * lard.h -- C ABI of the linear-memory attention-relation KL library (LinearARD) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (pith.science verdict page on LinearARD, pith_extraction.key_machinery
+ * and core_discovery; arXiv abstract on mlsanity.com):
+ *   for each batch b and relation head h, with X_m = x_m[b, head_map[h]] (N x d) for the
+ *   teacher m = t and the student m = s,
+ *     Z_m   = scale * X_m X_m^T + M        (M: 0 where kept, -inf where masked)
+ *     R_m   = row-softmax(Z_m)
+ *     KL_i  = sum_j R_t(i,j) * (log R_t(i,j) - log R_s(i,j))        (forward KL, nats)
+ *     loss  = sum over b, h, i of KL_i
+ *   and, for an upstream gradient g of the loss,
+ *     dZ    = g * (R_s - R_t)  (0 where masked)
+ *     dX_s  = scale * (dZ + dZ^T) X_s       (the teacher is frozen: no teacher gradient)
+ * "Phase 1" keeps only the per-row log-sum-exp LSE_m(i) = log sum_j exp(Z_m(i,j)); the
+ * backward recomputes the logits tile by tile from X and the LSEs, so no N x N matrix is
+ * ever stored (extra device memory is O(B*H*N)).
+ *
+ * Mask: causal = 1 keeps j <= i (the diagonal included); causal = 0 keeps every entry.
+ * The returned loss is the plain sum; the pages' mean over rows is loss / N and its
+ * gradient is obtained by passing g = 1 / N.
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers named x_*, lse_*, row_kl, loss, grad_loss, dx_student and workspace are
+ *    DEVICE pointers; head_map and the descriptors are HOST pointers.
+ *  - All validation happens on the host before any HIP call; a failed validation
+ *    returns LARD_ERR_INVALID_ARGUMENT / LARD_ERR_UNSUPPORTED /
+ *    LARD_ERR_WORKSPACE_TOO_SMALL and touches no device memory.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the null
+ *    stream).  The library never allocates, frees or synchronises, keeps no global
+ *    state and is safe to call from several threads.  A failed launch returns
+ *    LARD_ERR_HIP.  No exception or abort crosses the ABI.
+ *  - The caller owns every buffer, including the workspace, and must keep them alive
+ *    until the enqueued work has completed.
+ *  - Results are bitwise reproducible for a fixed shape and split count.
+ *  - NaN / Inf inputs are not checked and propagate.
+ *  - The backward rounds dZ and X_s to IEEE fp16 for its gradient contraction (X_s is
+ *    bf16 there, and bf16 -> fp16 is exact for 2^-17 <= |x| < 65504).  Inputs outside
+ *    |x| < 65504 are not supported by the bf16 backward.
+ */
+#ifndef LARD_H
+#define LARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum lard_status {
+  LARD_OK = 0,
+  LARD_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, stride, alignment or map */
+  LARD_ERR_UNSUPPORTED = 2,      /* valid request the library does not implement     */
+  LARD_ERR_WORKSPACE_TOO_SMALL = 3,
+  LARD_ERR_HIP = 4               /* a HIP launch or runtime call failed              */
+} lard_status;
+
+typedef enum lard_dtype { LARD_FP32 = 0, LARD_BF16 = 1 } lard_dtype;
+
+/* Largest number of relation heads one call may compute (length of head_map). */
+#define LARD_MAX_HEADS 256
+
+/*
+ * Problem descriptor.  Teacher and student are [B, H_in, N, d] tensors of the same dtype
+ * with element strides (stride over d must be 1, i.e. each row of d elements is
+ * contiguous).  Requirements checked by every entry point:
+ *   B >= 1, H_in >= 1, N >= 1, d in {64, 128};
+ *   all strides >= 0 and multiples of 8 (bf16) or 4 (fp32) elements, so that every row
+ *   starts on a 16-byte boundary; x pointers 16-byte aligned;
+ *   1 <= H <= LARD_MAX_HEADS;
+ *   head_map == NULL  -> H == H_in and relation head h reads input head h;
+ *   head_map != NULL  -> H entries, each in [0, H_in), pairwise distinct (injective:
+ *                        e.g. the distinct KV heads of a repeated GQA tensor);
+ *   causal in {0, 1}; scale finite and > 0 (normally float32(1/sqrt(d)), used for
+ *   teacher and student alike).
+ */
+typedef struct lard_relkl_desc {
+  int32_t dtype;          /* lard_dtype of x_teacher and x_student                    */
+  int32_t B, H_in, N, d;
+  int64_t t_stride_b, t_stride_h, t_stride_n;   /* teacher strides, in elements       */
+  int64_t s_stride_b, s_stride_h, s_stride_n;   /* student strides, in elements       */
+  int32_t H;              /* relation heads computed                                   */
+  int32_t causal;         /* 1: keep j <= i;  0: keep all                              */
+  const int32_t* head_map;/* HOST int32[H] or NULL                                     */
+  float scale;            /* logit scale                                               */
+} lard_relkl_desc;
+
+/*
+ * Output layout of the student gradient: [B, H_in, N, d] in `dtype` (LARD_FP32 or the
+ * input dtype), element strides with unit stride over d; same alignment rules as the
+ * inputs.  Heads listed in head_map (all heads when NULL) are overwritten; the other
+ * heads are left untouched.
+ */
+typedef struct lard_grad_desc {
+  int32_t dtype;
+  int32_t reserved;
+  int64_t stride_b, stride_h, stride_n;
+} lard_grad_desc;
+
+/*
+ * Bytes of device workspace that lard_relkl_fwd (pass = 0) or lard_relkl_bwd (pass = 1)
+ * needs for this descriptor (0 is possible).  Returns 0 and sets *status (if non-NULL)
+ * on an invalid descriptor.  The backward workspace depends on the split count the
+ * library picks for the shape (environment variable LARD_SPLITK overrides it).
+ */
+size_t lard_relkl_workspace_size(const lard_relkl_desc* desc, int pass, lard_status* status);
+
+/*
+ * Forward ("phase 1" plus the KL accumulation; key_machinery of the verdict page).
+ *   x_teacher, x_student : device, desc layout and dtype, read only.
+ *   lse_teacher, lse_student : device fp32 [B, H, N] (dense), written: LSE_m(i) in nats.
+ *   row_kl : device fp32 [B, H, N] or NULL; written: KL_i.
+ *   loss   : device fp32 scalar, written (not accumulated): sum of KL_i over b, h, i,
+ *            reduced in a fixed order in fp64.
+ *   workspace : device, >= lard_relkl_workspace_size(desc, 0) bytes, 8-byte aligned.
+ */
+lard_status lard_relkl_fwd(const lard_relkl_desc* desc, const void* x_teacher,
+                           const void* x_student, float* lse_teacher, float* lse_student,
+                           float* row_kl, float* loss, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
+ * Backward (logit recomputation fused with the gradient; key_machinery and the gradient
+ * identity of core_discovery on the verdict page).
+ *   lse_teacher, lse_student : device fp32 [B, H, N] as written by lard_relkl_fwd for
+ *            the same inputs.
+ *   grad_loss : device fp32 scalar g (the upstream gradient of `loss`).
+ *   dx_student : device, layout and dtype given by `grad`; see lard_grad_desc.
+ *   workspace : device, >= lard_relkl_workspace_size(desc, 1) bytes, 16-byte aligned.
+ */
+lard_status lard_relkl_bwd(const lard_relkl_desc* desc, const void* x_teacher,
+                           const void* x_student, const float* lse_teacher,
+                           const float* lse_student, const float* grad_loss,
+                           const lard_grad_desc* grad, void* dx_student, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* lard_status_string(lard_status status);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int lard_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LARD_H */

@@ -84,19 +84,22 @@ def _chunks(n: int, chunk: int | None):
         yield np.arange(r0, min(n, r0 + step))
 
 
-def forward_unit(x_t, x_s, scale: float, causal: bool, chunk: int | None = None):
+def forward_unit(x_t, x_s, scale: float, causal: bool, chunk: int | None = None, rows=None):
     """Forward for one (batch, head) unit.
 
-    x_t, x_s: [N, d].  Returns (lse_t, lse_s, row_kl), each float64 [N].
+    x_t, x_s: [N, d].  Returns (lse_t, lse_s, row_kl), each float64 [N] (or, when ``rows``
+    is given, float64 [len(rows)] for those rows only: every row is its own definition).
     """
     x_t = _f64(x_t)
     x_s = _f64(x_s)
     n = x_t.shape[0]
     cols = np.arange(n)
-    lse_t = np.empty(n)
-    lse_s = np.empty(n)
-    row_kl = np.empty(n)
-    for rows in _chunks(n, chunk):
+    sel = cols if rows is None else np.asarray(rows, dtype=np.int64)
+    lse_t = np.empty(sel.size)
+    lse_s = np.empty(sel.size)
+    row_kl = np.empty(sel.size)
+    for pos in _chunks(sel.size, chunk):
+        rows = sel[pos]
         keep = keep_mask(rows, cols, causal)
         z_t = logits(x_t[rows], x_t, scale)
         z_s = logits(x_s[rows], x_s, scale)
@@ -106,9 +109,9 @@ def forward_unit(x_t, x_s, scale: float, causal: bool, chunk: int | None = None)
         logp_s = z_s - ls[:, None]
         p_t = np.where(keep, np.exp(np.where(keep, logp_t, -np.inf)), 0.0)
         term = np.where(keep, p_t * (logp_t - logp_s), 0.0)
-        lse_t[rows] = lt
-        lse_s[rows] = ls
-        row_kl[rows] = term.sum(axis=1)
+        lse_t[pos] = lt
+        lse_s[pos] = ls
+        row_kl[pos] = term.sum(axis=1)
     return lse_t, lse_s, row_kl
 
 

@@ -1,0 +1,168 @@
+"""C-ABI tests that need no GPU: the library loads, exports what include/lard.h declares,
+and rejects invalid requests on the host before any HIP call (no compute is launched)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from attention_relation_distillation_amd import relkl
+from attention_relation_distillation_amd.relkl import _Desc, _GradDesc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, INVALID, UNSUPPORTED, WS_SMALL, HIP = 0, 1, 2, 3, 4
+FAKE = 0x100000  # 16-byte-aligned fake device address; never dereferenced on these paths
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return relkl.load_library()
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "lard.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(lard_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) >= {"lard_relkl_fwd", "lard_relkl_bwd", "lard_relkl_workspace_size",
+                          "lard_status_string", "lard_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.lard_version() >= 10000
+
+
+def test_status_strings(lib):
+    for code, name in relkl._STATUS_NAMES.items():
+        assert lib.lard_status_string(code).decode().startswith(name)
+    assert b"unknown" in lib.lard_status_string(99)
+
+
+def good_desc(**kw):
+    base = dict(dtype=1, B=1, H_in=4, N=100, d=128, t_stride_b=4 * 100 * 128,
+                t_stride_h=100 * 128, t_stride_n=128, s_stride_b=4 * 100 * 128,
+                s_stride_h=100 * 128, s_stride_n=128, H=4, causal=1,
+                head_map=ctypes.POINTER(ctypes.c_int32)(), scale=128 ** -0.5)
+    base.update(kw)
+    return _Desc(**base)
+
+
+def ws_query(lib, desc, pass_=0):
+    st = ctypes.c_int(-1)
+    n = lib.lard_relkl_workspace_size(ctypes.byref(desc), pass_, ctypes.byref(st))
+    return n, st.value
+
+
+def fwd(lib, desc, xt=FAKE, xs=FAKE, lt=FAKE, ls=FAKE, kl=None, loss=FAKE, ws=FAKE, nws=1 << 20):
+    return lib.lard_relkl_fwd(ctypes.byref(desc) if desc is not None else None, xt, xs, lt, ls,
+                              kl, loss, ws, nws, None)
+
+
+def bwd(lib, desc, g=None, xt=FAKE, xs=FAKE, dx=FAKE, ws=FAKE, nws=1 << 30):
+    g = g or _GradDesc(dtype=1, reserved=0, stride_b=4 * 100 * 128, stride_h=100 * 128,
+                       stride_n=128)
+    return lib.lard_relkl_bwd(ctypes.byref(desc), xt, xs, FAKE, FAKE, FAKE, ctypes.byref(g), dx,
+                              ws, nws, None)
+
+
+def test_workspace_sizes(lib):
+    n0, st = ws_query(lib, good_desc(), 0)
+    assert st == OK and n0 >= 8 and n0 % 256 == 0
+    n1, st = ws_query(lib, good_desc(), 1)
+    assert st == OK and n1 > 0  # 4 units x 1 row tile: the backward splits its key range
+    big = good_desc(N=32768, H_in=32, H=32, t_stride_h=32768 * 128, t_stride_b=32 * 32768 * 128,
+                    s_stride_h=32768 * 128, s_stride_b=32 * 32768 * 128)
+    n1, st = ws_query(lib, big, 1)
+    assert st == OK and n1 == 0  # the grid fills the chip: no split, no workspace
+    n0, st = ws_query(lib, big, 0)
+    assert st == OK and n0 < 32 * 32768  # O(B * H * N / 256) partial sums
+    _, st = ws_query(lib, good_desc(), 2)
+    assert st == INVALID
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), INVALID),
+    (dict(B=0), INVALID),
+    (dict(N=0), INVALID),
+    (dict(d=32), UNSUPPORTED),
+    (dict(d=96), UNSUPPORTED),
+    (dict(causal=2), INVALID),
+    (dict(scale=0.0), INVALID),
+    (dict(scale=-1.0), INVALID),
+    (dict(scale=float("nan")), INVALID),
+    (dict(scale=float("inf")), INVALID),
+    (dict(H=3), INVALID),                 # no head map: H must equal H_in
+    (dict(H=0), INVALID),
+    (dict(t_stride_n=100), INVALID),      # not a multiple of 8 bf16 elements
+    (dict(s_stride_h=-128), INVALID),
+    (dict(t_stride_n=64), INVALID),       # rows overlap (stride over n < d)
+])
+def test_descriptor_validation(lib, kw, code):
+    desc = good_desc(**kw)
+    _, st = ws_query(lib, desc, 0)
+    assert st == code
+    assert fwd(lib, desc) == code
+    assert bwd(lib, desc) == code
+
+
+def test_head_map_validation(lib):
+    def with_map(vals, h_in=4):
+        arr = (ctypes.c_int32 * len(vals))(*vals)
+        d = good_desc(H=len(vals), H_in=h_in,
+                      head_map=ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)))
+        return d, arr
+
+    d, keep = with_map([0, 2])
+    assert ws_query(lib, d)[1] == OK
+    d, keep = with_map([0, 4])
+    assert ws_query(lib, d)[1] == INVALID   # out of range
+    d, keep = with_map([1, 1])
+    assert ws_query(lib, d)[1] == INVALID   # not injective
+    d, keep = with_map([-1])
+    assert ws_query(lib, d)[1] == INVALID
+    d, keep = with_map(list(range(257)), h_in=300)
+    assert ws_query(lib, d)[1] == UNSUPPORTED  # more than LARD_MAX_HEADS
+    del keep
+
+
+def test_pointer_and_workspace_validation(lib):
+    d = good_desc()
+    assert fwd(lib, None) == INVALID
+    assert fwd(lib, d, xt=None) == INVALID
+    assert fwd(lib, d, loss=None) == INVALID
+    assert fwd(lib, d, xs=FAKE + 2) == INVALID     # misaligned
+    assert fwd(lib, d, nws=0) == WS_SMALL
+    assert bwd(lib, d, dx=None) == INVALID
+    assert bwd(lib, d, nws=0) == WS_SMALL
+    g = _GradDesc(dtype=1, reserved=0, stride_b=4 * 100 * 128, stride_h=100 * 128, stride_n=130)
+    assert bwd(lib, d, g=g) == INVALID
+    # fp32 inputs cannot produce a bf16 gradient
+    d32 = good_desc(dtype=0)
+    g = _GradDesc(dtype=1, reserved=0, stride_b=4 * 100 * 128, stride_h=100 * 128, stride_n=128)
+    assert bwd(lib, d32, g=g) == UNSUPPORTED
+
+
+def test_fault_injection_maps_to_hip_error(lib, monkeypatch):
+    """A failed launch is reported as LARD_ERR_HIP (the launch wrapper is told to fail
+    before it calls HIP), and the Python layer turns it into an exception."""
+    monkeypatch.setenv("LARD_FAULT_INJECT", "1")
+    assert fwd(lib, good_desc()) == HIP
+    assert bwd(lib, good_desc()) == HIP
+    with pytest.raises(relkl.LardError) as ei:
+        relkl._check(HIP)
+    assert ei.value.status == HIP
+
+
+def test_python_layer_refuses_cpu_tensors():
+    x = torch.zeros(1, 1, 8, 64)
+    with pytest.raises(RuntimeError, match="GPU"):
+        relkl.relkl_fwd(x, x)
+    with pytest.raises(relkl.LardError):
+        relkl.relkl_fwd(torch.zeros(1, 8, 64), torch.zeros(1, 8, 64))
+    with pytest.raises(relkl.LardError):
+        relkl.relkl_fwd(torch.zeros(1, 1, 8, 64, dtype=torch.float16),
+                        torch.zeros(1, 1, 8, 64, dtype=torch.float16))

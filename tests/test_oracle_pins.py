@@ -225,6 +225,8 @@ def test_row_chunking_is_exact():
         for u, v in zip(a, b):
             np.testing.assert_allclose(u, v, rtol=1e-14, atol=1e-15)
         rows = np.array([0, 3, 17, 49])
+        for u, v in zip(oracle.forward_unit(x_t, x_s, 0.3, causal, rows=rows, chunk=3), a):
+            np.testing.assert_allclose(u, v[rows], rtol=1e-14, atol=1e-15)
         np.testing.assert_allclose(oracle.backward_unit(x_t, x_s, 0.3, causal, rows=rows, chunk=3),
                                    oracle.backward_unit(x_t, x_s, 0.3, causal)[rows],
                                    rtol=1e-12, atol=1e-14)

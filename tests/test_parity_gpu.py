@@ -1,0 +1,183 @@
+"""GPU parity of the HIP relation-KL path (called through the C ABI) with the float64
+oracle, on the seeded workload recipes at sizes the oracle finishes in seconds, with
+ragged tails over several row tiles (256 rows) and key tiles (64 rows)."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from attention_relation_distillation_amd import relkl, workloads
+from tests._gpu import (GRAD_RL2, assert_parity, banner, device, gpu_fwd_bwd, np64,
+                        oracle_fwd_bwd, rel_l2)
+
+pytestmark = pytest.mark.gpu
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_tiny_workload_full():
+    """The tiny fp32 Q/Q workload at its full size (N=256, d=64, causal)."""
+    banner("tiny fp32 N=256 d=64 causal")
+    (rel,) = workloads.make_inputs("tiny")
+    f, dx = gpu_fwd_bwd(rel.x_t, rel.x_s, True)
+    fo, dxo = oracle_fwd_bwd(rel.x_t, rel.x_s, True)
+    assert_parity(f, dx, fo, dxo, torch.float32, "tiny")
+    np.testing.assert_allclose(np64(f["row_kl"]), fo["row_kl"], rtol=1e-4, atol=1e-7)
+
+
+@pytest.mark.parametrize("name,n,hq,hkv,b", [
+    ("llama2_4k", 1000, 2, 2, 1),
+    ("gqa_16k", 777, 4, 2, 1),
+    ("batched_8k", 600, 2, 2, 2),
+])
+def test_workload_recipes_reduced(name, n, hq, hkv, b):
+    """bf16 relations of each recipe at a reduced size, every mask the workload runs."""
+    wl = workloads.WORKLOADS[name]
+    rels = workloads.make_inputs(wl, N=n, Hq=hq, Hkv=hkv, B=b)
+    for causal in wl.masks:
+        for rel in rels:
+            banner(f"{name} {rel.name} N={n} causal={causal}")
+            f, dx = gpu_fwd_bwd(rel.x_t, rel.x_s, causal)
+            fo, dxo = oracle_fwd_bwd(rel.x_t, rel.x_s, causal)
+            assert_parity(f, dx, fo, dxo, torch.bfloat16, f"{name}/{rel.name}/c{int(causal)}")
+            # fp32 gradient output isolates the kernel's own error from bf16 output rounding
+            _, dx32 = gpu_fwd_bwd(rel.x_t, rel.x_s, causal, dx_dtype=torch.float32)
+            e32 = rel_l2(np64(dx32), dxo)
+            print(f"[parity] fp32-out grad rl2 {e32:.3e}", flush=True)
+            assert e32 <= 1e-3
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("n", [1, 2, 3, 5, 63, 64, 65, 255, 256, 257, 513])
+def test_edge_sizes(n, causal, d, dtype):
+    banner(f"edge N={n} d={d} causal={causal} {dtype}")
+    g = torch.Generator().manual_seed(n * 7 + d)
+    x = torch.randn((1, 2, n, d), generator=g)
+    x_t = x.to(dtype)
+    x_s = (x + 0.2 * torch.randn((1, 2, n, d), generator=g)).to(dtype)
+    f, dx = gpu_fwd_bwd(x_t, x_s, causal, dx_dtype=torch.float32)
+    fo, dxo = oracle_fwd_bwd(x_t, x_s, causal)
+    if n == 1:
+        # one kept entry per row: KL is exactly 0; the gradient is 0 up to the fp32
+        # rounding of exp(z - LSE) (the oracle's is exactly 0)
+        assert float(f["loss"].item()) == 0.0
+        assert float(dx.abs().max().item()) <= 1e-5 * float((x_s.float() ** 2).sum().item())
+        return
+    assert_parity(f, dx, fo, dxo, dtype, f"edge N={n}")
+
+
+def test_golden_closed_form():
+    """Structured inputs whose relation KL has a closed form (tests/golden)."""
+    with open(os.path.join(ROOT, "tests", "golden", "closed_form.json")) as fh:
+        gold = json.load(fh)
+    for case in gold["cases"]:
+        if case["d"] not in (64, 128):
+            continue
+        n, d = case["N"], case["d"]
+        for dtype in (torch.float32, torch.bfloat16):
+            banner(f"golden {case['name']} {dtype}")
+            e = torch.zeros((1, 1, n, d))
+            m = min(n, d)
+            e[0, 0, torch.arange(m), torch.arange(m)] = 1.0
+            x_t, x_s = (case["a"] * e).to(dtype), (case["b"] * e).to(dtype)
+            f, dx = gpu_fwd_bwd(x_t, x_s, case["causal"], dx_dtype=torch.float32,
+                                scale=case["scale"], g=case["g"])
+            np.testing.assert_allclose(np64(f["lse_t"])[0, 0], case["lse_t"], rtol=2e-6, atol=2e-6)
+            np.testing.assert_allclose(np64(f["lse_s"])[0, 0], case["lse_s"], rtol=2e-6, atol=2e-6)
+            assert float(f["loss"].item()) == pytest.approx(case["loss"], rel=1e-5)
+            rows = case["dx_rows"]
+            got = np64(dx)[0, 0][rows]
+            ref = np.array(case["dx"])
+            assert rel_l2(got, ref) <= 1e-3, rel_l2(got, ref)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_student_equals_teacher_is_exactly_zero(causal, dtype):
+    banner(f"exact zero causal={causal} {dtype}")
+    g = torch.Generator().manual_seed(3)
+    x = torch.randn((2, 3, 300, 128), generator=g).to(dtype)
+    f, dx = gpu_fwd_bwd(x, x.clone(), causal, dx_dtype=torch.float32)
+    assert float(f["loss"].item()) == 0.0
+    assert torch.all(f["row_kl"] == 0)
+    assert torch.equal(f["lse_t"], f["lse_s"])
+    assert torch.all(dx == 0)
+
+
+def test_deterministic_and_split_invariant(monkeypatch):
+    banner("determinism / split-K")
+    (rel,) = workloads.make_inputs("llama2_4k", N=700, Hq=2, Hkv=2, relations=("qq",))
+    f1, dx1 = gpu_fwd_bwd(rel.x_t, rel.x_s, True, dx_dtype=torch.float32)
+    f2, dx2 = gpu_fwd_bwd(rel.x_t, rel.x_s, True, dx_dtype=torch.float32)
+    assert torch.equal(f1["loss"], f2["loss"]) and torch.equal(dx1, dx2)
+    assert torch.equal(f1["lse_t"], f2["lse_t"]) and torch.equal(f1["row_kl"], f2["row_kl"])
+    outs = []
+    for s in ("1", "3", "11"):
+        monkeypatch.setenv("LARD_SPLITK", s)
+        _, dx = gpu_fwd_bwd(rel.x_t, rel.x_s, True, dx_dtype=torch.float32)
+        outs.append(np64(dx))
+    for o in outs[1:]:
+        assert rel_l2(o, outs[0]) < 1e-6
+
+
+def test_head_map_and_untouched_heads():
+    """GQA: K expanded to 8 query-head slots (repeat 4x); head_map picks the distinct KV
+    heads.  Unmapped heads of dx keep their previous contents."""
+    banner("head_map")
+    dev = device()
+    g = torch.Generator().manual_seed(5)
+    k = torch.randn((1, 2, 333, 128), generator=g)
+    k_s = k + 0.1 * torch.randn((1, 2, 333, 128), generator=g)
+    rep_t = k.repeat_interleave(4, dim=1).to(torch.bfloat16).to(dev)
+    rep_s = k_s.repeat_interleave(4, dim=1).to(torch.bfloat16).to(dev)
+    hm = [0, 4]
+    f = relkl.relkl_fwd(rep_t, rep_s, causal=True, head_map=hm, want_row_kl=True)
+    sentinel = torch.full(rep_s.shape, 7.0, dtype=torch.float32, device=dev)
+    relkl.relkl_bwd(rep_t, rep_s, f["lse_t"], f["lse_s"], torch.ones((), device=dev),
+                    causal=True, head_map=hm, dx=sentinel)
+    torch.cuda.synchronize()
+    base_t, base_s = k.to(torch.bfloat16), k_s.to(torch.bfloat16)
+    fo, dxo = oracle_fwd_bwd(base_t, base_s, True)
+    assert abs(float(f["loss"].item()) - fo["loss"]) <= 1e-4 * fo["loss"]
+    got = np64(sentinel)
+    assert rel_l2(got[:, [0, 4]], dxo) <= 1e-3
+    untouched = [h for h in range(8) if h not in hm]
+    assert np.all(got[:, untouched] == 7.0)
+
+
+def test_strided_inputs_match_contiguous():
+    """Inputs taken as views of a [B, N, H, d] buffer (stride over n = H * d)."""
+    banner("strided")
+    dev = device()
+    g = torch.Generator().manual_seed(6)
+    buf_t = torch.randn((2, 300, 3, 128), generator=g).to(torch.bfloat16).to(dev)
+    buf_s = (buf_t.float() + 0.1 * torch.randn((2, 300, 3, 128), generator=g).to(dev)).to(torch.bfloat16)
+    v_t, v_s = buf_t.permute(0, 2, 1, 3), buf_s.permute(0, 2, 1, 3)
+    assert not v_t.is_contiguous()
+    f1 = relkl.relkl_fwd(v_t, v_s, causal=True)
+    f2 = relkl.relkl_fwd(v_t.contiguous(), v_s.contiguous(), causal=True)
+    gl = torch.ones((), device=dev)
+    d1 = relkl.relkl_bwd(v_t, v_s, f1["lse_t"], f1["lse_s"], gl, causal=True)
+    d2 = relkl.relkl_bwd(v_t.contiguous(), v_s.contiguous(), f2["lse_t"], f2["lse_s"], gl,
+                         causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(f1["loss"], f2["loss"])
+    assert torch.equal(d1.contiguous(), d2)
+
+
+def test_autograd_function():
+    banner("autograd")
+    dev = device()
+    g = torch.Generator().manual_seed(8)
+    x_t = torch.randn((1, 2, 200, 64), generator=g).to(dev)
+    x_s = (x_t + 0.3 * torch.randn((1, 2, 200, 64), generator=g).to(dev)).requires_grad_(True)
+    loss = relkl.relation_kl(x_t, x_s, causal=True)
+    (2.5 * loss).backward()
+    fo, dxo = oracle_fwd_bwd(x_t.cpu(), x_s.detach().cpu(), True, g=2.5)
+    assert float(loss.item()) == pytest.approx(fo["loss"], rel=1e-5)
+    assert rel_l2(np64(x_s.grad), dxo) <= GRAD_RL2[torch.float32]
