@@ -276,13 +276,17 @@ __device__ __forceinline__ void stu_store(const StuRegs<In, D>& r, char* lds_rm,
 
 // ------------------------------------------------------------------ forward kernel
 // Online update of one lane's row statistics with the 16 columns it holds of a 32x32
-// score block (raw scores; exp2 with the pre-multiplied c2 = scale * log2 e).
-//   m: running max, l: sum of exp2((S - m) c2), acc_a: sum of e_t * (S_t - S_s).
+// score block (raw scores S; logits z = scale S; c2 = scale log2 e).
+//   b: exponent bias in use, b = -(running max of S) * c2, rounded once;
+//   l: sum of exp2(S c2 + b);  acc_a: sum of exp2(S_t c2 + b_t) (S_t - S_s).
+// The bias is carried as the exact fp32 value that entered every exponent, so the
+// rescale factors (exp2(b_new - b_old)) and the final LSE / KL use exactly the offsets
+// the sums were taken with; a rounded "max * c2" never has to cancel against itself.
 // Masked columns contribute exactly zero (the select is on the exponential itself).
 template <bool MASK, bool CAUSAL>
 __device__ __forceinline__ void online_update(const f32x16& st, const f32x16& ss, int jb0, int i,
-                                              int hh, int N, float c2, float& m_t, float& l_t,
-                                              float& acc_a, float& m_s, float& l_s) {
+                                              int hh, int N, float c2, float& b_t, float& l_t,
+                                              float& acc_a, float& b_s, float& l_s) {
   bool keep[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -295,15 +299,14 @@ __device__ __forceinline__ void online_update(const f32x16& st, const f32x16& ss
     mx_t = fmaxf(mx_t, keep[r] ? st[r] : kNegBig);
     mx_s = fmaxf(mx_s, keep[r] ? ss[r] : kNegBig);
   }
-  const float mn_t = fmaxf(m_t, mx_t), mn_s = fmaxf(m_s, mx_s);
-  const float alpha_t = fast_exp2((m_t - mn_t) * c2);
-  const float alpha_s = fast_exp2((m_s - mn_s) * c2);
-  const float nb_t = -mn_t * c2, nb_s = -mn_s * c2;
+  const float bn_t = fminf(b_t, -mx_t * c2), bn_s = fminf(b_s, -mx_s * c2);
+  const float alpha_t = fast_exp2(bn_t - b_t);
+  const float alpha_s = fast_exp2(bn_s - b_s);
   float e_t[16], e_s[16], dd[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const float et = fast_exp2(fmaf(st[r], c2, nb_t));
-    const float es = fast_exp2(fmaf(ss[r], c2, nb_s));
+    const float et = fast_exp2(fmaf(st[r], c2, bn_t));
+    const float es = fast_exp2(fmaf(ss[r], c2, bn_s));
     e_t[r] = keep[r] ? et : 0.f;
     e_s[r] = keep[r] ? es : 0.f;
     dd[r] = keep[r] ? et * (st[r] - ss[r]) : 0.f;
@@ -321,8 +324,8 @@ __device__ __forceinline__ void online_update(const f32x16& st, const f32x16& ss
   l_t = fmaf(l_t, alpha_t, e_t[0]);
   acc_a = fmaf(acc_a, alpha_t, dd[0]);
   l_s = fmaf(l_s, alpha_s, e_s[0]);
-  m_t = mn_t;
-  m_s = mn_s;
+  b_t = bn_t;
+  b_s = bn_s;
 }
 
 template <class In, int D, bool CAUSAL>
@@ -372,12 +375,13 @@ void relkl_fwd_kernel(const FwdArgs a) {
   }
 
   // Online statistics over this lane's column subset, in raw-score units.
-  float m_t[kRowBlocks], l_t[kRowBlocks], acc_a[kRowBlocks], m_s[kRowBlocks], l_s[kRowBlocks];
+  const float c2 = a.c2;
+  const float b_init = -kNegBig * c2;  // bias of an empty row: every real bias is below it
+  float b_t[kRowBlocks], l_t[kRowBlocks], acc_a[kRowBlocks], b_s[kRowBlocks], l_s[kRowBlocks];
 #pragma unroll
   for (int rb = 0; rb < kRowBlocks; ++rb) {
-    m_t[rb] = kNegBig; l_t[rb] = 0.f; acc_a[rb] = 0.f; m_s[rb] = kNegBig; l_s[rb] = 0.f;
+    b_t[rb] = b_init; l_t[rb] = 0.f; acc_a[rb] = 0.f; b_s[rb] = b_init; l_s[rb] = 0.f;
   }
-  const float c2 = a.c2;
 
   const int j_end = CAUSAL ? min(N, i0 + kBR) : N;
   const int n_tiles = (j_end + kBC - 1) / kBC;
@@ -422,33 +426,35 @@ void relkl_fwd_kernel(const FwdArgs a) {
         const int i = ib0 + l32;
         const bool need_mask = (CAUSAL && jb0 + 31 > ib0) || (jb0 + 32 > N);
         if (need_mask)
-          online_update<true, CAUSAL>(st[rb], ss[rb], jb0, i, hh, N, c2, m_t[rb], l_t[rb],
-                                      acc_a[rb], m_s[rb], l_s[rb]);
+          online_update<true, CAUSAL>(st[rb], ss[rb], jb0, i, hh, N, c2, b_t[rb], l_t[rb],
+                                      acc_a[rb], b_s[rb], l_s[rb]);
         else
-          online_update<false, CAUSAL>(st[rb], ss[rb], jb0, i, hh, N, c2, m_t[rb], l_t[rb],
-                                       acc_a[rb], m_s[rb], l_s[rb]);
+          online_update<false, CAUSAL>(st[rb], ss[rb], jb0, i, hh, N, c2, b_t[rb], l_t[rb],
+                                       acc_a[rb], b_s[rb], l_s[rb]);
       }
     }
   }
 
-  // Merge the two half-waves (lanes l and l ^ 32 hold the same row) and finish.
+  // Merge the two half-waves (lanes l and l ^ 32 hold the same row) and finish, in log2
+  // units:  LSE = ln2 (log2 L - b),
+  //         KL  = ln2 (c2 A_t / L_t + (b_t - b_s) - log2(L_t / L_s))
+  // (KL_i = E_t[z_t - z_s] - (LSE_t - LSE_s), with the LSE difference taken as a ratio).
   double kl_sum = 0.0;
-  const float scale = a.scale;
+  constexpr float kLn2 = 0.6931471805599453f;
 #pragma unroll
   for (int rb = 0; rb < kRowBlocks; ++rb) {
-    const float om_t = __shfl_xor(m_t[rb], 32), ol_t = __shfl_xor(l_t[rb], 32);
+    const float ob_t = __shfl_xor(b_t[rb], 32), ol_t = __shfl_xor(l_t[rb], 32);
     const float oa = __shfl_xor(acc_a[rb], 32);
-    const float om_s = __shfl_xor(m_s[rb], 32), ol_s = __shfl_xor(l_s[rb], 32);
-    const float M_t = fmaxf(m_t[rb], om_t), M_s = fmaxf(m_s[rb], om_s);
-    const float f1t = fast_exp2((m_t[rb] - M_t) * c2), f2t = fast_exp2((om_t - M_t) * c2);
-    const float f1s = fast_exp2((m_s[rb] - M_s) * c2), f2s = fast_exp2((om_s - M_s) * c2);
+    const float ob_s = __shfl_xor(b_s[rb], 32), ol_s = __shfl_xor(l_s[rb], 32);
+    const float B_t = fminf(b_t[rb], ob_t), B_s = fminf(b_s[rb], ob_s);
+    const float f1t = fast_exp2(B_t - b_t[rb]), f2t = fast_exp2(B_t - ob_t);
+    const float f1s = fast_exp2(B_s - b_s[rb]), f2s = fast_exp2(B_s - ob_s);
     const float L_t = l_t[rb] * f1t + ol_t * f2t;
     const float A_t = acc_a[rb] * f1t + oa * f2t;
     const float L_s = l_s[rb] * f1s + ol_s * f2s;
-    const float lse_t = M_t * scale + logf(L_t);
-    const float lse_s = M_s * scale + logf(L_s);
-    // KL_i = E_t[z_t - z_s] - (LSE_t - LSE_s), written in ratio form
-    const float kl = scale * (A_t / L_t - (M_t - M_s)) - logf(L_t / L_s);
+    const float lse_t = (log2f(L_t) - B_t) * kLn2;
+    const float lse_s = (log2f(L_s) - B_s) * kLn2;
+    const float kl = kLn2 * (c2 * (A_t / L_t) + (B_t - B_s) - log2f(L_t / L_s));
     const int i = wrow0 + 32 * rb + l32;
     if (hh == 0 && i < N) {
       const int64_t o = (int64_t)unit * N + i;

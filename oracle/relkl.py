@@ -100,9 +100,12 @@ def forward_unit(x_t, x_s, scale: float, causal: bool, chunk: int | None = None,
     row_kl = np.empty(sel.size)
     for pos in _chunks(sel.size, chunk):
         rows = sel[pos]
+        # causal rows never keep a column beyond their own index: leave those out
+        hi = int(rows.max()) + 1 if causal else n
+        cols = np.arange(hi)
         keep = keep_mask(rows, cols, causal)
-        z_t = logits(x_t[rows], x_t, scale)
-        z_s = logits(x_s[rows], x_s, scale)
+        z_t = logits(x_t[rows], x_t[:hi], scale)
+        z_s = logits(x_s[rows], x_s[:hi], scale)
         lt = row_lse(z_t, keep)
         ls = row_lse(z_s, keep)
         logp_t = z_t - lt[:, None]
@@ -143,14 +146,18 @@ def backward_unit(x_t, x_s, scale: float, causal: bool, g: float = 1.0,
     step = rows.size if not chunk else max(1, int(chunk))
     for c0 in range(0, rows.size, step):
         r = rows[c0:c0 + step]
+        # causal: row r keeps columns <= r, and column r is kept by rows >= r only
+        hi = int(r.max()) + 1 if causal else n
+        lo = int(r.min()) if causal else 0
+        left, right = all_idx[:hi], all_idx[lo:]
         # dZ[r, :]  (row r of the loss, normalised by the LSE of row r)
-        dz_rows = g * (_probs(x_s[r], r, x_s, lse_s[r], scale, causal, all_idx)
-                       - _probs(x_t[r], r, x_t, lse_t[r], scale, causal, all_idx))
+        dz_rows = g * (_probs(x_s[r], r, x_s[:hi], lse_s[r], scale, causal, left)
+                       - _probs(x_t[r], r, x_t[:hi], lse_t[r], scale, causal, left))
         # dZ[:, r]  (column r: rows j normalised by the LSE of row j); Z is symmetric
         # in its two indices, so Z[:, r] = scale * X X[r]^T
-        dz_cols = g * (_probs(x_s, all_idx, x_s[r], lse_s, scale, causal, r)
-                       - _probs(x_t, all_idx, x_t[r], lse_t, scale, causal, r))
-        out[c0:c0 + step] = scale * (dz_rows @ x_s + dz_cols.T @ x_s)
+        dz_cols = g * (_probs(x_s[lo:], right, x_s[r], lse_s[lo:], scale, causal, r)
+                       - _probs(x_t[lo:], right, x_t[r], lse_t[lo:], scale, causal, r))
+        out[c0:c0 + step] = scale * (dz_rows @ x_s[:hi] + dz_cols.T @ x_s[lo:])
     return out
 
 

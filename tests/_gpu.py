@@ -55,19 +55,47 @@ def oracle_fwd_bwd(x_t, x_s, causal, head_map=None, scale=None, g=1.0):
     return f, dx
 
 
-def assert_parity(f, dx, fo, dxo, dtype, label="", dx_out_dtype=None):
-    """Compare GPU outputs with the oracle at the dtype's gates; returns diagnostics."""
+def fp32_floor(fo, x_s, scale):
+    """Absolute error floors of fp32 on-chip arithmetic, for inputs whose result is much
+    smaller than the terms that produce it (tiny N, nearly equal teacher and student).
+
+    Every probability is formed as exp(z - LSE) with LSE held in fp32, so each carries a
+    relative error of a few ulps of max|LSE|; a row's KL is a difference of O(1) terms,
+    and the gradient is a sum of |R| |x| terms (sum_j |R_s - R_t| <= 4 per row counting
+    the row and the transposed terms).  eta = 2^-20 (1 + max |LSE|).
+    """
+    lse_max = float(max(np.max(np.abs(fo["lse_t"])), np.max(np.abs(fo["lse_s"]))))
+    eta = 2.0 ** -20 * (1.0 + lse_max)
+    rows = fo["row_kl"].size
+    loss_floor = eta * rows
+    xs = np64(x_s)
+    row_norm_max = float(np.sqrt(np.max(np.sum(xs * xs, axis=-1))))
+    grad_floor = 4.0 * eta * scale * row_norm_max * np.sqrt(xs.shape[0] * xs.shape[1] * xs.shape[2])
+    return loss_floor, grad_floor
+
+
+def assert_parity(f, dx, fo, dxo, dtype, label="", x_s=None, scale=None):
+    """Compare GPU outputs with the oracle at the dtype's gates; returns diagnostics.
+
+    With x_s and scale given, the gates become gate * |reference| + fp32 floor (see
+    fp32_floor) -- used for edge sizes where the result cancels far below its terms.
+    """
     loss = float(f["loss"].item())
-    loss_err = abs(loss - fo["loss"]) / max(abs(fo["loss"]), 1e-30)
+    loss_abs = abs(loss - fo["loss"])
+    loss_err = loss_abs / max(abs(fo["loss"]), 1e-30)
     lse_err = max(float(np.max(np.abs(np64(f["lse_t"]) - fo["lse_t"]))),
                   float(np.max(np.abs(np64(f["lse_s"]) - fo["lse_s"]))))
     kl_err = rel_l2(np64(f["row_kl"]), fo["row_kl"])
+    g_abs = float(np.linalg.norm(np64(dx) - dxo))
     g_err = rel_l2(np64(dx), dxo)
     diag = dict(loss=loss, loss_ref=fo["loss"], loss_rel=loss_err, lse_abs=lse_err,
                 row_kl_rl2=kl_err, grad_rl2=g_err)
+    loss_floor = grad_floor = 0.0
+    if x_s is not None:
+        loss_floor, grad_floor = fp32_floor(fo, x_s, scale)
+        diag.update(loss_floor=loss_floor, grad_floor=grad_floor, grad_abs=g_abs)
     print(f"[parity] {label} {diag}", flush=True)
-    assert loss_err <= LOSS_RTOL[dtype], diag
-    gate = GRAD_RL2[dtype]
-    assert g_err <= gate, diag
+    assert loss_abs <= LOSS_RTOL[dtype] * abs(fo["loss"]) + loss_floor, diag
+    assert g_abs <= GRAD_RL2[dtype] * float(np.linalg.norm(dxo)) + grad_floor, diag
     assert lse_err <= 5e-5 * max(1.0, float(np.max(np.abs(fo["lse_t"])))), diag
     return diag

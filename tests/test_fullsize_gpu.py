@@ -1,0 +1,107 @@
+"""Full-size parity on the workload shapes, in the launch configuration bench.py times.
+
+At these sizes the oracle cannot materialise everything, so it checks sampled outputs it
+can compute one by one: LSE and row KL of sampled rows of sampled units (each row is its
+own definition, O(N d) work), and the gradient of sampled rows of one unit per relation
+(which needs that unit's full LSE vectors: O(N^2 d) in row chunks).  Properties that hold
+at any size are checked everywhere: finite outputs, KL >= 0 up to fp32 noise, and the
+loss equal to the fp64 sum of the row KLs.  The 4K workload also gets its full loss."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from attention_relation_distillation_amd import relkl, workloads
+from tests._gpu import GRAD_RL2, LOSS_RTOL, banner, device, np64, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+
+def sample_rows(n, seed):
+    r = np.random.default_rng(seed)
+    fixed = [0, 1, 63, 64, 255, 256, n // 2, n - 2, n - 1]
+    rnd = r.integers(0, n, size=6).tolist()
+    return np.array(sorted(set(v for v in fixed + rnd if 0 <= v < n)))
+
+
+def check_workload(name, causal, full_loss=False, grad_units=1):
+    wl = workloads.WORKLOADS[name]
+    banner(f"full-size {name} causal={causal}: generating inputs")
+    rels = workloads.make_inputs(wl)
+    dev = device()
+    scale = oracle.default_scale(wl.d)
+    for rel in rels:
+        banner(f"{name} {rel.name} causal={causal}: GPU fwd+bwd")
+        xt, xs = rel.x_t.to(dev), rel.x_s.to(dev)
+        f = relkl.relkl_fwd(xt, xs, causal=causal, want_row_kl=True)
+        gl = torch.ones((), dtype=torch.float32, device=dev)
+        dx = relkl.relkl_bwd(xt, xs, f["lse_t"], f["lse_s"], gl, causal=causal)
+        torch.cuda.synchronize()
+        loss = float(f["loss"].item())
+        row_kl = np64(f["row_kl"])
+        lse_t, lse_s = np64(f["lse_t"]), np64(f["lse_s"])
+        assert np.isfinite(loss) and loss > 0
+        assert np.all(np.isfinite(row_kl)) and np.all(np.isfinite(lse_t))
+        assert row_kl.min() >= -1e-5, row_kl.min()
+        assert abs(loss - row_kl.sum()) <= 1e-6 * abs(loss) + 1e-6
+        assert torch.isfinite(dx.float()).all()
+        B, H, N = row_kl.shape
+        units = [(0, 0), (B - 1, H - 1), (B // 2, H // 3)]
+        for k, (b, h) in enumerate(units):
+            rows = sample_rows(N, seed=k)
+            ut = rel.x_t[b, h].double().numpy()
+            us = rel.x_s[b, h].double().numpy()
+            lt, ls, kl = oracle.forward_unit(ut, us, scale, causal, chunk=512, rows=rows)
+            assert np.max(np.abs(lse_t[b, h, rows] - lt)) <= 5e-5 * max(1.0, np.max(np.abs(lt)))
+            assert np.max(np.abs(lse_s[b, h, rows] - ls)) <= 5e-5 * max(1.0, np.max(np.abs(ls)))
+            err = np.abs(row_kl[b, h, rows] - kl)
+            assert np.all(err <= 1e-3 * np.abs(kl) + 2e-6), (rows, row_kl[b, h, rows], kl)
+            if k < grad_units:
+                banner(f"{name} {rel.name}: oracle gradient of sampled rows, unit {(b, h)}")
+                if causal and N > 4096:
+                    # long causal rows: sample the last 1024 rows; their column terms only
+                    # involve rows j >= i, so only those rows' LSE is needed
+                    rows = np.array(sorted(set([N - 1024, N - 513, N - 257, N - 1]
+                                               + np.random.default_rng(k).integers(N - 1024, N, 4).tolist())))
+                    need = np.arange(rows.min(), N)
+                else:
+                    need = np.arange(N)
+                flt = np.full(N, np.nan)
+                fls = np.full(N, np.nan)
+                flt[need], fls[need], _ = oracle.forward_unit(ut, us, scale, causal, chunk=1024,
+                                                               rows=need)
+                g_ref = oracle.backward_unit(ut, us, scale, causal, 1.0, lse_t=flt, lse_s=fls,
+                                             rows=rows, chunk=1024)
+                g_got = np64(dx[b, h])[rows]
+                e = rel_l2(g_got, g_ref)
+                print(f"[parity] {name}/{rel.name} sampled-row grad rel-L2 {e:.3e}", flush=True)
+                assert e <= GRAD_RL2[torch.bfloat16]
+        if full_loss:
+            banner(f"{name} {rel.name}: full oracle loss")
+            fo = oracle.forward(rel.x_t.double().numpy(), rel.x_s.double().numpy(), scale, causal,
+                                chunk=1024)
+            e = abs(loss - fo["loss"]) / fo["loss"]
+            print(f"[parity] {name}/{rel.name} full loss rel err {e:.3e}", flush=True)
+            assert e <= LOSS_RTOL[torch.bfloat16]
+        del xt, xs, f, dx
+
+
+def test_llama2_4k_full():
+    check_workload("llama2_4k", True, full_loss=True, grad_units=2)
+
+
+def test_llama2_32k_sampled():
+    check_workload("llama2_32k", True)
+
+
+def test_batched_8k_causal_sampled():
+    check_workload("batched_8k", True)
+
+
+def test_batched_8k_noncausal_sampled():
+    check_workload("batched_8k", False)
+
+
+def test_gqa_16k_sampled():
+    check_workload("gqa_16k", True)
