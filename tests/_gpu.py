@@ -59,15 +59,17 @@ def fp32_floor(fo, x_s, scale):
     """Absolute error floors of fp32 on-chip arithmetic, for inputs whose result is much
     smaller than the terms that produce it (tiny N, nearly equal teacher and student).
 
-    Every probability is formed as exp(z - LSE) with LSE held in fp32, so each carries a
-    relative error of a few ulps of max|LSE|; a row's KL is a difference of O(1) terms,
-    and the gradient is a sum of |R| |x| terms (sum_j |R_s - R_t| <= 4 per row counting
-    the row and the transposed terms).  eta = 2^-20 (1 + max |LSE|).
+    A row's KL is a difference of O(1 + |LSE|) terms (cross-entropy minus entropy), so its
+    fp32 value carries an absolute error of a few ulps of that size: the loss floor is
+    2^-24 (1 + max|LSE|) per row.  Every probability is formed as exp(z - LSE) with LSE
+    held in fp32, so each carries a relative error of a few ulps of max|LSE|, and the
+    gradient is a sum of |R| |x| terms (sum_j |R_s - R_t| <= 4 per row counting the row
+    and the transposed terms): the gradient floor uses eta = 2^-20 (1 + max|LSE|).
     """
     lse_max = float(max(np.max(np.abs(fo["lse_t"])), np.max(np.abs(fo["lse_s"]))))
     eta = 2.0 ** -20 * (1.0 + lse_max)
     rows = fo["row_kl"].size
-    loss_floor = eta * rows
+    loss_floor = 2.0 ** -24 * (1.0 + lse_max) * rows
     xs = np64(x_s)
     row_norm_max = float(np.sqrt(np.max(np.sum(xs * xs, axis=-1))))
     grad_floor = 4.0 * eta * scale * row_norm_max * np.sqrt(xs.shape[0] * xs.shape[1] * xs.shape[2])

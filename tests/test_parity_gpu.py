@@ -11,8 +11,8 @@ import torch
 
 import oracle
 from attention_relation_distillation_amd import relkl, workloads
-from tests._gpu import (GRAD_RL2, assert_parity, banner, device, gpu_fwd_bwd, np64,
-                        oracle_fwd_bwd, rel_l2)
+from tests._gpu import (GRAD_RL2, LOSS_RTOL, assert_parity, banner, device, fp32_floor,
+                        gpu_fwd_bwd, np64, oracle_fwd_bwd, rel_l2)
 
 pytestmark = pytest.mark.gpu
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -88,7 +88,13 @@ def test_golden_closed_form():
                                 scale=case["scale"], g=case["g"])
             np.testing.assert_allclose(np64(f["lse_t"])[0, 0], case["lse_t"], rtol=2e-6, atol=2e-6)
             np.testing.assert_allclose(np64(f["lse_s"])[0, 0], case["lse_s"], rtol=2e-6, atol=2e-6)
-            assert float(f["loss"].item()) == pytest.approx(case["loss"], rel=1e-5)
+            # every row of these inputs is alike, so per-row fp32 errors add up instead of
+            # averaging out: gate = dtype gate + the fp32 floor of the row formula
+            ref = {k: np.array(case[k]) for k in ("lse_t", "lse_s", "row_kl")}
+            loss_floor, _ = fp32_floor(ref, x_s, case["scale"])
+            err = abs(float(f["loss"].item()) - case["loss"])
+            print(f"[parity] golden {case['name']} loss abs err {err:.3e} floor {loss_floor:.3e}")
+            assert err <= LOSS_RTOL[dtype] * case["loss"] + loss_floor
             rows = case["dx_rows"]
             got = np64(dx)[0, 0][rows]
             ref = np.array(case["dx"])
