@@ -14,7 +14,7 @@ namespace {
 using namespace lard;
 
 constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
-constexpr int kTargetWorkgroups = 512;  // two waves of workgroups over 256 CUs
+constexpr int kTargetWorkgroups = 1024;  // two rounds of two workgroups per CU over 256 CUs
 constexpr int kMaxSplits = 64;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -95,6 +95,10 @@ size_t fwd_workspace(const lard_relkl_desc* d) {
   return ((n * sizeof(double) + 255) / 256) * 256;
 }
 
+ReserveLayout reserve_of(const lard_relkl_desc* d) {
+  return reserve_layout((int64_t)d->B * d->H, d->N, d->d, d->dtype == LARD_BF16);
+}
+
 size_t bwd_workspace(const lard_relkl_desc* d) {
   const int s = choose_splits(d);
   if (s == 1) return 0;
@@ -126,19 +130,29 @@ size_t lard_relkl_workspace_size(const lard_relkl_desc* desc, int pass, lard_sta
   return pass == 0 ? fwd_workspace(desc) : bwd_workspace(desc);
 }
 
+size_t lard_relkl_reserve_size(const lard_relkl_desc* desc, lard_status* status) {
+  const lard_status s = check_desc(desc);
+  if (status) *status = s;
+  if (s != LARD_OK) return 0;
+  return reserve_of(desc).total;
+}
+
 lard_status lard_relkl_fwd(const lard_relkl_desc* desc, const void* x_teacher,
                            const void* x_student, float* lse_teacher, float* lse_student,
-                           float* row_kl, float* loss, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+                           float* row_kl, float* loss, void* reserve, size_t reserve_bytes,
+                           void* workspace, size_t workspace_bytes, void* stream) {
   lard_status s = check_desc(desc);
   if (s != LARD_OK) return s;
-  if (!x_teacher || !x_student || !lse_teacher || !lse_student || !loss || !workspace)
+  if (!x_teacher || !x_student || !lse_teacher || !lse_student || !loss || !workspace ||
+      !reserve)
     return LARD_ERR_INVALID_ARGUMENT;
   if (!aligned(x_teacher, 16) || !aligned(x_student, 16) || !aligned(workspace, 8) ||
-      !aligned(lse_teacher, 4) || !aligned(lse_student, 4) || !aligned(loss, 4) ||
-      (row_kl && !aligned(row_kl, 4)))
+      !aligned(reserve, 256) || !aligned(lse_teacher, 4) || !aligned(lse_student, 4) ||
+      !aligned(loss, 4) || (row_kl && !aligned(row_kl, 4)))
     return LARD_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < fwd_workspace(desc)) return LARD_ERR_WORKSPACE_TOO_SMALL;
+  const ReserveLayout R = reserve_of(desc);
+  if (reserve_bytes < R.total) return LARD_ERR_WORKSPACE_TOO_SMALL;
 
   FwdArgs a;
   memset(&a, 0, sizeof(a));
@@ -154,20 +168,25 @@ lard_status lard_relkl_fwd(const lard_relkl_desc* desc, const void* x_teacher,
   a.lse_s = lse_student;
   a.row_kl = row_kl;
   a.partial = static_cast<double*>(workspace);
+  char* rb = static_cast<char*>(reserve);
+  a.npad = (int32_t)R.npad;
+  a.x16_t = desc->dtype == LARD_BF16 ? reinterpret_cast<uint16_t*>(rb + R.x16_t) : nullptr;
+  a.x16_s = desc->dtype == LARD_BF16 ? reinterpret_cast<uint16_t*>(rb + R.x16_s) : nullptr;
+  a.r_t = reinterpret_cast<float*>(rb + R.r_t);
+  a.r_s = reinterpret_cast<float*>(rb + R.r_s);
   fill_map(a.map, desc);
   const int e = launch_fwd(a, desc->dtype == LARD_BF16, desc->d, desc->causal == 1, loss, stream);
   return e == 0 ? LARD_OK : LARD_ERR_HIP;
 }
 
 lard_status lard_relkl_bwd(const lard_relkl_desc* desc, const void* x_teacher,
-                           const void* x_student, const float* lse_teacher,
-                           const float* lse_student, const float* grad_loss,
-                           const lard_grad_desc* grad, void* dx_student, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+                           const void* x_student, const void* reserve, size_t reserve_bytes,
+                           const float* grad_loss, const lard_grad_desc* grad,
+                           void* dx_student, void* workspace, size_t workspace_bytes,
+                           void* stream) {
   lard_status s = check_desc(desc);
   if (s != LARD_OK) return s;
-  if (!grad || !x_teacher || !x_student || !lse_teacher || !lse_student || !grad_loss ||
-      !dx_student)
+  if (!grad || !x_teacher || !x_student || !reserve || !grad_loss || !dx_student)
     return LARD_ERR_INVALID_ARGUMENT;
   if (grad->dtype != LARD_FP32 && grad->dtype != LARD_BF16) return LARD_ERR_INVALID_ARGUMENT;
   if (grad->dtype == LARD_BF16 && desc->dtype != LARD_BF16) return LARD_ERR_UNSUPPORTED;
@@ -175,8 +194,10 @@ lard_status lard_relkl_bwd(const lard_relkl_desc* desc, const void* x_teacher,
   if (s != LARD_OK) return s;
   if (desc->N > 1 && grad->stride_n < desc->d) return LARD_ERR_INVALID_ARGUMENT;
   if (!aligned(x_teacher, 16) || !aligned(x_student, 16) || !aligned(dx_student, 16) ||
-      !aligned(lse_teacher, 4) || !aligned(lse_student, 4) || !aligned(grad_loss, 4))
+      !aligned(reserve, 256) || !aligned(grad_loss, 4))
     return LARD_ERR_INVALID_ARGUMENT;
+  const ReserveLayout R = reserve_of(desc);
+  if (reserve_bytes < R.total) return LARD_ERR_WORKSPACE_TOO_SMALL;
   const size_t need = bwd_workspace(desc);
   if (need > 0 && (!workspace || !aligned(workspace, 16))) return LARD_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < need) return LARD_ERR_WORKSPACE_TOO_SMALL;
@@ -194,8 +215,12 @@ lard_status lard_relkl_bwd(const lard_relkl_desc* desc, const void* x_teacher,
   a.splits = choose_splits(desc);
   a.scale = desc->scale;
   a.c2 = desc->scale * 1.4426950408889634f;
-  a.lse_t = lse_teacher;
-  a.lse_s = lse_student;
+  const char* rb = static_cast<const char*>(reserve);
+  a.npad = (int32_t)R.npad;
+  a.x16_t = desc->dtype == LARD_BF16 ? reinterpret_cast<const uint16_t*>(rb + R.x16_t) : nullptr;
+  a.x16_s = desc->dtype == LARD_BF16 ? reinterpret_cast<const uint16_t*>(rb + R.x16_s) : nullptr;
+  a.r_t = reinterpret_cast<const float*>(rb + R.r_t);
+  a.r_s = reinterpret_cast<const float*>(rb + R.r_s);
   a.grad_loss = grad_loss;
   a.dx = dx_student;
   a.partial = static_cast<float*>(workspace);
@@ -213,7 +238,7 @@ lard_status lard_relkl_bwd(const lard_relkl_desc* desc, const void* x_teacher,
     r.rows_pad = a.row_tiles * kBR;
     r.splits = a.splits;
     r.map = a.map;
-    e = launch_splitk_reduce(r, out_f32, true, stream);
+    e = launch_splitk_reduce(r, out_f32, stream);
     if (e != 0) return LARD_ERR_HIP;
   }
   return LARD_OK;

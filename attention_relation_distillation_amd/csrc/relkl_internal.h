@@ -11,12 +11,37 @@ namespace lard {
 
 // Work decomposition shared by host sizing and device kernels.
 constexpr int kWave = 64;
-constexpr int kWaves = 4;                 // waves per workgroup
+constexpr int kWaves = 4;                 // waves per workgroup (two workgroups per CU)
 constexpr int kThreads = kWave * kWaves;  // 256
-constexpr int kRowBlocks = 2;             // 32-row blocks held by one wave
-constexpr int kRowsPerWave = 32 * kRowBlocks;
-constexpr int kBR = kWaves * kRowsPerWave;  // rows of one row tile (256)
-constexpr int kBC = 64;                     // rows of one key tile staged in LDS
+constexpr int kBR = kWaves * 32;          // rows of one row tile: one 32-row block per wave
+constexpr int kBC = 64;                   // rows of one key tile staged in LDS
+
+inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+// Phase-1 state the forward leaves for the backward ("reserve"), per relation head unit:
+//  * bf16 inputs only: IEEE fp16 copies of the teacher and student rows, dense
+//    [units][N][d] each (the backward's operands; bf16 -> fp16 is exact for
+//    2^-17 <= |x| < 65504);
+//  * row statistics in log2 units, r = log2(sum_j 2^(S_ij c2 + b_i)) - b_i - 14, dense
+//    [units][Npad] with Npad = N rounded up to kBC, for teacher and student, so that
+//    R(i, j) * 2^14 = exp2(S_ij c2 - r_i).
+struct ReserveLayout {
+  size_t x16_t, x16_s, r_t, r_s, total;
+  int64_t npad;
+};
+
+inline ReserveLayout reserve_layout(int64_t units, int64_t N, int64_t d, bool fp16_copies) {
+  ReserveLayout L;
+  L.npad = round_up(N, kBC);
+  const size_t copy = fp16_copies ? (size_t)round_up(units * N * d * 2, 256) : 0;
+  const size_t stats = (size_t)round_up(units * L.npad * 4, 256);
+  L.x16_t = 0;
+  L.x16_s = copy;
+  L.r_t = 2 * copy;
+  L.r_s = 2 * copy + stats;
+  L.total = 2 * copy + 2 * stats;
+  return L;
+}
 
 struct UnitMap {
   int32_t head_map[LARD_MAX_HEADS];
@@ -29,17 +54,22 @@ struct FwdArgs {
   int64_t s_sb, s_sh, s_sn;
   int32_t B, H, N;
   int32_t row_tiles;  // ceil(N / kBR)
+  int32_t npad;       // reserve statistics stride per unit
   float scale;        // logit scale
   float c2;           // scale * log2(e)
   float* lse_t;
   float* lse_s;
   float* row_kl;      // may be null
   double* partial;    // [B*H*row_tiles]
+  uint16_t* x16_t;    // reserve fp16 copies (bf16 inputs) or null
+  uint16_t* x16_s;
+  float* r_t;         // reserve log2 statistics
+  float* r_s;
   UnitMap map;
 };
 
 struct BwdArgs {
-  const void* x_t;
+  const void* x_t;    // inputs (read by the fp32 path)
   const void* x_s;
   int64_t t_sb, t_sh, t_sn;
   int64_t s_sb, s_sh, s_sn;
@@ -48,10 +78,13 @@ struct BwdArgs {
   int32_t row_tiles;
   int32_t key_tiles;   // ceil(N / kBC)
   int32_t splits;      // split-K count over key tiles
+  int32_t npad;
   float scale;
   float c2;
-  const float* lse_t;
-  const float* lse_s;
+  const uint16_t* x16_t;  // reserve fp16 copies (bf16 path)
+  const uint16_t* x16_s;
+  const float* r_t;
+  const float* r_s;
   const float* grad_loss;
   void* dx;            // final gradient (splits == 1)
   float* partial;      // [splits][B*H][row_tiles*kBR][d] (splits > 1)
@@ -74,6 +107,6 @@ int launch_fwd(const FwdArgs& a, bool in_bf16, int d, bool causal, float* loss,
                void* stream);
 int launch_bwd(const BwdArgs& a, bool in_bf16, int d, bool causal, bool out_f32,
                void* stream);
-int launch_splitk_reduce(const ReduceArgs& a, bool out_f32, bool out_bf16_ok, void* stream);
+int launch_splitk_reduce(const ReduceArgs& a, bool out_f32, void* stream);
 
 }  // namespace lard

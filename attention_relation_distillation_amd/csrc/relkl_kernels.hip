@@ -7,28 +7,33 @@
 // dL/dZ_s = g * (R_s - R_t).  The arXiv abstract (mlsanity.com) states that the kernel
 // fuses the logit recomputation into the backward and is exact.
 //
-// Layout of the work (one workgroup = 4 wave64s, 1 workgroup per CU):
-//  * A row tile is 256 consecutive rows i of one (batch, head) unit; each wave owns 64
-//    of them as two 32-row blocks and keeps their X_t and X_s rows in registers as
-//    MFMA B operands.
-//  * Key tiles of 64 rows j are staged through LDS (register-prefetched one tile ahead).
+// Layout of the work (one workgroup = 4 wave64s; two workgroups per CU, so every SIMD
+// runs two waves and one wave's exp/VALU work overlaps the other's MFMA work):
+//  * A row tile is 128 consecutive rows i of one (batch, head) unit; each wave owns 32
+//    of them and keeps their teacher and student rows in registers as MFMA B operands.
+//  * Key tiles of 64 rows j are copied global -> LDS by the DMA path
+//    (global_load_lds_dwordx4), double-buffered, one barrier per tile.  LDS rows are
+//    unpadded; their 16-byte chunks are XOR-swizzled by the row so that both the
+//    16-byte fragment reads of the score contraction and the transposed 8-byte reads of
+//    the gradient contraction hit distinct banks.
 //  * Score blocks are computed transposed, S^T[j][i] = <X[j], X[i]>, with
-//    v_mfma_f32_32x32x16_bf16 (fp32 inputs: v_mfma_f32_32x32x2f32), so that a lane holds
-//    one row i and 16 of its columns j: the row statistics reduce inside the lane, and
-//    the probability block is already in the A-operand layout of the next contraction.
-//  * Forward: one online sweep per row keeps (max, sum, sum of e_t * (S_t - S_s)) for
-//    teacher and student; the two half-waves that share a row merge at the end.
+//    v_mfma_f32_32x32x16 (fp32 inputs: v_mfma_f32_32x32x2f32), so that a lane holds one
+//    row i and 16 of its columns j: row statistics reduce inside the lane, and the
+//    probability block is already in the A-operand layout of the gradient contraction.
+//  * Forward: one online sweep per row keeps (bias, sum, sum of e_t (S_t - S_s)) for
+//    teacher and student; the two half-waves sharing a row merge at the end.  It also
+//    writes the reserve: fp16 copies of its rows (bf16 inputs) and the row statistics
+//    in log2 units.
 //  * Backward: the owner of row tile I sweeps the whole row (all key tiles), forms
 //    W = dZ + dZ^T block by block (row statistics below the diagonal, column statistics
-//    above it, both on it), rounds W * 2^14 to fp16 and accumulates W X_s on
-//    v_mfma_f32_32x32x16_f16 from a transposed fp16 copy of the key tile in LDS.
-//    No atomics: every output row has exactly one owner (times an optional split over
-//    key tiles reduced in a fixed order).
+//    above it, both on it), carries W * 2^14 as fp16 and accumulates W X_s on
+//    v_mfma_f32_32x32x16_f16, reading X_s transposed from the row-major key tile with
+//    ds_read_b64_tr_b16.  No atomics: every output row has one owner (times an optional
+//    split over key tiles reduced in a fixed order).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
-#include <string.h>
 
 #include "relkl_internal.h"
 
@@ -36,30 +41,36 @@ namespace lard {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define LDS_AS __attribute__((address_space(3)))
 
 constexpr float kNegBig = -1.0e30f;  // finite "minus infinity" for masked logits
-constexpr float kPosBig = 1.0e30f;   // LSE of rows beyond N (probabilities become 0)
-constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kPosBig = 1.0e30f;   // statistic of rows beyond N (probabilities become 0)
 constexpr float kWScaleLog2 = 14.0f;  // W is carried as W * 2^14 through fp16
+constexpr float kLn2 = 0.6931471805599453f;
 
 // ------------------------------------------------------------------ element traits
 // A "fragment" is 8 consecutive elements along d of one row: the k-chunk one lane
 // supplies to a 16-deep step of the score contraction.
-struct Bf16In {
+struct Bf16In {  // bf16 inputs as given by the caller (forward)
   using elem_t = uint16_t;
   using frag_t = bf16x8;
-  using gfrag_t = f16x8;   // operand type of the gradient contraction
   static constexpr int kES = 2;
 };
-struct F32In {
+struct F16Op {   // fp16 reserve copies (backward of bf16 inputs)
+  using elem_t = uint16_t;
+  using frag_t = f16x8;
+  static constexpr int kES = 2;
+};
+struct F32In {   // fp32 inputs (forward and backward)
   using elem_t = float;
   using frag_t = f32x8;
-  using gfrag_t = f32x8;
   static constexpr int kES = 4;
 };
 
@@ -80,30 +91,14 @@ __device__ __forceinline__ f32x16 mma_k16(const f32x8& a, const f32x8& b, f32x16
 
 template <class In>
 __device__ __forceinline__ typename In::frag_t load_frag_global(const typename In::elem_t* p) {
-  typename In::frag_t f;
   if constexpr (In::kES == 2) {
-    u32x4 v = *reinterpret_cast<const u32x4*>(p);
-    f = __builtin_bit_cast(bf16x8, v);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+    return __builtin_bit_cast(typename In::frag_t, v);
   } else {
-    f32x4 lo = *reinterpret_cast<const f32x4*>(p);
-    f32x4 hi = *reinterpret_cast<const f32x4*>(p + 4);
-    f = f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(p + 4);
+    return f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
-  return f;
-}
-
-template <class In>
-__device__ __forceinline__ typename In::frag_t load_frag_lds(const char* p) {
-  typename In::frag_t f;
-  if constexpr (In::kES == 2) {
-    u32x4 v = *reinterpret_cast<const u32x4*>(p);
-    f = __builtin_bit_cast(bf16x8, v);
-  } else {
-    f32x4 lo = *reinterpret_cast<const f32x4*>(p);
-    f32x4 hi = *reinterpret_cast<const f32x4*>(p + 16);
-    f = f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  }
-  return f;
 }
 
 // Map the hardware workgroup index to a work index such that the workgroups the
@@ -124,157 +119,61 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// ------------------------------------------------------------------ key-tile staging
-// Byte pitch of a row-major LDS tile row (16 bytes of padding keep the 16-byte fragment
-// reads of 8 consecutive rows on distinct banks).
-template <class In, int D>
-struct Tile {
-  static constexpr int kPitch = D * In::kES + 16;
-  static constexpr int kBytes = kBC * kPitch;
-  static constexpr int kChunksPerRow = D * In::kES / 16;
-  static constexpr int kChunks = kBC * kChunksPerRow;
-  static constexpr int kPerThread = kChunks / kThreads;
-  static_assert(kChunks % kThreads == 0, "tile chunks must divide evenly");
+// Wait for this wave's outstanding vector-memory operations (the LDS DMA included).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// ------------------------------------------------------------------ LDS key tiles
+// Row-major [kBC][D] tile, 16-byte chunks of row r stored at chunk (c ^ swz(r)).
+// swz sends 8 consecutive rows to 8 distinct chunk positions (conflict-free 16-byte
+// fragment reads), and 4 consecutive rows to 4 distinct chunk pairs (conflict-free
+// transposed reads of two adjacent chunks).
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+template <int D, int ES>
+struct Geo {
+  static constexpr int kRowBytes = D * ES;
+  static constexpr int kCPR = kRowBytes / 16;  // chunks per row
+  static constexpr int kTileBytes = kBC * kRowBytes;
+  static constexpr int kDmaPerWave = kBC * kCPR / (kWave * kWaves);
+  static_assert(kCPR >= 8, "swizzle needs at least 8 chunks per row");
+  static_assert(kBC * kCPR % (kWave * kWaves) == 0, "tile must split evenly over the waves");
+  __device__ static __forceinline__ int off(int r, int c) { return r * kRowBytes + ((c ^ swz(r)) << 4); }
 };
 
-// Transposed copy of the student key tile for the gradient contraction: [D][kBC] of the
-// gradient operand type (fp16 for bf16 inputs, fp32 for fp32 inputs).
-template <class In, int D>
-struct TileT {
-  static constexpr int kGES = In::kES == 2 ? 2 : 4;
-  static constexpr int kPitch = kBC * kGES + (kGES == 2 ? 8 : 16);
-  static constexpr int kBytes = D * kPitch;
-};
-
-// Coalesced mapping: chunk c = tid + 256 q covers row c / CPR, 16-byte column c % CPR.
-template <class In, int D>
-struct TileRegs {
-  u32x4 v[Tile<In, D>::kPerThread];
-};
-
-template <class In, int D>
-__device__ __forceinline__ void tile_load(TileRegs<In, D>& r, const typename In::elem_t* base,
-                                          int64_t sn, int j0, int N, int tid) {
-  using T = Tile<In, D>;
+// Copy key rows [j0, j0 + kBC) of one unit (row stride `sn_bytes`) into an LDS tile.  Lane
+// l of DMA instruction q of wave w fills LDS chunk slot t = (w Q + q) 64 + l (the DMA
+// writes lane l at base + 16 l); the slot's row and swizzled chunk say which global
+// chunk it takes.  Rows beyond N read row N-1 (finite values, masked by the callers).
+template <int D, int ES>
+__device__ __forceinline__ void dma_tile(const char* base, int64_t sn_bytes, int j0, int N,
+                                         char* lds, int wave, int lane) {
+  using G = Geo<D, ES>;
 #pragma unroll
-  for (int q = 0; q < T::kPerThread; ++q) {
-    const int c = tid + kThreads * q;
-    const int row = c / T::kChunksPerRow;
-    const int col = c % T::kChunksPerRow;
-    const int j = j0 + row;
-    if (j < N) {
-      const char* p = reinterpret_cast<const char*>(base + (int64_t)j * sn) + col * 16;
-      r.v[q] = *reinterpret_cast<const u32x4*>(p);
-    } else {
-      r.v[q] = u32x4{0u, 0u, 0u, 0u};
-    }
+  for (int q = 0; q < G::kDmaPerWave; ++q) {
+    const int slot0 = (wave * G::kDmaPerWave + q) * kWave;
+    const int t = slot0 + lane;
+    const int r = t / G::kCPR;
+    const int c = (t % G::kCPR) ^ swz(r);
+    const int j = min(j0 + r, N - 1);
+    const char* g = base + (int64_t)j * sn_bytes + c * 16;
+    __builtin_amdgcn_global_load_lds(g, (LDS_AS void*)(lds + slot0 * 16), 16, 0, 0);
   }
 }
 
 template <class In, int D>
-__device__ __forceinline__ void tile_store(const TileRegs<In, D>& r, char* lds, int tid) {
-  using T = Tile<In, D>;
-#pragma unroll
-  for (int q = 0; q < T::kPerThread; ++q) {
-    const int c = tid + kThreads * q;
-    const int row = c / T::kChunksPerRow;
-    const int col = c % T::kChunksPerRow;
-    *reinterpret_cast<u32x4*>(lds + row * T::kPitch + col * 16) = r.v[q];
-  }
-}
-
-// Student key tile for the backward: each lane loads rows (2p, 2p+1) of one 16-byte
-// column so that it can write the transposed fp16 copy as packed pairs (one dword per
-// d: 32 lanes fill 128 contiguous bytes).  fp32 inputs use one row per lane instead.
-template <class In, int D>
-struct StuRegs {
-  u32x4 v[Tile<In, D>::kPerThread];
-};
-
-template <class In, int D>
-__device__ __forceinline__ void stu_coords(int q, int tid, int& row, int& col) {
-  using T = Tile<In, D>;
-  const int lane = tid & 63, wave = tid >> 6;
+__device__ __forceinline__ typename In::frag_t lds_frag(const char* tile, int r, int k0) {
+  using G = Geo<D, In::kES>;
   if constexpr (In::kES == 2) {
-    // per wave and pair-step: 32 row pairs x 2 columns = 64 lanes; q = 2 s + t (t: row of pair)
-    const int s = q >> 1, t = q & 1;
-    const int colpairs = T::kChunksPerRow / 2;
-    const int cp = wave * (colpairs / kWaves) + s;  // column pair handled in step s
-    row = 2 * (lane & 31) + t;
-    col = 2 * cp + (lane >> 5);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(tile + G::off(r, k0 >> 3));
+    return __builtin_bit_cast(typename In::frag_t, v);
   } else {
-    // one row per lane, columns spread over waves and steps
-    row = lane;
-    col = wave * (T::kChunksPerRow / kWaves) + q;
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(tile + G::off(r, k0 >> 2));
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(tile + G::off(r, (k0 >> 2) + 1));
+    return f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
 }
 
-template <class In, int D>
-__device__ __forceinline__ void stu_load(StuRegs<In, D>& r, const typename In::elem_t* base,
-                                         int64_t sn, int j0, int N, int tid) {
-  using T = Tile<In, D>;
-#pragma unroll
-  for (int q = 0; q < T::kPerThread; ++q) {
-    int row, col;
-    stu_coords<In, D>(q, tid, row, col);
-    const int j = j0 + row;
-    if (j < N) {
-      const char* p = reinterpret_cast<const char*>(base + (int64_t)j * sn) + col * 16;
-      r.v[q] = *reinterpret_cast<const u32x4*>(p);
-    } else {
-      r.v[q] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-}
-
-__device__ __forceinline__ _Float16 bf16_bits_to_f16(uint32_t bits16) {
-  return (_Float16)__uint_as_float(bits16 << 16);
-}
-
-template <class In, int D>
-__device__ __forceinline__ void stu_store(const StuRegs<In, D>& r, char* lds_rm, char* lds_t,
-                                          int tid) {
-  using T = Tile<In, D>;
-  using TT = TileT<In, D>;
-#pragma unroll
-  for (int q = 0; q < T::kPerThread; ++q) {
-    int row, col;
-    stu_coords<In, D>(q, tid, row, col);
-    *reinterpret_cast<u32x4*>(lds_rm + row * T::kPitch + col * 16) = r.v[q];
-  }
-  if constexpr (In::kES == 2) {
-#pragma unroll
-    for (int s = 0; s < T::kPerThread / 2; ++s) {
-      int row, col;
-      stu_coords<In, D>(2 * s, tid, row, col);  // row is even: the pair (row, row + 1)
-      const u32x4 a = r.v[2 * s], b = r.v[2 * s + 1];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t wa = a[e >> 1], wb = b[e >> 1];
-        const uint32_t ba = (e & 1) ? (wa >> 16) : (wa & 0xffffu);
-        const uint32_t bb = (e & 1) ? (wb >> 16) : (wb & 0xffffu);
-        const _Float16 ha = bf16_bits_to_f16(ba), hb = bf16_bits_to_f16(bb);
-        const uint32_t packed = (uint32_t)__builtin_bit_cast(uint16_t, ha) |
-                                ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
-        const int dcol = col * 8 + e;
-        *reinterpret_cast<uint32_t*>(lds_t + dcol * TT::kPitch + row * 2) = packed;
-      }
-    }
-  } else {
-#pragma unroll
-    for (int q = 0; q < T::kPerThread; ++q) {
-      int row, col;
-      stu_coords<In, D>(q, tid, row, col);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int dcol = col * 4 + e;
-        *reinterpret_cast<uint32_t*>(lds_t + dcol * TT::kPitch + row * 4) = r.v[q][e];
-      }
-    }
-  }
-}
-
-// ------------------------------------------------------------------ forward kernel
+// ------------------------------------------------------------------ forward
 // Online update of one lane's row statistics with the 16 columns it holds of a 32x32
 // score block (raw scores S; logits z = scale S; c2 = scale log2 e).
 //   b: exponent bias in use, b = -(running max of S) * c2, rounded once;
@@ -328,16 +227,32 @@ __device__ __forceinline__ void online_update(const f32x16& st, const f32x16& ss
   b_s = bn_s;
 }
 
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8_bits(const bf16x8& v) {
+  const u32x4 w = __builtin_bit_cast(u32x4, v);
+  u32x4 o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float lo = __uint_as_float(w[q] << 16);
+    const float hi = __uint_as_float(w[q] & 0xffff0000u);
+    // exact for values representable in fp16; round-toward-zero only matters beyond that
+    o[q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+  }
+  return o;
+}
+
 template <class In, int D, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void relkl_fwd_kernel(const FwdArgs a) {
   using elem_t = typename In::elem_t;
   using frag_t = typename In::frag_t;
-  using T = Tile<In, D>;
+  using G = Geo<D, In::kES>;
   constexpr int KS = D / 16;  // 16-deep steps over d
+  constexpr int kStage = 2 * G::kTileBytes;
 
-  __shared__ __attribute__((aligned(16))) char lds_t[T::kBytes];
-  __shared__ __attribute__((aligned(16))) char lds_s[T::kBytes];
+  // two stage buffers as distinct objects, so the compiler can tell the DMA into one
+  // from the reads of the other and does not wait for the DMA before those reads
+  __shared__ __attribute__((aligned(1024))) char lds0[kStage];
+  __shared__ __attribute__((aligned(1024))) char lds1[kStage];
   __shared__ double red[kWaves];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -352,117 +267,107 @@ void relkl_fwd_kernel(const FwdArgs a) {
   const int hin = a.map.head_map[h];
   const elem_t* xt = reinterpret_cast<const elem_t*>(a.x_t) + b * a.t_sb + hin * a.t_sh;
   const elem_t* xs = reinterpret_cast<const elem_t*>(a.x_s) + b * a.s_sb + hin * a.s_sh;
+  const char* xt_c = reinterpret_cast<const char*>(xt);
+  const char* xs_c = reinterpret_cast<const char*>(xs);
+  const int64_t tsn_b = a.t_sn * In::kES, ssn_b = a.s_sn * In::kES;
 
   const int i0 = I * kBR;
-  const int wrow0 = i0 + wave * kRowsPerWave;
-
-  // Own rows as B operands: lane (l32, hh) holds row wrow0 + 32 rb + l32, elements
-  // 16 ks + 8 hh .. +7.
-  frag_t qt[kRowBlocks][KS], qs[kRowBlocks][KS];
-#pragma unroll
-  for (int rb = 0; rb < kRowBlocks; ++rb) {
-    const int row = wrow0 + 32 * rb + l32;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (row < N) {
-        qt[rb][ks] = load_frag_global<In>(xt + (int64_t)row * a.t_sn + 16 * ks + 8 * hh);
-        qs[rb][ks] = load_frag_global<In>(xs + (int64_t)row * a.s_sn + 16 * ks + 8 * hh);
-      } else {
-        qt[rb][ks] = frag_t{};
-        qs[rb][ks] = frag_t{};
-      }
-    }
-  }
-
-  // Online statistics over this lane's column subset, in raw-score units.
-  const float c2 = a.c2;
-  const float b_init = -kNegBig * c2;  // bias of an empty row: every real bias is below it
-  float b_t[kRowBlocks], l_t[kRowBlocks], acc_a[kRowBlocks], b_s[kRowBlocks], l_s[kRowBlocks];
-#pragma unroll
-  for (int rb = 0; rb < kRowBlocks; ++rb) {
-    b_t[rb] = b_init; l_t[rb] = 0.f; acc_a[rb] = 0.f; b_s[rb] = b_init; l_s[rb] = 0.f;
-  }
+  const int ib0 = i0 + 32 * wave;  // first row of this wave
+  const int row = ib0 + l32;       // this lane's row
 
   const int j_end = CAUSAL ? min(N, i0 + kBR) : N;
   const int n_tiles = (j_end + kBC - 1) / kBC;
+  dma_tile<D, In::kES>(xt_c, tsn_b, 0, N, lds0, wave, lane);
+  dma_tile<D, In::kES>(xs_c, ssn_b, 0, N, lds0 + G::kTileBytes, wave, lane);
 
-  TileRegs<In, D> pt, ps;
-  tile_load<In, D>(pt, xt, a.t_sn, 0, N, tid);
-  tile_load<In, D>(ps, xs, a.s_sn, 0, N, tid);
-
-  for (int jt = 0; jt < n_tiles; ++jt) {
-    if (jt > 0) __syncthreads();
-    tile_store<In, D>(pt, lds_t, tid);
-    tile_store<In, D>(ps, lds_s, tid);
-    __syncthreads();
-    if (jt + 1 < n_tiles) {
-      tile_load<In, D>(pt, xt, a.t_sn, (jt + 1) * kBC, N, tid);
-      tile_load<In, D>(ps, xs, a.s_sn, (jt + 1) * kBC, N, tid);
+  // Own rows as B operands: lane (l32, hh) holds elements 16 ks + 8 hh .. +7 of its row.
+  frag_t qt[KS], qs[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (row < N) {
+      qt[ks] = load_frag_global<In>(xt + (int64_t)row * a.t_sn + 16 * ks + 8 * hh);
+      qs[ks] = load_frag_global<In>(xs + (int64_t)row * a.s_sn + 16 * ks + 8 * hh);
+    } else {
+      qt[ks] = frag_t{};
+      qs[ks] = frag_t{};
     }
-    const int j0 = jt * kBC;
-#pragma unroll
-    for (int jb = 0; jb < kBC / 32; ++jb) {
-      const int jb0 = j0 + 32 * jb;
-      if (jb0 >= N) break;
-      if (CAUSAL && jb0 > wrow0 + kRowsPerWave - 1) break;  // above every row of the wave
-      f32x16 st[kRowBlocks], ss[kRowBlocks];
-#pragma unroll
-      for (int rb = 0; rb < kRowBlocks; ++rb) { st[rb] = f32x16{}; ss[rb] = f32x16{}; }
-      const int lrow = 32 * jb + l32;
+  }
+  if constexpr (In::kES == 2) {
+    // reserve: fp16 copies of this lane's part of its row
+    if (row < N) {
+      const int64_t o = ((int64_t)unit * N + row) * D + 8 * hh;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int off = lrow * T::kPitch + (16 * ks + 8 * hh) * In::kES;
-        const frag_t at = load_frag_lds<In>(lds_t + off);
-        const frag_t as = load_frag_lds<In>(lds_s + off);
-#pragma unroll
-        for (int rb = 0; rb < kRowBlocks; ++rb) {
-          st[rb] = mma_k16(at, qt[rb][ks], st[rb]);
-          ss[rb] = mma_k16(as, qs[rb][ks], ss[rb]);
-        }
-      }
-#pragma unroll
-      for (int rb = 0; rb < kRowBlocks; ++rb) {
-        const int ib0 = wrow0 + 32 * rb;
-        const int i = ib0 + l32;
-        const bool need_mask = (CAUSAL && jb0 + 31 > ib0) || (jb0 + 32 > N);
-        if (need_mask)
-          online_update<true, CAUSAL>(st[rb], ss[rb], jb0, i, hh, N, c2, b_t[rb], l_t[rb],
-                                      acc_a[rb], b_s[rb], l_s[rb]);
-        else
-          online_update<false, CAUSAL>(st[rb], ss[rb], jb0, i, hh, N, c2, b_t[rb], l_t[rb],
-                                       acc_a[rb], b_s[rb], l_s[rb]);
+        *reinterpret_cast<u32x4*>(a.x16_t + o + 16 * ks) = bf16x8_to_f16x8_bits(qt[ks]);
+        *reinterpret_cast<u32x4*>(a.x16_s + o + 16 * ks) = bf16x8_to_f16x8_bits(qs[ks]);
       }
     }
+  }
+
+  const float c2 = a.c2;
+  const float b_init = -kNegBig * c2;  // bias of an empty row: every real bias is below it
+  float b_t = b_init, l_t = 0.f, acc_a = 0.f, b_s = b_init, l_s = 0.f;
+
+  auto step = [&](int kt, const char* cur, char* nxt) __attribute__((always_inline)) {
+    wait_vmem();
+    __syncthreads();
+    if (kt + 1 < n_tiles) {
+      dma_tile<D, In::kES>(xt_c, tsn_b, (kt + 1) * kBC, N, nxt, wave, lane);
+      dma_tile<D, In::kES>(xs_c, ssn_b, (kt + 1) * kBC, N, nxt + G::kTileBytes, wave, lane);
+    }
+    const char* tile_t = cur;
+    const char* tile_s = cur + G::kTileBytes;
+#pragma unroll 1
+    for (int jb = 0; jb < kBC / 32; ++jb) {
+      const int jb0 = kt * kBC + 32 * jb;
+      if (jb0 >= N) break;
+      if (CAUSAL && jb0 > ib0 + 31) break;  // above every row of the wave
+      f32x16 st = f32x16{}, ss = f32x16{};
+      const int lr = 32 * jb + l32;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const frag_t at = lds_frag<In, D>(tile_t, lr, 16 * ks + 8 * hh);
+        const frag_t as = lds_frag<In, D>(tile_s, lr, 16 * ks + 8 * hh);
+        st = mma_k16(at, qt[ks], st);
+        ss = mma_k16(as, qs[ks], ss);
+      }
+      const bool need_mask = (CAUSAL && jb0 + 31 > ib0) || (jb0 + 32 > N);
+      if (need_mask)
+        online_update<true, CAUSAL>(st, ss, jb0, row, hh, N, c2, b_t, l_t, acc_a, b_s, l_s);
+      else
+        online_update<false, CAUSAL>(st, ss, jb0, row, hh, N, c2, b_t, l_t, acc_a, b_s, l_s);
+    }
+  };
+  for (int kt = 0; kt < n_tiles; kt += 2) {
+    step(kt, lds0, lds1);
+    if (kt + 1 < n_tiles) step(kt + 1, lds1, lds0);
   }
 
   // Merge the two half-waves (lanes l and l ^ 32 hold the same row) and finish, in log2
   // units:  LSE = ln2 (log2 L - b),
   //         KL  = ln2 (c2 A_t / L_t + (b_t - b_s) - log2(L_t / L_s))
   // (KL_i = E_t[z_t - z_s] - (LSE_t - LSE_s), with the LSE difference taken as a ratio).
+  const float ob_t = __shfl_xor(b_t, 32), ol_t = __shfl_xor(l_t, 32);
+  const float oa = __shfl_xor(acc_a, 32);
+  const float ob_s = __shfl_xor(b_s, 32), ol_s = __shfl_xor(l_s, 32);
+  const float B_t = fminf(b_t, ob_t), B_s = fminf(b_s, ob_s);
+  const float f1t = fast_exp2(B_t - b_t), f2t = fast_exp2(B_t - ob_t);
+  const float f1s = fast_exp2(B_s - b_s), f2s = fast_exp2(B_s - ob_s);
+  const float L_t = l_t * f1t + ol_t * f2t;
+  const float A_t = acc_a * f1t + oa * f2t;
+  const float L_s = l_s * f1s + ol_s * f2s;
+  const float lg_t = log2f(L_t), lg_s = log2f(L_s);
+  const float kl = kLn2 * (c2 * (A_t / L_t) + (B_t - B_s) - log2f(L_t / L_s));
   double kl_sum = 0.0;
-  constexpr float kLn2 = 0.6931471805599453f;
-#pragma unroll
-  for (int rb = 0; rb < kRowBlocks; ++rb) {
-    const float ob_t = __shfl_xor(b_t[rb], 32), ol_t = __shfl_xor(l_t[rb], 32);
-    const float oa = __shfl_xor(acc_a[rb], 32);
-    const float ob_s = __shfl_xor(b_s[rb], 32), ol_s = __shfl_xor(l_s[rb], 32);
-    const float B_t = fminf(b_t[rb], ob_t), B_s = fminf(b_s[rb], ob_s);
-    const float f1t = fast_exp2(B_t - b_t[rb]), f2t = fast_exp2(B_t - ob_t);
-    const float f1s = fast_exp2(B_s - b_s[rb]), f2s = fast_exp2(B_s - ob_s);
-    const float L_t = l_t[rb] * f1t + ol_t * f2t;
-    const float A_t = acc_a[rb] * f1t + oa * f2t;
-    const float L_s = l_s[rb] * f1s + ol_s * f2s;
-    const float lse_t = (log2f(L_t) - B_t) * kLn2;
-    const float lse_s = (log2f(L_s) - B_s) * kLn2;
-    const float kl = kLn2 * (c2 * (A_t / L_t) + (B_t - B_s) - log2f(L_t / L_s));
-    const int i = wrow0 + 32 * rb + l32;
-    if (hh == 0 && i < N) {
-      const int64_t o = (int64_t)unit * N + i;
-      a.lse_t[o] = lse_t;
-      a.lse_s[o] = lse_s;
-      if (a.row_kl) a.row_kl[o] = kl;
-      kl_sum += (double)kl;
-    }
+  if (hh == 0 && row < N) {
+    const int64_t o = (int64_t)unit * N + row;
+    a.lse_t[o] = (lg_t - B_t) * kLn2;
+    a.lse_s[o] = (lg_s - B_s) * kLn2;
+    if (a.row_kl) a.row_kl[o] = kl;
+    const int64_t ro = (int64_t)unit * a.npad + row;
+    a.r_t[ro] = (lg_t - B_t) - kWScaleLog2;
+    a.r_s[ro] = (lg_s - B_s) - kWScaleLog2;
+    kl_sum = (double)kl;
   }
   // Deterministic workgroup sum in fp64.
 #pragma unroll
@@ -492,79 +397,111 @@ __global__ __launch_bounds__(256) void loss_reduce_kernel(const double* partial,
   if (threadIdx.x == 0) loss[0] = (float)red[0];
 }
 
-// ------------------------------------------------------------------ backward kernel
-template <class In, int D>
-__device__ __forceinline__ typename In::gfrag_t load_gfrag_lds(const char* lds_t, int dcol,
-                                                               int jcol0) {
-  using TT = TileT<In, D>;
-  typename In::gfrag_t f;
-  const char* p = lds_t + dcol * TT::kPitch;
-  if constexpr (In::kES == 2) {
-    const f16x4 lo = *reinterpret_cast<const f16x4*>(p + jcol0 * 2);
-    const f16x4 hi = *reinterpret_cast<const f16x4*>(p + (jcol0 + 8) * 2);
-    f = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  } else {
-    const f32x4 lo = *reinterpret_cast<const f32x4*>(p + jcol0 * 4);
-    const f32x4 hi = *reinterpret_cast<const f32x4*>(p + (jcol0 + 8) * 4);
-    f = f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  }
-  return f;
-}
-
+// ------------------------------------------------------------------ backward
 // W block (times 2^14) of one lane: the 16 columns j = jb0 + 8 (r/4) + 4 hh + (r%4) of
-// its row i, from the transposed score blocks st / ss (raw scores).
-//   row term  (entry (i, j) of dZ, normalised by the LSE of row i):  kept if j <= i
-//   col term  (entry (j, i) of dZ, normalised by the LSE of row j):  kept if i <= j
+// its row i, from the transposed score blocks st / ss (raw scores) and the log2 row
+// statistics r (R * 2^14 = exp2(S c2 - r)).
+//   row term  (entry (i, j) of dZ, normalised by the statistic of row i):  kept if j <= i
+//   col term  (entry (j, i) of dZ, normalised by the statistic of row j):  kept if i <= j
 // CLS 0: non-causal (both terms everywhere); 1: block strictly below the diagonal (row
 // term only); 2: strictly above (column term only); 3: diagonal block (both, masked).
-// TAIL zeroes columns j >= N (only the non-causal row term can see them).
-template <class In, int CLS, bool TAIL>
-__device__ __forceinline__ void make_w(const f32x16& st, const f32x16& ss, float rlt, float rls,
+// TAIL zeroes columns j >= N (their staged rows and statistics are copies of row N-1).
+template <int CLS, bool TAIL>
+__device__ __forceinline__ void make_w(const f32x16& st, const f32x16& ss, float rt, float rs,
                                        const float* clt, const float* cls, int hh, int di,
-                                       int n_left, float c2, typename In::gfrag_t (&wf)[2]) {
+                                       int n_left, float c2, f32x8 (&w32)[2]) {
   float wv[16];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int dj = 8 * (r >> 2) + 4 * hh + (r & 3);  // j - jb0
-    float v = 0.f;
-    if constexpr (CLS != 2) {
-      const float rt = fast_exp2(fmaf(ss[r], c2, -rls)) - fast_exp2(fmaf(st[r], c2, -rlt));
-      v = (CLS == 3) ? (dj <= di ? rt : 0.f) : rt;
-    }
+  for (int q = 0; q < 4; ++q) {
+    f32x4 ct4 = f32x4{0.f, 0.f, 0.f, 0.f}, cs4 = ct4;
     if constexpr (CLS != 1) {
-      const float ct = fast_exp2(fmaf(ss[r], c2, -cls[dj])) - fast_exp2(fmaf(st[r], c2, -clt[dj]));
-      v += (CLS == 3) ? (dj >= di ? ct : 0.f) : ct;
+      ct4 = *reinterpret_cast<const f32x4*>(clt + 8 * q + 4 * hh);
+      cs4 = *reinterpret_cast<const f32x4*>(cls + 8 * q + 4 * hh);
     }
-    if constexpr (TAIL) v = dj < n_left ? v : 0.f;
-    wv[r] = v;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int r = 4 * q + t;
+      const int dj = 8 * q + 4 * hh + t;  // j - jb0
+      float v = 0.f;
+      if constexpr (CLS != 2) {
+        const float rt_ = fast_exp2(fmaf(ss[r], c2, -rs)) - fast_exp2(fmaf(st[r], c2, -rt));
+        v = (CLS == 3) ? (dj <= di ? rt_ : 0.f) : rt_;
+      }
+      if constexpr (CLS != 1) {
+        const float ct_ = fast_exp2(fmaf(ss[r], c2, -cs4[t])) - fast_exp2(fmaf(st[r], c2, -ct4[t]));
+        v += (CLS == 3) ? (dj >= di ? ct_ : 0.f) : ct_;
+      }
+      if constexpr (TAIL) v = dj < n_left ? v : 0.f;
+      wv[r] = v;
+    }
   }
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if constexpr (In::kES == 2)
-        wf[kb][e] = (_Float16)wv[8 * kb + e];
-      else
-        wf[kb][e] = wv[8 * kb + e];
-    }
+    for (int e = 0; e < 8; ++e) w32[kb][e] = wv[8 * kb + e];
 }
 
-template <class In, int D, bool CAUSAL, bool OUT_F32>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+template <class Op>
+__device__ __forceinline__ typename Op::frag_t w_frag(const f32x8& w) {
+  if constexpr (Op::kES == 2) {
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const _Float16 lo = (_Float16)w[2 * q], hi = (_Float16)w[2 * q + 1];
+      o[q] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+             ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+    return __builtin_bit_cast(f16x8, o);
+  } else {
+    return w;
+  }
+}
+
+// Gradient-contraction B fragment: X_s[j][d] for d = 32 mb + l32 and the 8 k-slots
+// j = jbase + 8 (e/4) + 4 hh + (e%4) (jbase = 32 jb + 16 kb), read transposed from the
+// row-major key tile.  ds_read_b64_tr_b16: in each 16-lane group, lane s gives the
+// address of row (r0 + s/4), columns c0 + 4 (s%4) .. +3, and lane q receives column
+// c0 + q of rows r0 .. r0 + 3.
+template <class Op, int D>
+__device__ __forceinline__ typename Op::frag_t grad_bfrag(const char* tile, int jbase, int mb,
+                                                          int lane) {
+  using G = Geo<D, Op::kES>;
+  if constexpr (Op::kES == 2) {
+    const int s = lane & 15, g = lane >> 4, hh = lane >> 5;
+    const int col = 32 * mb + 16 * (g & 1) + 4 * (s & 3);  // element column
+    const int r0 = jbase + 4 * hh + (s >> 2);
+    const int r1 = r0 + 8;
+    const char* p0 = tile + G::off(r0, col >> 3) + (col & 7) * 2;
+    const char* p1 = tile + G::off(r1, col >> 3) + (col & 7) * 2;
+    const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)p0);
+    const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)p1);
+    const u32x2 a0 = __builtin_bit_cast(u32x2, v0), a1 = __builtin_bit_cast(u32x2, v1);
+    return __builtin_bit_cast(f16x8, u32x4{a0[0], a0[1], a1[0], a1[1]});
+  } else {
+    const int d = 32 * mb + (lane & 31), hh = lane >> 5;
+    f32x8 f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int r = jbase + 8 * (e >> 2) + 4 * hh + (e & 3);
+      f[e] = *reinterpret_cast<const float*>(tile + G::off(r, d >> 2) + (d & 3) * 4);
+    }
+    return f;
+  }
+}
+
+template <class Op, int D, bool CAUSAL, bool OUT_F32>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void relkl_bwd_kernel(const BwdArgs a) {
-  using elem_t = typename In::elem_t;
-  using frag_t = typename In::frag_t;
-  using gfrag_t = typename In::gfrag_t;
-  using T = Tile<In, D>;
-  using TT = TileT<In, D>;
+  using elem_t = typename Op::elem_t;
+  using frag_t = typename Op::frag_t;
+  using G = Geo<D, Op::kES>;
   constexpr int KS = D / 16;
   constexpr int MB = D / 32;  // 32-wide output blocks over d
+  constexpr int kStats = 2 * kBC * 4;
+  constexpr int kStage = 2 * G::kTileBytes + kStats;
 
-  __shared__ __attribute__((aligned(16))) char lds_t[T::kBytes];
-  __shared__ __attribute__((aligned(16))) char lds_s[T::kBytes];
-  __shared__ __attribute__((aligned(16))) char lds_st[TT::kBytes];
-  __shared__ __attribute__((aligned(16))) float lds_lt[kBC];
-  __shared__ __attribute__((aligned(16))) float lds_ls[kBC];
+  __shared__ __attribute__((aligned(1024))) char lds0[kStage];
+  __shared__ __attribute__((aligned(1024))) char lds1[kStage];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
@@ -577,163 +514,160 @@ void relkl_bwd_kernel(const BwdArgs a) {
   const int I = wt - unit * a.row_tiles;
   const int b = unit / a.H, h = unit - (unit / a.H) * a.H;
   const int hin = a.map.head_map[h];
-  const elem_t* xt = reinterpret_cast<const elem_t*>(a.x_t) + b * a.t_sb + hin * a.t_sh;
-  const elem_t* xs = reinterpret_cast<const elem_t*>(a.x_s) + b * a.s_sb + hin * a.s_sh;
-  const float* lse_t = a.lse_t + (int64_t)unit * N;
-  const float* lse_s = a.lse_s + (int64_t)unit * N;
+
+  // Operands: the fp16 reserve copies (dense [unit][N][D]) or the fp32 inputs.
+  const elem_t* xt;
+  const elem_t* xs;
+  int64_t tsn, ssn;
+  if constexpr (Op::kES == 2) {
+    xt = a.x16_t + (int64_t)unit * N * D;
+    xs = a.x16_s + (int64_t)unit * N * D;
+    tsn = D;
+    ssn = D;
+  } else {
+    xt = reinterpret_cast<const elem_t*>(a.x_t) + b * a.t_sb + hin * a.t_sh;
+    xs = reinterpret_cast<const elem_t*>(a.x_s) + b * a.s_sb + hin * a.s_sh;
+    tsn = a.t_sn;
+    ssn = a.s_sn;
+  }
+  const char* xt_c = reinterpret_cast<const char*>(xt);
+  const char* xs_c = reinterpret_cast<const char*>(xs);
+  const int64_t tsn_b = tsn * Op::kES, ssn_b = ssn * Op::kES;
+  const float* rst_t = a.r_t + (int64_t)unit * a.npad;
+  const float* rst_s = a.r_s + (int64_t)unit * a.npad;
 
   const int i0 = I * kBR;
-  const int wrow0 = i0 + wave * kRowsPerWave;
+  const int ib0 = i0 + 32 * wave;
+  const int row = ib0 + l32;
   const float c2 = a.c2;
-
-  frag_t qt[kRowBlocks][KS], qs[kRowBlocks][KS];
-  float rl_t[kRowBlocks], rl_s[kRowBlocks];  // row statistics in log2 units, minus 14
-#pragma unroll
-  for (int rb = 0; rb < kRowBlocks; ++rb) {
-    const int row = wrow0 + 32 * rb + l32;
-    if (row < N) {
-      rl_t[rb] = lse_t[row] * kLog2e - kWScaleLog2;
-      rl_s[rb] = lse_s[row] * kLog2e - kWScaleLog2;
-    } else {
-      rl_t[rb] = kPosBig;
-      rl_s[rb] = kPosBig;
-    }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (row < N) {
-        qt[rb][ks] = load_frag_global<In>(xt + (int64_t)row * a.t_sn + 16 * ks + 8 * hh);
-        qs[rb][ks] = load_frag_global<In>(xs + (int64_t)row * a.s_sn + 16 * ks + 8 * hh);
-      } else {
-        qt[rb][ks] = frag_t{};
-        qs[rb][ks] = frag_t{};
-      }
-    }
-  }
-
-  f32x16 acc[kRowBlocks][MB];
-#pragma unroll
-  for (int rb = 0; rb < kRowBlocks; ++rb)
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) acc[rb][mb] = f32x16{};
 
   const int kt_begin = (int)(((int64_t)a.key_tiles * split) / a.splits);
   const int kt_end = (int)(((int64_t)a.key_tiles * (split + 1)) / a.splits);
 
-  TileRegs<In, D> pt;
-  StuRegs<In, D> ps;
-  float plt = 0.f, pls = 0.f;
-  auto prefetch = [&](int kt) {
+  // Stage: [teacher tile][student tile][teacher stats][student stats].  Statistics of a
+  // key tile are 2 x 256 bytes: lanes 0..15 of wave 0 copy the teacher's, 16..31 the
+  // student's (the reserve pads each unit's statistics to a multiple of kBC).
+  auto stage_tile = [&](int kt, char* st_base) {
     const int j0 = kt * kBC;
-    tile_load<In, D>(pt, xt, a.t_sn, j0, N, tid);
-    stu_load<In, D>(ps, xs, a.s_sn, j0, N, tid);
-    if (tid < kBC) {
-      const int j = j0 + tid;
-      plt = j < N ? lse_t[j] * kLog2e - kWScaleLog2 : kPosBig;
-      pls = j < N ? lse_s[j] * kLog2e - kWScaleLog2 : kPosBig;
+    dma_tile<D, Op::kES>(xt_c, tsn_b, j0, N, st_base, wave, lane);
+    dma_tile<D, Op::kES>(xs_c, ssn_b, j0, N, st_base + G::kTileBytes, wave, lane);
+    if (wave == 0 && lane < 32) {
+      const float* src = (lane < 16 ? rst_t : rst_s) + j0 + 4 * (lane & 15);
+      __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)(st_base + 2 * G::kTileBytes), 16, 0, 0);
     }
   };
-  if (kt_begin < kt_end) prefetch(kt_begin);
+  if (kt_begin < kt_end) stage_tile(kt_begin, lds0);
 
-  for (int kt = kt_begin; kt < kt_end; ++kt) {
-    if (kt > kt_begin) __syncthreads();
-    tile_store<In, D>(pt, lds_t, tid);
-    stu_store<In, D>(ps, lds_s, lds_st, tid);
-    if (tid < kBC) {
-      lds_lt[tid] = plt;
-      lds_ls[tid] = pls;
-    }
-    __syncthreads();
-    if (kt + 1 < kt_end) prefetch(kt + 1);
-
-    const int j0 = kt * kBC;
-#pragma unroll 1
-    for (int jb = 0; jb < kBC / 32; ++jb) {
-      const int jb0 = j0 + 32 * jb;
-      if (jb0 >= N) break;
-      f32x16 st[kRowBlocks], ss[kRowBlocks];
+  frag_t qt[KS], qs[KS];
+  float rt, rs;  // own row statistics
+  if (row < N) {
+    rt = rst_t[row];
+    rs = rst_s[row];
+  } else {
+    rt = kPosBig;
+    rs = kPosBig;
+  }
 #pragma unroll
-      for (int rb = 0; rb < kRowBlocks; ++rb) { st[rb] = f32x16{}; ss[rb] = f32x16{}; }
-      const int lrow = 32 * jb + l32;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int off = lrow * T::kPitch + (16 * ks + 8 * hh) * In::kES;
-        const frag_t at = load_frag_lds<In>(lds_t + off);
-        const frag_t as = load_frag_lds<In>(lds_s + off);
-#pragma unroll
-        for (int rb = 0; rb < kRowBlocks; ++rb) {
-          st[rb] = mma_k16(at, qt[rb][ks], st[rb]);
-          ss[rb] = mma_k16(as, qs[rb][ks], ss[rb]);
-        }
-      }
-      gfrag_t wf[kRowBlocks][2];
-      const float* clt = lds_lt + 32 * jb;
-      const float* cls_ = lds_ls + 32 * jb;
-#pragma unroll
-      for (int rb = 0; rb < kRowBlocks; ++rb) {
-        const int ib0 = wrow0 + 32 * rb;
-        const int di = ib0 + l32 - jb0;  // i - jb0
-        if constexpr (!CAUSAL) {
-          if (jb0 + 32 > N)
-            make_w<In, 0, true>(st[rb], ss[rb], rl_t[rb], rl_s[rb], clt, cls_, hh, di, N - jb0, c2, wf[rb]);
-          else
-            make_w<In, 0, false>(st[rb], ss[rb], rl_t[rb], rl_s[rb], clt, cls_, hh, di, N - jb0, c2, wf[rb]);
-        } else {
-          if (jb0 + 31 < ib0)
-            make_w<In, 1, false>(st[rb], ss[rb], rl_t[rb], rl_s[rb], clt, cls_, hh, di, N - jb0, c2, wf[rb]);
-          else if (jb0 > ib0 + 31)
-            make_w<In, 2, false>(st[rb], ss[rb], rl_t[rb], rl_s[rb], clt, cls_, hh, di, N - jb0, c2, wf[rb]);
-          else
-            make_w<In, 3, false>(st[rb], ss[rb], rl_t[rb], rl_s[rb], clt, cls_, hh, di, N - jb0, c2, wf[rb]);
-        }
-      }
-      // dX[I] += W[I, J] X_s[J]: A = W (row i per lane), B = X_s[J] (d per lane).
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const gfrag_t bx = load_gfrag_lds<In, D>(lds_st, 32 * mb + l32, 32 * jb + 16 * kb + 4 * hh);
-#pragma unroll
-          for (int rb = 0; rb < kRowBlocks; ++rb) acc[rb][mb] = mma_k16(wf[rb][kb], bx, acc[rb][mb]);
-        }
-      }
+  for (int ks = 0; ks < KS; ++ks) {
+    if (row < N) {
+      qt[ks] = load_frag_global<Op>(xt + (int64_t)row * tsn + 16 * ks + 8 * hh);
+      qs[ks] = load_frag_global<Op>(xs + (int64_t)row * ssn + 16 * ks + 8 * hh);
+    } else {
+      qt[ks] = frag_t{};
+      qs[ks] = frag_t{};
     }
   }
 
-  // Scale and write: acc[rb][mb][r] = dX[i][d] * 2^14 / (scale g) for
-  // i = wrow0 + 32 rb + 8 (r/4) + 4 hh + (r%4), d = 32 mb + l32.
+  f32x16 acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x16{};
+
+  auto step = [&](int kt, const char* cur, char* nxt) __attribute__((always_inline)) {
+    wait_vmem();
+    __syncthreads();
+    if (kt + 1 < kt_end) stage_tile(kt + 1, nxt);
+    const char* tile_t = cur;
+    const char* tile_s = tile_t + G::kTileBytes;
+    const float* stat_t = reinterpret_cast<const float*>(tile_t + 2 * G::kTileBytes);
+    const float* stat_s = stat_t + kBC;
+#pragma unroll 1
+    for (int jb = 0; jb < kBC / 32; ++jb) {
+      const int jb0 = kt * kBC + 32 * jb;
+      if (jb0 >= N) break;
+      f32x16 st = f32x16{}, ss = f32x16{};
+      const int lr = 32 * jb + l32;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const frag_t at = lds_frag<Op, D>(tile_t, lr, 16 * ks + 8 * hh);
+        const frag_t as = lds_frag<Op, D>(tile_s, lr, 16 * ks + 8 * hh);
+        st = mma_k16(at, qt[ks], st);
+        ss = mma_k16(as, qs[ks], ss);
+      }
+      f32x8 w32[2];
+      const float* clt = stat_t + 32 * jb;
+      const float* cls = stat_s + 32 * jb;
+      const int di = row - jb0;
+      const int nl = N - jb0;
+      const bool tail = jb0 + 32 > N;
+      if constexpr (!CAUSAL) {
+        if (tail) make_w<0, true>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, w32);
+        else make_w<0, false>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, w32);
+      } else {
+        if (jb0 + 31 < ib0) {
+          make_w<1, false>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, w32);
+        } else if (jb0 > ib0 + 31) {
+          if (tail) make_w<2, true>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, w32);
+          else make_w<2, false>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, w32);
+        } else {
+          if (tail) make_w<3, true>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, w32);
+          else make_w<3, false>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, w32);
+        }
+      }
+      const frag_t wf0 = w_frag<Op>(w32[0]);
+      const frag_t wf1 = w_frag<Op>(w32[1]);
+      // dX[I] += W[I, J] X_s[J]: A = W (row i per lane), B = X_s[J] (d per lane).
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const frag_t b0 = grad_bfrag<Op, D>(tile_s, 32 * jb, mb, lane);
+        const frag_t b1 = grad_bfrag<Op, D>(tile_s, 32 * jb + 16, mb, lane);
+        acc[mb] = mma_k16(wf0, b0, acc[mb]);
+        acc[mb] = mma_k16(wf1, b1, acc[mb]);
+      }
+    }
+  };
+  for (int kt = kt_begin; kt < kt_end; kt += 2) {
+    step(kt, lds0, lds1);
+    if (kt + 1 < kt_end) step(kt + 1, lds1, lds0);
+  }
+
+  // Scale and write: acc[mb][r] = dX[i][d] * 2^14 / (scale g) for
+  // i = ib0 + 8 (r/4) + 4 hh + (r%4), d = 32 mb + l32.
   const float factor = a.scale * a.grad_loss[0] * (1.0f / 16384.0f);
   if (a.splits == 1) {
-    const bool full = wrow0 + kRowsPerWave <= N;
-    char* gbase = reinterpret_cast<char*>(a.dx) +
-                  (b * a.g_sb + hin * a.g_sh) * (OUT_F32 ? 4 : 2);
+    const bool full = ib0 + 32 <= N;
+    char* gbase = reinterpret_cast<char*>(a.dx) + (b * a.g_sb + hin * a.g_sh) * (OUT_F32 ? 4 : 2);
 #pragma unroll
-    for (int rb = 0; rb < kRowBlocks; ++rb) {
+    for (int r = 0; r < 16; ++r) {
+      const int i = ib0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+      if (!full && i >= N) continue;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = wrow0 + 32 * rb + 8 * (r >> 2) + 4 * hh + (r & 3);
-        if (!full && i >= N) continue;
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const int64_t o = (int64_t)i * a.g_sn + 32 * mb + l32;
-          const float v = acc[rb][mb][r] * factor;
-          if constexpr (OUT_F32)
-            reinterpret_cast<float*>(gbase)[o] = v;
-          else
-            reinterpret_cast<uint16_t*>(gbase)[o] = f32_to_bf16_rne(v);
-        }
+      for (int mb = 0; mb < MB; ++mb) {
+        const int64_t o = (int64_t)i * a.g_sn + 32 * mb + l32;
+        const float v = acc[mb][r] * factor;
+        if constexpr (OUT_F32)
+          reinterpret_cast<float*>(gbase)[o] = v;
+        else
+          reinterpret_cast<uint16_t*>(gbase)[o] = f32_to_bf16_rne(v);
       }
     }
   } else {
     const int rows_pad = a.row_tiles * kBR;
     float* dst = a.partial + ((int64_t)split * a.B * a.H + unit) * rows_pad * D;
 #pragma unroll
-    for (int rb = 0; rb < kRowBlocks; ++rb) {
+    for (int r = 0; r < 16; ++r) {
+      const int i = ib0 + 8 * (r >> 2) + 4 * hh + (r & 3);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = wrow0 + 32 * rb + 8 * (r >> 2) + 4 * hh + (r & 3);
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) dst[(int64_t)i * D + 32 * mb + l32] = acc[rb][mb][r] * factor;
-      }
+      for (int mb = 0; mb < MB; ++mb) dst[(int64_t)i * D + 32 * mb + l32] = acc[mb][r] * factor;
     }
   }
 }
@@ -763,7 +697,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const ReduceArgs a) 
     uint16_t* dst = reinterpret_cast<uint16_t*>(a.dx) + o;
     const uint32_t lo = (uint32_t)f32_to_bf16_rne(s[0]) | ((uint32_t)f32_to_bf16_rne(s[1]) << 16);
     const uint32_t hi = (uint32_t)f32_to_bf16_rne(s[2]) | ((uint32_t)f32_to_bf16_rne(s[3]) << 16);
-    *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+    *reinterpret_cast<u32x2*>(dst) = u32x2{lo, hi};
   }
 }
 
@@ -798,33 +732,33 @@ int launch_fwd(const FwdArgs& a, bool in_bf16, int d, bool causal, float* loss, 
                 : launch_fwd_t<F32In, 64, false>(a, loss, s);
 }
 
-template <class In, int D, bool CAUSAL, bool OUT_F32>
+template <class Op, int D, bool CAUSAL, bool OUT_F32>
 static int launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   const int grid = a.B * a.H * a.row_tiles * a.splits;
-  hipLaunchKernelGGL((relkl_bwd_kernel<In, D, CAUSAL, OUT_F32>), dim3(grid), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((relkl_bwd_kernel<Op, D, CAUSAL, OUT_F32>), dim3(grid), dim3(kThreads), 0, s,
                      a);
   return (int)hipGetLastError();
 }
 
-template <class In, int D>
+template <class Op, int D>
 static int launch_bwd_d(const BwdArgs& a, bool causal, bool out_f32, hipStream_t s) {
-  if (causal) return out_f32 ? launch_bwd_t<In, D, true, true>(a, s) : launch_bwd_t<In, D, true, false>(a, s);
-  return out_f32 ? launch_bwd_t<In, D, false, true>(a, s) : launch_bwd_t<In, D, false, false>(a, s);
+  if (causal) return out_f32 ? launch_bwd_t<Op, D, true, true>(a, s) : launch_bwd_t<Op, D, true, false>(a, s);
+  return out_f32 ? launch_bwd_t<Op, D, false, true>(a, s) : launch_bwd_t<Op, D, false, false>(a, s);
 }
 
 int launch_bwd(const BwdArgs& a, bool in_bf16, int d, bool causal, bool out_f32, void* stream) {
   if (fault_injected()) return (int)hipErrorLaunchFailure;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (in_bf16) {
-    // a bf16 gradient is only produced for bf16 inputs; fp32 inputs always give fp32
-    return d == 128 ? launch_bwd_d<Bf16In, 128>(a, causal, out_f32, s)
-                    : launch_bwd_d<Bf16In, 64>(a, causal, out_f32, s);
+    return d == 128 ? launch_bwd_d<F16Op, 128>(a, causal, out_f32, s)
+                    : launch_bwd_d<F16Op, 64>(a, causal, out_f32, s);
   }
+  // fp32 inputs always give an fp32 gradient
   return d == 128 ? launch_bwd_d<F32In, 128>(a, causal, true, s)
                   : launch_bwd_d<F32In, 64>(a, causal, true, s);
 }
 
-int launch_splitk_reduce(const ReduceArgs& a, bool out_f32, bool, void* stream) {
+int launch_splitk_reduce(const ReduceArgs& a, bool out_f32, void* stream) {
   if (fault_injected()) return (int)hipErrorLaunchFailure;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int64_t total = (int64_t)a.B * a.H * a.N * (a.d / 4);

@@ -18,7 +18,7 @@ from typing import Optional, Sequence
 import torch
 
 __all__ = ["LardError", "library_path", "load_library", "relkl_fwd", "relkl_bwd",
-           "relation_kl", "workspace_size", "LARD_MAX_HEADS"]
+           "relation_kl", "workspace_size", "reserve_size", "LARD_MAX_HEADS"]
 
 LARD_FP32 = 0
 LARD_BF16 = 1
@@ -79,10 +79,13 @@ def load_library():
     lib.lard_relkl_workspace_size.restype = sz
     lib.lard_relkl_workspace_size.argtypes = [ctypes.POINTER(_Desc), ctypes.c_int,
                                               ctypes.POINTER(ctypes.c_int)]
+    lib.lard_relkl_reserve_size.restype = sz
+    lib.lard_relkl_reserve_size.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(ctypes.c_int)]
     lib.lard_relkl_fwd.restype = ctypes.c_int
-    lib.lard_relkl_fwd.argtypes = [ctypes.POINTER(_Desc), vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.lard_relkl_fwd.argtypes = [ctypes.POINTER(_Desc), vp, vp, vp, vp, vp, vp, vp, sz, vp, sz,
+                                   vp]
     lib.lard_relkl_bwd.restype = ctypes.c_int
-    lib.lard_relkl_bwd.argtypes = [ctypes.POINTER(_Desc), vp, vp, vp, vp, vp,
+    lib.lard_relkl_bwd.argtypes = [ctypes.POINTER(_Desc), vp, vp, vp, sz, vp,
                                    ctypes.POINTER(_GradDesc), vp, vp, sz, vp]
     lib.lard_status_string.restype = ctypes.c_char_p
     lib.lard_status_string.argtypes = [ctypes.c_int]
@@ -155,10 +158,20 @@ def workspace_size(x_t, x_s, *, causal=True, scale=None, head_map=None, pass_: i
     return int(n)
 
 
+def reserve_size(x_t, x_s, *, causal=True, scale=None, head_map=None) -> int:
+    lib = load_library()
+    desc, _keep = _make_desc(x_t, x_s, causal, scale, head_map)
+    st = ctypes.c_int(0)
+    n = lib.lard_relkl_reserve_size(ctypes.byref(desc), ctypes.byref(st))
+    _check(st.value)
+    return int(n)
+
+
 def relkl_fwd(x_t: torch.Tensor, x_s: torch.Tensor, *, causal: bool = True,
               scale: Optional[float] = None, head_map: Optional[Sequence[int]] = None,
               want_row_kl: bool = False, stream=None):
-    """Forward: returns dict(loss: 0-d fp32, lse_t, lse_s: fp32 [B, H, N], row_kl or None)."""
+    """Forward: returns dict(loss: 0-d fp32, lse_t, lse_s: fp32 [B, H, N], row_kl or None,
+    reserve: uint8 device buffer the backward needs)."""
     lib = load_library()
     desc, keep = _make_desc(x_t, x_s, causal, scale, head_map)
     _require_gpu(x_t)
@@ -172,16 +185,19 @@ def relkl_fwd(x_t: torch.Tensor, x_s: torch.Tensor, *, causal: bool = True,
     ws_bytes = lib.lard_relkl_workspace_size(ctypes.byref(desc), 0, ctypes.byref(st))
     _check(st.value)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    rs_bytes = lib.lard_relkl_reserve_size(ctypes.byref(desc), ctypes.byref(st))
+    _check(st.value)
+    reserve = torch.empty(max(rs_bytes, 256), dtype=torch.uint8, device=dev)
     _check(lib.lard_relkl_fwd(ctypes.byref(desc), x_t.data_ptr(), x_s.data_ptr(),
                               lse_t.data_ptr(), lse_s.data_ptr(),
                               row_kl.data_ptr() if row_kl is not None else None,
-                              loss.data_ptr(), ws.data_ptr(), ws.numel(),
-                              _stream_handle(dev, stream)))
+                              loss.data_ptr(), reserve.data_ptr(), reserve.numel(),
+                              ws.data_ptr(), ws.numel(), _stream_handle(dev, stream)))
     del keep
-    return {"loss": loss, "lse_t": lse_t, "lse_s": lse_s, "row_kl": row_kl}
+    return {"loss": loss, "lse_t": lse_t, "lse_s": lse_s, "row_kl": row_kl, "reserve": reserve}
 
 
-def relkl_bwd(x_t: torch.Tensor, x_s: torch.Tensor, lse_t: torch.Tensor, lse_s: torch.Tensor,
+def relkl_bwd(x_t: torch.Tensor, x_s: torch.Tensor, reserve: torch.Tensor,
               grad_loss: torch.Tensor, *, causal: bool = True, scale: Optional[float] = None,
               head_map: Optional[Sequence[int]] = None, dx: Optional[torch.Tensor] = None,
               dx_dtype: Optional[torch.dtype] = None, stream=None) -> torch.Tensor:
@@ -194,10 +210,8 @@ def relkl_bwd(x_t: torch.Tensor, x_s: torch.Tensor, lse_t: torch.Tensor, lse_s: 
     desc, keep = _make_desc(x_t, x_s, causal, scale, head_map)
     _require_gpu(x_t)
     dev = x_t.device
-    for t, name in ((lse_t, "lse_t"), (lse_s, "lse_s")):
-        if (t.dtype != torch.float32 or not t.is_contiguous() or t.device != dev
-                or tuple(t.shape) != (desc.B, desc.H, desc.N)):
-            raise LardError(1, f"{name} must be contiguous fp32 [B, H, N] on {dev}")
+    if reserve.dtype != torch.uint8 or not reserve.is_contiguous() or reserve.device != dev:
+        raise LardError(1, "reserve must be the uint8 device buffer returned by relkl_fwd")
     if (grad_loss.dtype != torch.float32 or grad_loss.numel() != 1 or grad_loss.device != dev):
         raise LardError(1, "grad_loss must be a one-element fp32 tensor on the inputs' device")
     grad_loss = grad_loss.contiguous()
@@ -214,7 +228,7 @@ def relkl_bwd(x_t: torch.Tensor, x_s: torch.Tensor, lse_t: torch.Tensor, lse_s: 
     _check(st.value)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     _check(lib.lard_relkl_bwd(ctypes.byref(desc), x_t.data_ptr(), x_s.data_ptr(),
-                              lse_t.data_ptr(), lse_s.data_ptr(), grad_loss.data_ptr(),
+                              reserve.data_ptr(), reserve.numel(), grad_loss.data_ptr(),
                               ctypes.byref(gdesc), dx.data_ptr(), ws.data_ptr(), ws.numel(),
                               _stream_handle(dev, stream)))
     del keep
@@ -225,15 +239,15 @@ class _RelationKL(torch.autograd.Function):
     @staticmethod
     def forward(ctx, x_t, x_s, causal, scale, head_map):
         out = relkl_fwd(x_t, x_s, causal=causal, scale=scale, head_map=head_map)
-        ctx.save_for_backward(x_t, x_s, out["lse_t"], out["lse_s"])
+        ctx.save_for_backward(x_t, x_s, out["reserve"])
         ctx.causal, ctx.scale, ctx.head_map = causal, scale, head_map
         return out["loss"]
 
     @staticmethod
     def backward(ctx, grad):
-        x_t, x_s, lse_t, lse_s = ctx.saved_tensors
+        x_t, x_s, reserve = ctx.saved_tensors
         g = grad if grad.dtype == torch.float32 else grad.float()
-        dx = relkl_bwd(x_t, x_s, lse_t, lse_s, g, causal=ctx.causal, scale=ctx.scale,
+        dx = relkl_bwd(x_t, x_s, reserve, g, causal=ctx.causal, scale=ctx.scale,
                        head_map=ctx.head_map)
         return None, dx, None, None, None
 

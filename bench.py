@@ -114,7 +114,7 @@ def main():
             f = relkl.relkl_fwd(xt, xs, causal=causal)
             if record:
                 e1.record(stream)
-            relkl.relkl_bwd(xt, xs, f["lse_t"], f["lse_s"], gl, causal=causal)
+            relkl.relkl_bwd(xt, xs, f["reserve"], gl, causal=causal)
             if record:
                 e2.record(stream)
                 ev_log.append((name, e0, e1, e2))

@@ -13,17 +13,19 @@
  *   and, for an upstream gradient g of the loss,
  *     dZ    = g * (R_s - R_t)  (0 where masked)
  *     dX_s  = scale * (dZ + dZ^T) X_s       (the teacher is frozen: no teacher gradient)
- * "Phase 1" keeps only the per-row log-sum-exp LSE_m(i) = log sum_j exp(Z_m(i,j)); the
- * backward recomputes the logits tile by tile from X and the LSEs, so no N x N matrix is
- * ever stored (extra device memory is O(B*H*N)).
+ * "Phase 1" keeps only per-row log-sum-exp statistics; the backward recomputes the logits
+ * tile by tile, so no N x N matrix is ever stored.  Between the two calls the library keeps
+ * a caller-owned "reserve" buffer (see lard_relkl_reserve_size): the row statistics in
+ * log2 units and, for bf16 inputs, IEEE fp16 copies of the teacher and student rows that
+ * the backward uses as its matrix-core operands.  Its size is linear in N.
  *
  * Mask: causal = 1 keeps j <= i (the diagonal included); causal = 0 keeps every entry.
  * The returned loss is the plain sum; the pages' mean over rows is loss / N and its
  * gradient is obtained by passing g = 1 / N.
  *
  * Conventions shared by every entry point:
- *  - Pointers named x_*, lse_*, row_kl, loss, grad_loss, dx_student and workspace are
- *    DEVICE pointers; head_map and the descriptors are HOST pointers.
+ *  - Pointers named x_*, lse_*, row_kl, loss, reserve, grad_loss, dx_student and
+ *    workspace are DEVICE pointers; head_map and the descriptors are HOST pointers.
  *  - All validation happens on the host before any HIP call; a failed validation
  *    returns LARD_ERR_INVALID_ARGUMENT / LARD_ERR_UNSUPPORTED /
  *    LARD_ERR_WORKSPACE_TOO_SMALL and touches no device memory.
@@ -35,9 +37,10 @@
  *    until the enqueued work has completed.
  *  - Results are bitwise reproducible for a fixed shape and split count.
  *  - NaN / Inf inputs are not checked and propagate.
- *  - The backward rounds dZ and X_s to IEEE fp16 for its gradient contraction (X_s is
- *    bf16 there, and bf16 -> fp16 is exact for 2^-17 <= |x| < 65504).  Inputs outside
- *    |x| < 65504 are not supported by the bf16 backward.
+ *  - For bf16 inputs the backward computes in IEEE fp16: the reserve holds fp16 copies
+ *    of the inputs (bf16 -> fp16 is exact for 2^-17 <= |x| < 65504; smaller magnitudes
+ *    keep an absolute error below 2^-25), and dZ is carried as fp16 scaled by 2^14.
+ *    Inputs with |x| >= 65504 are not supported by the bf16 backward.
  */
 #ifndef LARD_H
 #define LARD_H
@@ -108,33 +111,44 @@ typedef struct lard_grad_desc {
 size_t lard_relkl_workspace_size(const lard_relkl_desc* desc, int pass, lard_status* status);
 
 /*
+ * Bytes of the reserve buffer that lard_relkl_fwd writes and lard_relkl_bwd reads for
+ * this descriptor: 2 * 4 * B * H * roundup(N, 64) for fp32 inputs, plus
+ * 2 * 2 * B * H * N * d for bf16 inputs (each part rounded up to 256 bytes).  Returns 0
+ * and sets *status (if non-NULL) on an invalid descriptor.
+ */
+size_t lard_relkl_reserve_size(const lard_relkl_desc* desc, lard_status* status);
+
+/*
  * Forward ("phase 1" plus the KL accumulation; key_machinery of the verdict page).
  *   x_teacher, x_student : device, desc layout and dtype, read only.
  *   lse_teacher, lse_student : device fp32 [B, H, N] (dense), written: LSE_m(i) in nats.
  *   row_kl : device fp32 [B, H, N] or NULL; written: KL_i.
  *   loss   : device fp32 scalar, written (not accumulated): sum of KL_i over b, h, i,
  *            reduced in a fixed order in fp64.
+ *   reserve : device, >= lard_relkl_reserve_size(desc) bytes, 256-byte aligned; written,
+ *            and must be passed unchanged to lard_relkl_bwd for the same inputs.
  *   workspace : device, >= lard_relkl_workspace_size(desc, 0) bytes, 8-byte aligned.
  */
 lard_status lard_relkl_fwd(const lard_relkl_desc* desc, const void* x_teacher,
                            const void* x_student, float* lse_teacher, float* lse_student,
-                           float* row_kl, float* loss, void* workspace,
-                           size_t workspace_bytes, void* stream);
+                           float* row_kl, float* loss, void* reserve, size_t reserve_bytes,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Backward (logit recomputation fused with the gradient; key_machinery and the gradient
  * identity of core_discovery on the verdict page).
- *   lse_teacher, lse_student : device fp32 [B, H, N] as written by lard_relkl_fwd for
- *            the same inputs.
+ *   x_teacher, x_student : the inputs given to lard_relkl_fwd.
+ *   reserve : device, as written by lard_relkl_fwd for the same inputs and descriptor.
  *   grad_loss : device fp32 scalar g (the upstream gradient of `loss`).
  *   dx_student : device, layout and dtype given by `grad`; see lard_grad_desc.
- *   workspace : device, >= lard_relkl_workspace_size(desc, 1) bytes, 16-byte aligned.
+ *   workspace : device, >= lard_relkl_workspace_size(desc, 1) bytes, 16-byte aligned
+ *            (may be NULL when that size is 0).
  */
 lard_status lard_relkl_bwd(const lard_relkl_desc* desc, const void* x_teacher,
-                           const void* x_student, const float* lse_teacher,
-                           const float* lse_student, const float* grad_loss,
-                           const lard_grad_desc* grad, void* dx_student, void* workspace,
-                           size_t workspace_bytes, void* stream);
+                           const void* x_student, const void* reserve, size_t reserve_bytes,
+                           const float* grad_loss, const lard_grad_desc* grad,
+                           void* dx_student, void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* lard_status_string(lard_status status);

@@ -40,7 +40,7 @@ def gpu_fwd_bwd(x_t, x_s, causal, head_map=None, dx_dtype=None, scale=None, g=1.
     xt, xs = x_t.to(dev), x_s.to(dev)
     f = relkl.relkl_fwd(xt, xs, causal=causal, head_map=head_map, want_row_kl=True, scale=scale)
     gl = torch.tensor(g, dtype=torch.float32, device=dev)
-    dx = relkl.relkl_bwd(xt, xs, f["lse_t"], f["lse_s"], gl, causal=causal, head_map=head_map,
+    dx = relkl.relkl_bwd(xt, xs, f["reserve"], gl, causal=causal, head_map=head_map,
                          dx_dtype=dx_dtype, scale=scale)
     torch.cuda.synchronize()
     return f, dx

@@ -30,7 +30,7 @@ def declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) >= {"lard_relkl_fwd", "lard_relkl_bwd", "lard_relkl_workspace_size",
-                          "lard_status_string", "lard_version"}
+                          "lard_relkl_reserve_size", "lard_status_string", "lard_version"}
     for n in names:
         assert hasattr(lib, n), n
     assert lib.lard_version() >= 10000
@@ -57,15 +57,17 @@ def ws_query(lib, desc, pass_=0):
     return n, st.value
 
 
-def fwd(lib, desc, xt=FAKE, xs=FAKE, lt=FAKE, ls=FAKE, kl=None, loss=FAKE, ws=FAKE, nws=1 << 20):
+def fwd(lib, desc, xt=FAKE, xs=FAKE, lt=FAKE, ls=FAKE, kl=None, loss=FAKE, rs=FAKE,
+        nrs=1 << 30, ws=FAKE, nws=1 << 20):
     return lib.lard_relkl_fwd(ctypes.byref(desc) if desc is not None else None, xt, xs, lt, ls,
-                              kl, loss, ws, nws, None)
+                              kl, loss, rs, nrs, ws, nws, None)
 
 
-def bwd(lib, desc, g=None, xt=FAKE, xs=FAKE, dx=FAKE, ws=FAKE, nws=1 << 30):
+def bwd(lib, desc, g=None, xt=FAKE, xs=FAKE, rs=FAKE, nrs=1 << 30, dx=FAKE, ws=FAKE,
+        nws=1 << 30):
     g = g or _GradDesc(dtype=1, reserved=0, stride_b=4 * 100 * 128, stride_h=100 * 128,
                        stride_n=128)
-    return lib.lard_relkl_bwd(ctypes.byref(desc), xt, xs, FAKE, FAKE, FAKE, ctypes.byref(g), dx,
+    return lib.lard_relkl_bwd(ctypes.byref(desc), xt, xs, rs, nrs, FAKE, ctypes.byref(g), dx,
                               ws, nws, None)
 
 
@@ -129,8 +131,27 @@ def test_head_map_validation(lib):
     del keep
 
 
+def test_reserve_size(lib):
+    st = ctypes.c_int(-1)
+    d = good_desc()  # bf16, B=1, H=4, N=100, d=128
+    n = lib.lard_relkl_reserve_size(ctypes.byref(d), ctypes.byref(st))
+    assert st.value == OK
+    copies = 2 * (((4 * 100 * 128 * 2) + 255) // 256 * 256)
+    stats = 2 * (((4 * 128 * 4) + 255) // 256 * 256)
+    assert n == copies + stats
+    d32 = good_desc(dtype=0)
+    assert lib.lard_relkl_reserve_size(ctypes.byref(d32), ctypes.byref(st)) == stats
+    assert lib.lard_relkl_reserve_size(ctypes.byref(good_desc(d=32)), ctypes.byref(st)) == 0
+    assert st.value == UNSUPPORTED
+
+
 def test_pointer_and_workspace_validation(lib):
     d = good_desc()
+    assert fwd(lib, d, rs=None) == INVALID
+    assert fwd(lib, d, rs=FAKE + 16) == INVALID    # reserve must be 256-byte aligned
+    assert fwd(lib, d, nrs=16) == WS_SMALL
+    assert bwd(lib, d, rs=None) == INVALID
+    assert bwd(lib, d, nrs=16) == WS_SMALL
     assert fwd(lib, None) == INVALID
     assert fwd(lib, d, xt=None) == INVALID
     assert fwd(lib, d, loss=None) == INVALID

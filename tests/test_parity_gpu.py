@@ -143,7 +143,7 @@ def test_head_map_and_untouched_heads():
     hm = [0, 4]
     f = relkl.relkl_fwd(rep_t, rep_s, causal=True, head_map=hm, want_row_kl=True)
     sentinel = torch.full(rep_s.shape, 7.0, dtype=torch.float32, device=dev)
-    relkl.relkl_bwd(rep_t, rep_s, f["lse_t"], f["lse_s"], torch.ones((), device=dev),
+    relkl.relkl_bwd(rep_t, rep_s, f["reserve"], torch.ones((), device=dev),
                     causal=True, head_map=hm, dx=sentinel)
     torch.cuda.synchronize()
     base_t, base_s = k.to(torch.bfloat16), k_s.to(torch.bfloat16)
@@ -167,8 +167,8 @@ def test_strided_inputs_match_contiguous():
     f1 = relkl.relkl_fwd(v_t, v_s, causal=True)
     f2 = relkl.relkl_fwd(v_t.contiguous(), v_s.contiguous(), causal=True)
     gl = torch.ones((), device=dev)
-    d1 = relkl.relkl_bwd(v_t, v_s, f1["lse_t"], f1["lse_s"], gl, causal=True)
-    d2 = relkl.relkl_bwd(v_t.contiguous(), v_s.contiguous(), f2["lse_t"], f2["lse_s"], gl,
+    d1 = relkl.relkl_bwd(v_t, v_s, f1["reserve"], gl, causal=True)
+    d2 = relkl.relkl_bwd(v_t.contiguous(), v_s.contiguous(), f2["reserve"], gl,
                          causal=True)
     torch.cuda.synchronize()
     assert torch.equal(f1["loss"], f2["loss"])
