@@ -14,7 +14,7 @@ namespace {
 using namespace lard;
 
 constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
-constexpr int kTargetWorkgroups = 1024;  // two rounds of two workgroups per CU over 256 CUs
+constexpr int kTargetWorkgroups = 512;  // two rounds of one backward workgroup per CU
 constexpr int kMaxSplits = 64;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -70,12 +70,13 @@ void fill_map(UnitMap& m, const lard_relkl_desc* d) {
 }
 
 int row_tiles_of(const lard_relkl_desc* d) { return (d->N + kBR - 1) / kBR; }
+int bwd_row_tiles_of(const lard_relkl_desc* d) { return (d->N + kBRB - 1) / kBRB; }
 int key_tiles_of(const lard_relkl_desc* d) { return (d->N + kBC - 1) / kBC; }
 
 // Split the key range of the backward when the (unit, row tile) grid alone cannot fill
 // the chip.  Deterministic in the shape; LARD_SPLITK overrides it (clamped).
 int choose_splits(const lard_relkl_desc* d) {
-  const int64_t base = (int64_t)d->B * d->H * row_tiles_of(d);
+  const int64_t base = (int64_t)d->B * d->H * bwd_row_tiles_of(d);
   const int kt = key_tiles_of(d);
   int s = 1;
   if (base < kTargetWorkgroups) s = (int)((kTargetWorkgroups + base - 1) / base);
@@ -102,7 +103,7 @@ ReserveLayout reserve_of(const lard_relkl_desc* d) {
 size_t bwd_workspace(const lard_relkl_desc* d) {
   const int s = choose_splits(d);
   if (s == 1) return 0;
-  return (size_t)s * d->B * d->H * (size_t)row_tiles_of(d) * kBR * d->d * sizeof(float);
+  return (size_t)s * d->B * d->H * (size_t)bwd_row_tiles_of(d) * kBRB * d->d * sizeof(float);
 }
 
 }  // namespace
@@ -210,7 +211,7 @@ lard_status lard_relkl_bwd(const lard_relkl_desc* desc, const void* x_teacher,
   a.s_sb = desc->s_stride_b; a.s_sh = desc->s_stride_h; a.s_sn = desc->s_stride_n;
   a.g_sb = grad->stride_b; a.g_sh = grad->stride_h; a.g_sn = grad->stride_n;
   a.B = desc->B; a.H = desc->H; a.N = desc->N;
-  a.row_tiles = row_tiles_of(desc);
+  a.row_tiles = bwd_row_tiles_of(desc);
   a.key_tiles = key_tiles_of(desc);
   a.splits = choose_splits(desc);
   a.scale = desc->scale;
@@ -235,7 +236,7 @@ lard_status lard_relkl_bwd(const lard_relkl_desc* desc, const void* x_teacher,
     r.dx = dx_student;
     r.g_sb = a.g_sb; r.g_sh = a.g_sh; r.g_sn = a.g_sn;
     r.B = a.B; r.H = a.H; r.N = a.N; r.d = desc->d;
-    r.rows_pad = a.row_tiles * kBR;
+    r.rows_pad = a.row_tiles * kBRB;
     r.splits = a.splits;
     r.map = a.map;
     e = launch_splitk_reduce(r, out_f32, stream);

@@ -13,7 +13,9 @@ namespace lard {
 constexpr int kWave = 64;
 constexpr int kWaves = 4;                 // waves per workgroup (two workgroups per CU)
 constexpr int kThreads = kWave * kWaves;  // 256
-constexpr int kBR = kWaves * 32;          // rows of one row tile: one 32-row block per wave
+constexpr int kBR = kWaves * 32;          // forward rows per workgroup: 32 per wave
+constexpr int kBWaves = 8;                // backward waves per workgroup (two groups of 4)
+constexpr int kBRB = kBWaves * 32;        // backward rows per workgroup
 constexpr int kBC = 64;                   // rows of one key tile staged in LDS
 
 inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
@@ -75,7 +77,7 @@ struct BwdArgs {
   int64_t s_sb, s_sh, s_sn;
   int64_t g_sb, g_sh, g_sn;  // gradient strides (elements)
   int32_t B, H, N;
-  int32_t row_tiles;
+  int32_t row_tiles;   // ceil(N / kBRB)
   int32_t key_tiles;   // ceil(N / kBC)
   int32_t splits;      // split-K count over key tiles
   int32_t npad;
@@ -96,7 +98,7 @@ struct ReduceArgs {
   void* dx;
   int64_t g_sb, g_sh, g_sn;
   int32_t B, H, N, d;
-  int32_t rows_pad;    // row_tiles * kBR
+  int32_t rows_pad;    // row_tiles * kBRB
   int32_t splits;
   UnitMap map;
 };

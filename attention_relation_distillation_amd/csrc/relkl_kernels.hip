@@ -123,12 +123,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // ------------------------------------------------------------------ LDS key tiles
-// Row-major [kBC][D] tile, 16-byte chunks of row r stored at chunk (c ^ swz(r)).
-// swz sends 8 consecutive rows to 8 distinct chunk positions (conflict-free 16-byte
-// fragment reads), and 4 consecutive rows to 4 distinct chunk pairs (conflict-free
-// transposed reads of two adjacent chunks).
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
-
+// Row-major [kBC][D] tile, 16-byte chunks of row r stored at chunk (c ^ swz(r)).  The LDS
+// has 64 four-byte banks, i.e. 16 chunk slots per 256-byte bank line.  For rows of 16 or
+// more chunks, swz(r) = 4 (r % 4) + (r / 4) % 4 is a bijection on r % 16, so the 16
+// rows a 16-byte fragment read touches at one chunk land on 16 distinct slots; and for
+// any 4 consecutive rows (aligned to 4) it spreads a run of 4 adjacent chunks over 16
+// distinct slots, which is what a transposed 8-byte read of 32 lanes touches.  Rows of 8
+// chunks use the 8-slot analogue.
 template <int D, int ES>
 struct Geo {
   static constexpr int kRowBytes = D * ES;
@@ -137,6 +138,10 @@ struct Geo {
   static constexpr int kDmaPerWave = kBC * kCPR / (kWave * kWaves);
   static_assert(kCPR >= 8, "swizzle needs at least 8 chunks per row");
   static_assert(kBC * kCPR % (kWave * kWaves) == 0, "tile must split evenly over the waves");
+  __device__ static __forceinline__ int swz(int r) {
+    if constexpr (kCPR >= 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return ((r & 3) << 1) | ((r >> 2) & 1);
+  }
   __device__ static __forceinline__ int off(int r, int c) { return r * kRowBytes + ((c ^ swz(r)) << 4); }
 };
 
@@ -153,22 +158,35 @@ __device__ __forceinline__ void dma_tile(const char* base, int64_t sn_bytes, int
     const int slot0 = (wave * G::kDmaPerWave + q) * kWave;
     const int t = slot0 + lane;
     const int r = t / G::kCPR;
-    const int c = (t % G::kCPR) ^ swz(r);
+    const int c = (t % G::kCPR) ^ G::swz(r);
     const int j = min(j0 + r, N - 1);
     const char* g = base + (int64_t)j * sn_bytes + c * 16;
     __builtin_amdgcn_global_load_lds(g, (LDS_AS void*)(lds + slot0 * 16), 16, 0, 0);
   }
 }
 
+// Score-contraction A fragment of key row 32 jb + l32, elements 16 ks + 8 hh .. +7.  The
+// swizzle of that row only depends on l32 (32 jb is a multiple of 16), and chunk
+// 2 ks + hh (2-byte types) or 4 ks + 2 hh (fp32) differs from the ks = 0 chunk by XOR
+// with 2 ks (resp. 4 ks): so the address is a per-lane base XOR a constant, plus the
+// immediate 32 jb rows.
 template <class In, int D>
-__device__ __forceinline__ typename In::frag_t lds_frag(const char* tile, int r, int k0) {
+__device__ __forceinline__ int frag_base(int l32, int hh) {
   using G = Geo<D, In::kES>;
+  return In::kES == 2 ? G::off(l32, hh) : G::off(l32, 2 * hh);
+}
+
+template <class In, int D>
+__device__ __forceinline__ typename In::frag_t lds_frag(const char* tile, int base, int jb, int ks) {
+  using G = Geo<D, In::kES>;
+  const char* row = tile + jb * 32 * G::kRowBytes;
   if constexpr (In::kES == 2) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(tile + G::off(r, k0 >> 3));
+    const u32x4 v = *reinterpret_cast<const u32x4*>(row + (base ^ (ks << 5)));
     return __builtin_bit_cast(typename In::frag_t, v);
   } else {
-    const f32x4 lo = *reinterpret_cast<const f32x4*>(tile + G::off(r, k0 >> 2));
-    const f32x4 hi = *reinterpret_cast<const f32x4*>(tile + G::off(r, (k0 >> 2) + 1));
+    const int o = base ^ (ks << 6);
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(row + o);
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(row + (o ^ 16));
     return f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
 }
@@ -255,7 +273,8 @@ void relkl_fwd_kernel(const FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds1[kStage];
   __shared__ double red[kWaves];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31, hh = lane >> 5;
   const int N = a.N;
 
@@ -304,6 +323,7 @@ void relkl_fwd_kernel(const FwdArgs a) {
     }
   }
 
+  const int fbase = frag_base<In, D>(l32, hh);
   const float c2 = a.c2;
   const float b_init = -kNegBig * c2;  // bias of an empty row: every real bias is below it
   float b_t = b_init, l_t = 0.f, acc_a = 0.f, b_s = b_init, l_s = 0.f;
@@ -323,11 +343,10 @@ void relkl_fwd_kernel(const FwdArgs a) {
       if (jb0 >= N) break;
       if (CAUSAL && jb0 > ib0 + 31) break;  // above every row of the wave
       f32x16 st = f32x16{}, ss = f32x16{};
-      const int lr = 32 * jb + l32;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const frag_t at = lds_frag<In, D>(tile_t, lr, 16 * ks + 8 * hh);
-        const frag_t as = lds_frag<In, D>(tile_s, lr, 16 * ks + 8 * hh);
+        const frag_t at = lds_frag<In, D>(tile_t, fbase, jb, ks);
+        const frag_t as = lds_frag<In, D>(tile_s, fbase, jb, ks);
         st = mma_k16(at, qt[ks], st);
         ss = mma_k16(as, qs[ks], ss);
       }
@@ -444,14 +463,7 @@ __device__ __forceinline__ void make_w(const f32x16& st, const f32x16& ss, float
 template <class Op>
 __device__ __forceinline__ typename Op::frag_t w_frag(const f32x8& w) {
   if constexpr (Op::kES == 2) {
-    u32x4 o;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const _Float16 lo = (_Float16)w[2 * q], hi = (_Float16)w[2 * q + 1];
-      o[q] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-             ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-    }
-    return __builtin_bit_cast(f16x8, o);
+    return __builtin_convertvector(w, f16x8);  // round to nearest even, two per instruction
   } else {
     return w;
   }
@@ -461,20 +473,27 @@ __device__ __forceinline__ typename Op::frag_t w_frag(const f32x8& w) {
 // j = jbase + 8 (e/4) + 4 hh + (e%4) (jbase = 32 jb + 16 kb), read transposed from the
 // row-major key tile.  ds_read_b64_tr_b16: in each 16-lane group, lane s gives the
 // address of row (r0 + s/4), columns c0 + 4 (s%4) .. +3, and lane q receives column
-// c0 + q of rows r0 .. r0 + 3.
+// c0 + q of rows r0 .. r0 + 3.  Here r0 = jbase + 8 half + 4 hh and c0 = 32 mb + 16 (g%2)
+// for lane group g; the row swizzle does not depend on jb or kb (multiples of 16 rows),
+// and mb only flips chunk bits 2-3, so the address is a per-lane base for each half,
+// XOR (mb << 6), plus the immediate jbase rows.
+template <int D>
+__device__ __forceinline__ int trb_base(int lane, int half) {
+  using G = Geo<D, 2>;
+  const int s = lane & 15, g = lane >> 4, hh = lane >> 5;
+  const int r = 8 * half + 4 * hh + (s >> 2);
+  const int col = 16 * (g & 1) + 4 * (s & 3);
+  return G::off(r, col >> 3) + (col & 7) * 2;
+}
+
 template <class Op, int D>
 __device__ __forceinline__ typename Op::frag_t grad_bfrag(const char* tile, int jbase, int mb,
-                                                          int lane) {
+                                                          int lane, int tb0, int tb1) {
   using G = Geo<D, Op::kES>;
   if constexpr (Op::kES == 2) {
-    const int s = lane & 15, g = lane >> 4, hh = lane >> 5;
-    const int col = 32 * mb + 16 * (g & 1) + 4 * (s & 3);  // element column
-    const int r0 = jbase + 4 * hh + (s >> 2);
-    const int r1 = r0 + 8;
-    const char* p0 = tile + G::off(r0, col >> 3) + (col & 7) * 2;
-    const char* p1 = tile + G::off(r1, col >> 3) + (col & 7) * 2;
-    const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)p0);
-    const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)p1);
+    const char* rows = tile + jbase * G::kRowBytes;
+    const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(rows + (tb0 ^ (mb << 6))));
+    const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(rows + (tb1 ^ (mb << 6))));
     const u32x2 a0 = __builtin_bit_cast(u32x2, v0), a1 = __builtin_bit_cast(u32x2, v1);
     return __builtin_bit_cast(f16x8, u32x4{a0[0], a0[1], a1[0], a1[1]});
   } else {
@@ -489,8 +508,18 @@ __device__ __forceinline__ typename Op::frag_t grad_bfrag(const char* tile, int 
   }
 }
 
+// Backward work decomposition: a workgroup of 8 waves owns kBRB = 256 rows (32 per
+// wave).  Waves 0-3 (group A) and 4-7 (group B) run the same sequence of phases, B one
+// barrier-separated slot behind A ("ping-pong"):
+//    M(n): gradient MFMAs of block n-1 (W(n-1) X_s) and score MFMAs of block n
+//    V(n): W(n) from the scores of block n (exp / VALU work)
+// where block n is the n-th 32-key half of the workgroup's key range.  Every SIMD holds
+// one wave of each group, so while one of its waves issues matrix instructions the
+// other issues vector instructions.  Key tile k (blocks 2k, 2k+1) lives in stage buffer
+// k % 2; it is read from A's M(2k) to B's M(2k+2), and tile k+1 is copied in during the
+// slot of A's M(2k+1) / B's V(2k) and waited for at the end of the next slot.
 template <class Op, int D, bool CAUSAL, bool OUT_F32>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void relkl_bwd_kernel(const BwdArgs a) {
   using elem_t = typename Op::elem_t;
   using frag_t = typename Op::frag_t;
@@ -499,12 +528,17 @@ void relkl_bwd_kernel(const BwdArgs a) {
   constexpr int MB = D / 32;  // 32-wide output blocks over d
   constexpr int kStats = 2 * kBC * 4;
   constexpr int kStage = 2 * G::kTileBytes + kStats;
+  constexpr int kDma = kBC * G::kCPR / (kWave * kBWaves);  // DMA instructions per wave per tile
+  static_assert(kBC * G::kCPR % (kWave * kBWaves) == 0, "tile must split evenly over 8 waves");
 
+  // two stage buffers as distinct objects (see the forward)
   __shared__ __attribute__((aligned(1024))) char lds0[kStage];
   __shared__ __attribute__((aligned(1024))) char lds1[kStage];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31, hh = lane >> 5;
+  const int group = wave >> 2;
   const int N = a.N;
 
   const int w = xcd_remap(blockIdx.x, gridDim.x);
@@ -536,27 +570,41 @@ void relkl_bwd_kernel(const BwdArgs a) {
   const float* rst_t = a.r_t + (int64_t)unit * a.npad;
   const float* rst_s = a.r_s + (int64_t)unit * a.npad;
 
-  const int i0 = I * kBR;
+  const int i0 = I * kBRB;
   const int ib0 = i0 + 32 * wave;
   const int row = ib0 + l32;
   const float c2 = a.c2;
+  const int fbase = frag_base<Op, D>(l32, hh);
+  const int tb0 = Op::kES == 2 ? trb_base<D>(lane, 0) : 0;
+  const int tb1 = Op::kES == 2 ? trb_base<D>(lane, 1) : 0;
 
   const int kt_begin = (int)(((int64_t)a.key_tiles * split) / a.splits);
   const int kt_end = (int)(((int64_t)a.key_tiles * (split + 1)) / a.splits);
+  const int NB = 2 * (kt_end - kt_begin);
 
-  // Stage: [teacher tile][student tile][teacher stats][student stats].  Statistics of a
-  // key tile are 2 x 256 bytes: lanes 0..15 of wave 0 copy the teacher's, 16..31 the
-  // student's (the reserve pads each unit's statistics to a multiple of kBC).
-  auto stage_tile = [&](int kt, char* st_base) {
-    const int j0 = kt * kBC;
-    dma_tile<D, Op::kES>(xt_c, tsn_b, j0, N, st_base, wave, lane);
-    dma_tile<D, Op::kES>(xs_c, ssn_b, j0, N, st_base + G::kTileBytes, wave, lane);
+  // Stage: [teacher tile][student tile][teacher stats][student stats]; all 8 waves copy
+  // their share of the two tiles, and lanes 0..31 of wave 0 the 2 x 256 bytes of
+  // statistics (the reserve pads each unit's statistics to a multiple of kBC).
+  auto stage_tile = [&](int k, char* st_base) __attribute__((always_inline)) {
+    const int j0 = (kt_begin + k) * kBC;
+#pragma unroll
+    for (int q = 0; q < kDma; ++q) {
+      const int slot0 = (wave * kDma + q) * kWave;
+      const int t = slot0 + lane;
+      const int r = t / G::kCPR;
+      const int c = (t % G::kCPR) ^ G::swz(r);
+      const int j = min(j0 + r, N - 1);
+      __builtin_amdgcn_global_load_lds(xt_c + (int64_t)j * tsn_b + c * 16,
+                                       (LDS_AS void*)(st_base + slot0 * 16), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(xs_c + (int64_t)j * ssn_b + c * 16,
+                                       (LDS_AS void*)(st_base + G::kTileBytes + slot0 * 16), 16, 0, 0);
+    }
     if (wave == 0 && lane < 32) {
       const float* src = (lane < 16 ? rst_t : rst_s) + j0 + 4 * (lane & 15);
       __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)(st_base + 2 * G::kTileBytes), 16, 0, 0);
     }
   };
-  if (kt_begin < kt_end) stage_tile(kt_begin, lds0);
+  if (NB > 0) stage_tile(0, lds0);
 
   frag_t qt[KS], qs[KS];
   float rt, rs;  // own row statistics
@@ -581,31 +629,52 @@ void relkl_bwd_kernel(const BwdArgs a) {
   f32x16 acc[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x16{};
+  f32x16 st = f32x16{}, ss = f32x16{};
+  frag_t wf0 = frag_t{}, wf1 = frag_t{};
 
-  auto step = [&](int kt, const char* cur, char* nxt) __attribute__((always_inline)) {
-    wait_vmem();
-    __syncthreads();
-    if (kt + 1 < kt_end) stage_tile(kt + 1, nxt);
-    const char* tile_t = cur;
-    const char* tile_s = tile_t + G::kTileBytes;
-    const float* stat_t = reinterpret_cast<const float*>(tile_t + 2 * G::kTileBytes);
-    const float* stat_s = stat_t + kBC;
-#pragma unroll 1
-    for (int jb = 0; jb < kBC / 32; ++jb) {
-      const int jb0 = kt * kBC + 32 * jb;
-      if (jb0 >= N) break;
-      f32x16 st = f32x16{}, ss = f32x16{};
-      const int lr = 32 * jb + l32;
+  auto block_j0 = [&](int n) { return (kt_begin + (n >> 1)) * kBC + 32 * (n & 1); };
+
+  // M(n): gradient of block n-1 from buffer gb, scores of block n from buffer sb; group A
+  // starts the copy of tile (n+1)/2 into db when n is odd.
+  auto m_phase = [&](int n, const char* sb, const char* gb, char* db) __attribute__((always_inline)) {
+    if (group == 0 && (n & 1) && ((n + 1) >> 1) < (NB >> 1)) stage_tile((n + 1) >> 1, db);
+    if (n >= 1 && block_j0(n - 1) < N) {
+      const char* tile_s = gb + G::kTileBytes;
+      const int jb = (n - 1) & 1;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const frag_t b0 = grad_bfrag<Op, D>(tile_s, 32 * jb, mb, lane, tb0, tb1);
+        const frag_t b1 = grad_bfrag<Op, D>(tile_s, 32 * jb + 16, mb, lane, tb0, tb1);
+        acc[mb] = mma_k16(wf0, b0, acc[mb]);
+        acc[mb] = mma_k16(wf1, b1, acc[mb]);
+      }
+    }
+    if (n < NB && block_j0(n) < N) {
+      const int jb = n & 1;
+      st = f32x16{};
+      ss = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const frag_t at = lds_frag<Op, D>(tile_t, lr, 16 * ks + 8 * hh);
-        const frag_t as = lds_frag<Op, D>(tile_s, lr, 16 * ks + 8 * hh);
+        const frag_t at = lds_frag<Op, D>(sb, fbase, jb, ks);
+        const frag_t as = lds_frag<Op, D>(sb + G::kTileBytes, fbase, jb, ks);
         st = mma_k16(at, qt[ks], st);
         ss = mma_k16(as, qs[ks], ss);
       }
+    }
+    if (group == 1 && (n & 1)) wait_vmem();
+    __syncthreads();
+  };
+
+  // V(n): W(n) from the scores of block n and the column statistics in buffer sb; group B
+  // starts the copy of tile n/2 + 1 into db when n is even.
+  auto v_phase = [&](int n, const char* sb, char* db) __attribute__((always_inline)) {
+    if (group == 1 && !(n & 1) && ((n >> 1) + 1) < (NB >> 1)) stage_tile((n >> 1) + 1, db);
+    const int jb0 = block_j0(n);
+    if (jb0 < N) {
+      const int jb = n & 1;
+      const float* clt = reinterpret_cast<const float*>(sb + 2 * G::kTileBytes) + 32 * jb;
+      const float* cls = clt + kBC;
       f32x8 w32[2];
-      const float* clt = stat_t + 32 * jb;
-      const float* cls = stat_s + 32 * jb;
       const int di = row - jb0;
       const int nl = N - jb0;
       const bool tail = jb0 + 32 > N;
@@ -623,22 +692,34 @@ void relkl_bwd_kernel(const BwdArgs a) {
           else make_w<3, false>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, w32);
         }
       }
-      const frag_t wf0 = w_frag<Op>(w32[0]);
-      const frag_t wf1 = w_frag<Op>(w32[1]);
-      // dX[I] += W[I, J] X_s[J]: A = W (row i per lane), B = X_s[J] (d per lane).
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const frag_t b0 = grad_bfrag<Op, D>(tile_s, 32 * jb, mb, lane);
-        const frag_t b1 = grad_bfrag<Op, D>(tile_s, 32 * jb + 16, mb, lane);
-        acc[mb] = mma_k16(wf0, b0, acc[mb]);
-        acc[mb] = mma_k16(wf1, b1, acc[mb]);
-      }
+      wf0 = w_frag<Op>(w32[0]);
+      wf1 = w_frag<Op>(w32[1]);
     }
+    if (group == 0 && (n & 1)) wait_vmem();
+    __syncthreads();
   };
-  for (int kt = kt_begin; kt < kt_end; kt += 2) {
-    step(kt, lds0, lds1);
-    if (kt + 1 < kt_end) step(kt + 1, lds1, lds0);
+
+  wait_vmem();
+  __syncthreads();
+  if (group == 1) __syncthreads();  // group B runs one slot behind group A
+  // Block n reads tile n/2 (buffer (n/2) % 2) and the previous block's tile; the
+  // pattern of buffers repeats every 4 blocks, written out so that every buffer is a
+  // known object in each phase.
+  for (int n = 0; n <= NB; n += 4) {
+    m_phase(n, lds0, lds1, lds1);
+    if (n == NB) break;
+    v_phase(n, lds0, lds1);
+    m_phase(n + 1, lds0, lds0, lds1);
+    if (n + 1 == NB) break;
+    v_phase(n + 1, lds0, lds1);
+    m_phase(n + 2, lds1, lds0, lds0);
+    if (n + 2 == NB) break;
+    v_phase(n + 2, lds1, lds0);
+    m_phase(n + 3, lds1, lds1, lds0);
+    if (n + 3 == NB) break;
+    v_phase(n + 3, lds1, lds0);
   }
+  if (group == 0) __syncthreads();  // same number of barriers in both groups
 
   // Scale and write: acc[mb][r] = dX[i][d] * 2^14 / (scale g) for
   // i = ib0 + 8 (r/4) + 4 hh + (r%4), d = 32 mb + l32.
@@ -661,7 +742,7 @@ void relkl_bwd_kernel(const BwdArgs a) {
       }
     }
   } else {
-    const int rows_pad = a.row_tiles * kBR;
+    const int rows_pad = a.row_tiles * kBRB;
     float* dst = a.partial + ((int64_t)split * a.B * a.H + unit) * rows_pad * D;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -735,8 +816,8 @@ int launch_fwd(const FwdArgs& a, bool in_bf16, int d, bool causal, float* loss, 
 template <class Op, int D, bool CAUSAL, bool OUT_F32>
 static int launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   const int grid = a.B * a.H * a.row_tiles * a.splits;
-  hipLaunchKernelGGL((relkl_bwd_kernel<Op, D, CAUSAL, OUT_F32>), dim3(grid), dim3(kThreads), 0, s,
-                     a);
+  hipLaunchKernelGGL((relkl_bwd_kernel<Op, D, CAUSAL, OUT_F32>), dim3(grid), dim3(kBWaves * kWave),
+                     0, s, a);
   return (int)hipGetLastError();
 }
 
