@@ -1,6 +1,7 @@
 """Throughput of the relation-KL hot path (forward + backward of Q/Q, K/K and V/V) on one GPU.
 
     python bench.py [--steps K] [--warmup W] [--workload llama2_32k] [--no-cpu-baseline]
+                    [--no-mem-sweep] [--calibrate-copy MIB]
 
 A step is one pass of the whole path over one batch: for each of the three relations the
 forward (LSE statistics + KL) and the backward (recompute + gradient) kernels.  Inputs are
@@ -12,9 +13,12 @@ events on the stream it runs on; its algorithmic FLOP count gives the roofline f
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import platform
+import re
+import statistics
 import sys
 import time
 
@@ -25,6 +29,32 @@ if ROOT not in sys.path:
 METRIC = "relation-KL fwd+bwd tokens/s at 32 heads,d=128,N=32K; % bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ("attention_relation_distillation_amd/csrc/relkl_kernels.hip",
+                  "attention_relation_distillation_amd/csrc/relkl_internal.h")
+TRAFFIC_PROFILE = "profiles/relkl_bwd_kernel_llama2_32k_hbm_traffic.md"
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per backward launch from the committed counter summary, or None when the
+    summary is missing, covers another workload, or was taken on other kernel sources."""
+    try:
+        with open(os.path.join(ROOT, TRAFFIC_PROFILE)) as f:
+            text = f.read()
+    except OSError:
+        return None
+    m = re.search(r"traffic: workload=(\S+) bytes_per_launch=(\d+) source_sha256=([0-9a-f]+)",
+                  text)
+    if not m or m.group(1) != workload or m.group(3) != kernel_source_digest():
+        return None
+    return int(m.group(2))
 
 
 def alg_flops(B, H, N, d, causal):
@@ -39,32 +69,84 @@ def alg_flops(B, H, N, d, causal):
     return B * H * 2 * per, B * H * 4 * per
 
 
-def cpu_baseline(rel, causal, rows):
-    """Time the float64 oracle on a bounded sample: forward and gradient of the last
-    `rows` rows of one unit (batch 0, head 0).  For a causal relation these rows are
-    self-contained (their column terms only involve rows j >= i of the same sample)."""
+def cpu_baseline(rel, causal, target_s=12.0):
+    """Time the float64 oracle on a bounded sample: forward and gradient of the last `rows`
+    rows of one unit (batch 0, head 0).  For a causal relation these rows are
+    self-contained (their column terms only involve rows j >= i of the same sample).  A
+    512-row probe sizes the sample to about `target_s` seconds of host time; the oracle's
+    cost is proportional to the number of rows it evaluates."""
     import numpy as np
     import oracle
 
     try:
-        cores = len(os.sched_getaffinity(0))
+        avail = len(os.sched_getaffinity(0))
     except AttributeError:
-        cores = os.cpu_count()
+        avail = os.cpu_count()
+    try:  # threads the oracle's BLAS calls actually run on
+        from threadpoolctl import threadpool_info
+        blas = [p["num_threads"] for p in threadpool_info() if p.get("user_api") == "blas"]
+        cores = min(max(blas), avail) if blas else 1
+    except ImportError:
+        cores = avail
     x_t = rel.x_t[0, 0].double().numpy()
     x_s = rel.x_s[0, 0].double().numpy()
     n = x_t.shape[0]
-    r0 = n - rows
-    sel = np.arange(r0, n)
     s = oracle.default_scale(x_t.shape[1])
-    t0 = time.perf_counter()
-    lt, ls, kl = oracle.forward_unit(x_t, x_s, s, causal, chunk=1024, rows=sel)
-    full_lt = np.full(n, np.nan)
-    full_ls = np.full(n, np.nan)
-    full_lt[sel], full_ls[sel] = lt, ls
-    oracle.backward_unit(x_t, x_s, s, causal, 1.0, lse_t=full_lt, lse_s=full_ls, rows=sel,
-                         chunk=1024)
-    dt = time.perf_counter() - t0
-    return dt, cores
+
+    def run(rows):
+        sel = np.arange(n - rows, n)
+        t0 = time.perf_counter()
+        lt, ls, kl = oracle.forward_unit(x_t, x_s, s, causal, chunk=1024, rows=sel)
+        full_lt = np.full(n, np.nan)
+        full_ls = np.full(n, np.nan)
+        full_lt[sel], full_ls[sel] = lt, ls
+        oracle.backward_unit(x_t, x_s, s, causal, 1.0, lse_t=full_lt, lse_s=full_ls, rows=sel,
+                             chunk=1024)
+        return time.perf_counter() - t0
+
+    probe = min(512, n)
+    t_probe = run(probe)
+    rows = int(min(n, max(probe, round(probe * target_s / max(t_probe, 1e-3) / 512) * 512)))
+    dt = run(rows)
+    return dt, rows, cores
+
+
+def mem_sweep(relkl, torch, dev, d=128, H=32, ns=(4096, 8192, 16384, 32768)):
+    """Extra device memory of one causal bf16 relation call (fwd + bwd) against N: the peak
+    allocation during the call beyond the inputs and the gradient it returns, next to the
+    library's own reserve/workspace sizes and a materialised fp32 relation (H N^2 4 B)."""
+    rows = []
+    for n in ns:
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        g = torch.Generator(device=dev).manual_seed(n)
+        xt = torch.randn((1, H, n, d), generator=g, device=dev, dtype=torch.float32).bfloat16()
+        xs = (xt.float() + 0.05 * torch.randn(xt.shape, generator=g, device=dev)).bfloat16()
+        gl = torch.ones((), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated(dev)
+        torch.cuda.reset_peak_memory_stats(dev)
+        f = relkl.relkl_fwd(xt, xs, causal=True)
+        dx = relkl.relkl_bwd(xt, xs, f["reserve"], gl, causal=True)
+        torch.cuda.synchronize()
+        extra = torch.cuda.max_memory_allocated(dev) - base - dx.numel() * dx.element_size()
+        rows.append({"N": n, "extra_mb": round(extra / 1e6, 2),
+                     "reserve_mb": round(f["reserve"].numel() / 1e6, 2),
+                     "bwd_workspace_mb": round(relkl.workspace_size(xt, xs, pass_=1) / 1e6, 2),
+                     "materialised_fp32_gb": round(H * n * n * 4 / 1e9, 2)})
+        del xt, xs, f, dx
+    # least-squares slope / intercept of extra bytes against N
+    xs_ = [r["N"] for r in rows]
+    ys_ = [r["extra_mb"] * 1e6 for r in rows]
+    mx, my = sum(xs_) / len(xs_), sum(ys_) / len(ys_)
+    slope = (sum((x - mx) * (y - my) for x, y in zip(xs_, ys_))
+             / sum((x - mx) ** 2 for x in xs_))
+    return {"H": H, "d": d, "points": rows, "fit_bytes_per_token": round(slope, 1),
+            "fit_intercept_mb": round((my - slope * mx) / 1e6, 3)}
+
+
+def stats_ms(v):
+    return {"median": round(statistics.median(v), 3), "min": round(min(v), 3)}
 
 
 def main():
@@ -74,7 +156,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama2_32k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=2048)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="host time the oracle sample is sized to")
+    ap.add_argument("--no-mem-sweep", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="before the steps, copy a MIB-MiB buffer three times (a plain copy "
+                         "kernel of known size, for scaling HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -89,6 +176,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    relkl.load_library()
     wl = workloads.WORKLOADS[args.workload]
     causal = wl.masks[0]
     t_gen = time.perf_counter()
@@ -100,6 +188,16 @@ def main():
         gpu.append((r.name, r.x_t.to(dev), r.x_s.to(dev)))
     gl = torch.ones((), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
+
+    if args.calibrate_copy > 0:
+        src = torch.ones(args.calibrate_copy << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copy calibration: 3 x {args.calibrate_copy} MiB", file=sys.stderr,
+              flush=True)
+        del src, dst
 
     stream = torch.cuda.current_stream(dev)
     ev_log = []
@@ -132,15 +230,17 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
+    print("[bench] timed steps done", file=sys.stderr, flush=True)
 
-    fwd_ms = sum(e0.elapsed_time(e1) for _, e0, e1, _ in ev_log) / args.steps
+    fwd_launch_ms = [e0.elapsed_time(e1) for _, e0, e1, _ in ev_log]
     bwd_launch_ms = [e1.elapsed_time(e2) for _, _, e1, e2 in ev_log]
+    fwd_ms = sum(fwd_launch_ms) / args.steps
     bwd_ms = sum(bwd_launch_ms) / args.steps
     per_rel = {}
     for name, e0, e1, e2 in ev_log:
-        a = per_rel.setdefault(name, [0.0, 0.0])
-        a[0] += e0.elapsed_time(e1) / args.steps
-        a[1] += e1.elapsed_time(e2) / args.steps
+        a = per_rel.setdefault(name, ([], []))
+        a[0].append(e0.elapsed_time(e1))
+        a[1].append(e1.elapsed_time(e2))
 
     tokens = wl.B * wl.N
     value = tokens / (ms_per_step / 1e3)
@@ -153,14 +253,15 @@ def main():
         fl_b += b_
         bwd_flops_per_launch.append(b_)
     # dominant kernel: the backward; achieved = its algorithmic FLOPs per launch divided by
-    # its mean launch duration, averaged over launches (one per relation per step)
+    # its mean launch duration (launches of all relations pooled; equal shapes here)
     n_rel = len(rels)
-    ach = []
-    for k, ms in enumerate(bwd_launch_ms):
-        ach.append(bwd_flops_per_launch[k % n_rel] / (ms / 1e3) / 1e12)
-    achieved = sum(ach) / len(ach)
+    mean_bwd_flops = sum(bwd_flops_per_launch) / n_rel
+    mean_bwd_s = sum(bwd_launch_ms) / len(bwd_launch_ms) / 1e3
+    achieved = mean_bwd_flops / mean_bwd_s / 1e12
     total_tflops = (fl_f + fl_b) / (ms_per_step / 1e3) / 1e12
+    traffic = measured_traffic(wl.name)
 
+    props = torch.cuda.get_device_properties(dev)
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -180,21 +281,30 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "relkl_bwd_kernel",
                      "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": traffic,
+                     "alg_flops_per_launch": mean_bwd_flops,
+                     "mean_launch_ms": round(mean_bwd_s * 1e3, 3)},
         "alg_tflops_total": round(total_tflops, 1),
         "frac_of_bf16_peak_total": round(total_tflops / PEAK_BF16_TFLOPS, 4),
         "fwd_ms": round(fwd_ms, 3),
         "bwd_ms": round(bwd_ms, 3),
-        "per_relation_ms": {k: [round(v[0], 3), round(v[1], 3)] for k, v in per_rel.items()},
+        "per_relation_ms": {k: {"fwd": stats_ms(v[0]), "bwd": stats_ms(v[1])}
+                            for k, v in per_rel.items()},
         "peak_mem_gb": round(torch.cuda.max_memory_allocated(dev) / 1e9, 3),
-        "device": torch.cuda.get_device_name(dev),
+        "device": f"{props.name} ({getattr(props, 'gcnArchName', '?')}, "
+                  f"{props.multi_processor_count} CUs)",
+        "kernel_sources": kernel_source_digest(),
         "cpu_baseline": None,
     }
 
+    if not args.no_mem_sweep:
+        del gpu
+        out["extra_memory_vs_N"] = mem_sweep(relkl, torch, dev)
+        print("[bench] memory sweep done", file=sys.stderr, flush=True)
+
     if not args.no_cpu_baseline:
-        rows = min(args.cpu_rows, wl.N)
         rel0 = rels[0]
-        dt, cores = cpu_baseline(rel0, causal, rows)
+        dt, rows, cores = cpu_baseline(rel0, causal, args.cpu_seconds)
         # the oracle's cost is proportional to rows x N (it evaluates full rows), so one
         # unit costs N / rows samples and the step has sum over relations of B * H units
         units = sum(wl.B * r.x_t.shape[1] for r in rels)
@@ -203,9 +313,11 @@ def main():
             "value": round(tokens / est_step_s, 3), "unit": "tokens/s", "cores": cores,
             "kind": "oracle",
             "sample": (f"float64 oracle forward+gradient of the last {rows} rows of one "
-                       f"{rel0.name} head at N={wl.N} ({dt:.2f}s), extrapolated x{wl.N // rows} "
-                       f"rows x {units} units; host {platform.processor() or platform.machine()}"),
+                       f"{rel0.name} head at N={wl.N} ({dt:.2f}s), extrapolated (labelled as "
+                       f"such) x{wl.N / rows:.2f} rows x {units} units; host "
+                       f"{platform.processor() or platform.machine()}"),
             "sample_seconds": round(dt, 3),
+            "extrapolated": True,
         }
     print(json.dumps(out), flush=True)
 

@@ -18,7 +18,8 @@ What it computes (page "LinearARD ... verdict" on pith.science, fields
   (the identity stated in key_machinery; there with the 1/n factor).  The student
   matrix X_s appears on both sides of X_s X_s^T, so
   dL/dX_s = scale * (dZ + dZ^T) X_s with dZ = g * (R_s - R_t), zero where masked.
-  The teacher is frozen and gets no gradient (abstract: "frozen native-RoPE teacher").
+  The teacher is frozen and gets no gradient (the abstract describes the teacher as a
+  fixed model with native RoPE).
 
 Readings where the pages are silent (all listed in the design notes):
 * causal mask keeps j <= i (diagonal included); non-causal keeps everything;
