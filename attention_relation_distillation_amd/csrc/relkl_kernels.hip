@@ -7,15 +7,17 @@
 // dL/dZ_s = g * (R_s - R_t).  The arXiv abstract (mlsanity.com) states that the kernel
 // fuses the logit recomputation into the backward and is exact.
 //
-// Layout of the work (one workgroup = 4 wave64s; two workgroups per CU, so every SIMD
-// runs two waves and one wave's exp/VALU work overlaps the other's MFMA work):
-//  * A row tile is 128 consecutive rows i of one (batch, head) unit; each wave owns 32
-//    of them and keeps their teacher and student rows in registers as MFMA B operands.
+// Layout of the work:
+//  * Forward: a workgroup of 4 wave64s owns a row tile of 128 consecutive rows i of one
+//    (batch, head) unit, 32 per wave; two workgroups share a CU, so every SIMD runs two
+//    waves.  Backward: a workgroup of 8 waves (two per SIMD) owns 256 rows.  Each wave keeps
+//    its rows of the teacher and student as MFMA B operands in registers.
 //  * Key tiles of 64 rows j are copied global -> LDS by the DMA path
-//    (global_load_lds_dwordx4), double-buffered, one barrier per tile.  LDS rows are
-//    unpadded; their 16-byte chunks are XOR-swizzled by the row so that both the
-//    16-byte fragment reads of the score contraction and the transposed 8-byte reads of
-//    the gradient contraction hit distinct banks.
+//    (global_load_lds_dwordx4), double-buffered in the forward and triple-buffered in the
+//    backward, one barrier per tile.  LDS rows are unpadded; their 16-byte chunks are
+//    XOR-swizzled by the row so that both the 16-byte fragment reads of the score
+//    contraction and the transposed 8-byte reads of the gradient contraction hit distinct
+//    banks.  Fragment reads run ahead of their MFMAs (explicit software pipelines).
 //  * Score blocks are computed transposed, S^T[j][i] = <X[j], X[i]>, with
 //    v_mfma_f32_32x32x16 (fp32 inputs: v_mfma_f32_32x32x2f32), so that a lane holds one
 //    row i and 16 of its columns j: row statistics reduce inside the lane, and the
@@ -24,7 +26,7 @@
 //    teacher and student; the two half-waves sharing a row merge at the end.  It also
 //    writes the reserve: fp16 copies of its rows (bf16 inputs) and the row statistics
 //    in log2 units.
-//  * Backward: the owner of row tile I sweeps the whole row (all key tiles), forms
+//  * Backward: the owner of a row tile sweeps the whole row (all key tiles), forms
 //    W = dZ + dZ^T block by block (row statistics below the diagonal, column statistics
 //    above it, both on it), carries W * 2^14 as fp16 and accumulates W X_s on
 //    v_mfma_f32_32x32x16_f16, reading X_s transposed from the row-major key tile with
@@ -34,6 +36,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
+
+#include <array>
+#include <utility>
 
 #include "relkl_internal.h"
 
@@ -122,6 +127,34 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 // Wait for this wave's outstanding vector-memory operations (the LDS DMA included).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// 32-bit LDS address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)(const LDS_AS char*)p;
+}
+
+// LDS copy of 16 bytes per lane (lane l writes lds_base + 16 l), issued as inline assembly
+// so that the compiler does not track it.  The backward reads stage buffers chosen at run
+// time; tracking the copies, the compiler would wait for all of them before any LDS read
+// it cannot prove disjoint from a copy target.  Completion is awaited explicitly with
+// wait_vmem().  The s_nop covers the one wait state needed between writing M0 and the
+// copy.
+__device__ __forceinline__ void lds_copy16(const void* g, uint32_t lds_base) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds_base) : "memory");
+}
+
+// Workgroup barrier of the backward's tile pipeline.  It completes this wave's LDS reads
+// (lgkmcnt(0)) and keeps the compiler from moving memory accesses across it, but unlike
+// __syncthreads() it does not wait for the wave's LDS copies still in flight (the fence
+// of __syncthreads() waits for every outstanding memory operation).  A copied tile is
+// published by an explicit wait_vmem() of every issuing wave before the barrier after
+// which it is read.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // ------------------------------------------------------------------ LDS key tiles
 // Row-major [kBC][D] tile, 16-byte chunks of row r stored at chunk (c ^ swz(r)).  The LDS
 // has 64 four-byte banks, i.e. 16 chunk slots per 256-byte bank line.  For rows of 16 or
@@ -191,6 +224,32 @@ __device__ __forceinline__ typename In::frag_t lds_frag(const char* tile, int ba
   }
 }
 
+// ------------------------------------------------------------------ LDS read pipelines
+// A single wave only sustains about 30 B/clk of LDS reads with a few reads in flight, while
+// its MFMAs consume a 1 KB fragment per 32 cycles; so matrix phases request fragments as
+// far ahead of their MFMAs as the LGKM counter allows: before each MFMA, further fragments
+// are requested while at most kMaxLdsOps reads are outstanding (the counter tracks 15).
+constexpr int kMaxLdsOps = 8;
+
+template <int NG, int NF, int OPS_G, int OPS_S>
+struct LoadSchedule {
+  // LDS instructions of fragment k: OPS_G per gradient fragment, OPS_S per score fragment
+  static constexpr int ops(int k) { return k < NG ? OPS_G : OPS_S; }
+  // upto[f]: fragments [0, upto[f]) are requested before the MFMA of fragment f
+  static constexpr std::array<int, NF> make() {
+    std::array<int, NF> a{};
+    int issued = 0;
+    for (int f = 0; f < NF; ++f) {
+      int inflight = 0;
+      for (int k = f; k < issued; ++k) inflight += ops(k);
+      while (issued < NF && inflight + ops(issued) <= kMaxLdsOps) inflight += ops(issued++);
+      a[f] = issued;
+    }
+    return a;
+  }
+  static constexpr std::array<int, NF> upto = make();
+};
+
 // ------------------------------------------------------------------ forward
 // Online update of one lane's row statistics with the 16 columns it holds of a 32x32
 // score block (raw scores S; logits z = scale S; c2 = scale log2 e).
@@ -245,6 +304,40 @@ __device__ __forceinline__ void online_update(const f32x16& st, const f32x16& ss
   b_s = bn_s;
 }
 
+// Fast path of the online update for a block without masked entries: the exponentials use
+// the lane's current biases as they are, so no block maximum is formed.  The block is
+// accumulated only if both block sums are at most 2^64, which bounds every exponential
+// (and rules out inf / NaN); then the running sums stay finite and exact in the sense of
+// the bias form above.  Otherwise (a row's first block, whose bias is still the empty-row
+// value, or a row maximum that grew by more than 64 in log2 units) nothing is changed and
+// the caller runs the exact path.  Returns whether the block was accumulated.
+__device__ __forceinline__ bool online_update_fast(const f32x16& st, const f32x16& ss, float c2,
+                                                   float b_t, float b_s, float& l_t,
+                                                   float& acc_a, float& l_s) {
+  float lt0 = 0.f, lt1 = 0.f, ls0 = 0.f, ls1 = 0.f, a0 = 0.f, a1 = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; r += 2) {
+    const float et0 = fast_exp2(fmaf(st[r], c2, b_t));
+    const float es0 = fast_exp2(fmaf(ss[r], c2, b_s));
+    const float et1 = fast_exp2(fmaf(st[r + 1], c2, b_t));
+    const float es1 = fast_exp2(fmaf(ss[r + 1], c2, b_s));
+    lt0 += et0;
+    ls0 += es0;
+    a0 = fmaf(et0, st[r] - ss[r], a0);
+    lt1 += et1;
+    ls1 += es1;
+    a1 = fmaf(et1, st[r + 1] - ss[r + 1], a1);
+  }
+  const float sum_t = lt0 + lt1, sum_s = ls0 + ls1;
+  const bool ok = sum_t <= 0x1p64f && sum_s <= 0x1p64f;
+  if (ok) {
+    l_t += sum_t;
+    l_s += sum_s;
+    acc_a += a0 + a1;
+  }
+  return ok;
+}
+
 __device__ __forceinline__ u32x4 bf16x8_to_f16x8_bits(const bf16x8& v) {
   const u32x4 w = __builtin_bit_cast(u32x4, v);
   u32x4 o;
@@ -256,6 +349,43 @@ __device__ __forceinline__ u32x4 bf16x8_to_f16x8_bits(const bf16x8& v) {
     o[q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
   }
   return o;
+}
+
+// Score contraction of one 32 x 32 block of the forward as a software pipeline: the LDS
+// reads of the key fragments run ahead of their MFMAs with at most kMaxLdsOps reads in
+// flight (see the backward's matrix phase).
+template <class In, int D>
+__device__ __forceinline__ void score_pipeline(const char* tile_t, const char* tile_s, int fbase,
+                                               int jb, const typename In::frag_t (&qt)[D / 16],
+                                               const typename In::frag_t (&qs)[D / 16],
+                                               f32x16& st, f32x16& ss) {
+  using frag_t = typename In::frag_t;
+  constexpr int KS = D / 16, NF = 2 * KS;
+  using S = LoadSchedule<0, NF, 1, In::kES == 2 ? 1 : 2>;
+  frag_t fr[NF];
+  auto load = [&](auto fc) __attribute__((always_inline)) {
+    constexpr int f = decltype(fc)::value, ks = f / 2, m = f % 2;
+    fr[f] = lds_frag<In, D>(m ? tile_s : tile_t, fbase, jb, ks);
+  };
+  auto mma = [&](auto fc) __attribute__((always_inline)) {
+    constexpr int f = decltype(fc)::value, ks = f / 2, m = f % 2;
+    if constexpr (m == 0) st = mma_k16(fr[f], qt[ks], st);
+    else ss = mma_k16(fr[f], qs[ks], ss);
+  };
+  st = f32x16{};
+  ss = f32x16{};
+  [&]<int... I>(std::integer_sequence<int, I...>) {
+    ((
+      [&] {
+        constexpr int lo = I == 0 ? 0 : S::upto[I == 0 ? 0 : I - 1];
+        [&]<int... J>(std::integer_sequence<int, J...>) {
+          (load(std::integral_constant<int, lo + J>{}), ...);
+        }(std::make_integer_sequence<int, S::upto[I] - lo>{});
+        __builtin_amdgcn_sched_barrier(0);
+        mma(std::integral_constant<int, I>{});
+        __builtin_amdgcn_sched_barrier(0);
+      }()), ...);
+  }(std::make_integer_sequence<int, NF>{});
 }
 
 template <class In, int D, bool CAUSAL>
@@ -342,18 +472,12 @@ void relkl_fwd_kernel(const FwdArgs a) {
       const int jb0 = kt * kBC + 32 * jb;
       if (jb0 >= N) break;
       if (CAUSAL && jb0 > ib0 + 31) break;  // above every row of the wave
-      f32x16 st = f32x16{}, ss = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const frag_t at = lds_frag<In, D>(tile_t, fbase, jb, ks);
-        const frag_t as = lds_frag<In, D>(tile_s, fbase, jb, ks);
-        st = mma_k16(at, qt[ks], st);
-        ss = mma_k16(as, qs[ks], ss);
-      }
+      f32x16 st, ss;
+      score_pipeline<In, D>(tile_t, tile_s, fbase, jb, qt, qs, st, ss);
       const bool need_mask = (CAUSAL && jb0 + 31 > ib0) || (jb0 + 32 > N);
       if (need_mask)
         online_update<true, CAUSAL>(st, ss, jb0, row, hh, N, c2, b_t, l_t, acc_a, b_s, l_s);
-      else
+      else if (!online_update_fast(st, ss, c2, b_t, b_s, l_t, acc_a, l_s))
         online_update<false, CAUSAL>(st, ss, jb0, row, hh, N, c2, b_t, l_t, acc_a, b_s, l_s);
     }
   };
@@ -508,16 +632,78 @@ __device__ __forceinline__ typename Op::frag_t grad_bfrag(const char* tile, int 
   }
 }
 
-// Backward work decomposition: a workgroup of 8 waves owns kBRB = 256 rows (32 per
-// wave).  Waves 0-3 (group A) and 4-7 (group B) run the same sequence of phases, B one
-// barrier-separated slot behind A ("ping-pong"):
+// Matrix phase of the backward as an explicit software pipeline over "fragments": first the
+// 2 MB gradient B fragments of the previous block (two transposed 8-byte LDS reads each),
+// then the 2 KS score A fragments of the current block (one 16-byte read each), one MFMA
+// per fragment, with the reads running ahead of their MFMAs as LoadSchedule allows.
+// Scheduling barriers keep that order; consecutive MFMAs use different accumulators.
+
+// Gradient fragment f of a matrix phase: k-half h = f / MB, output block mb = f % MB.
+template <class Op, int D, int F>
+__device__ __forceinline__ typename Op::frag_t grad_frag(const char* gtile, int jbg, int lane,
+                                                         int tb0, int tb1) {
+  constexpr int MB = D / 32, mb = F % MB, h = F / MB;
+  return grad_bfrag<Op, D>(gtile, jbg + 16 * h, mb, lane, tb0, tb1);
+}
+
+template <class Op, int D>
+__device__ __forceinline__ void m_pipeline(const char* gtile, int jbg, const char* stile, int jbs,
+                                           int fbase, int lane, int tb0, int tb1,
+                                           const typename Op::frag_t& wf0,
+                                           const typename Op::frag_t& wf1,
+                                           const typename Op::frag_t (&qt)[D / 16],
+                                           const typename Op::frag_t (&qs)[D / 16],
+                                           f32x16 (&acc)[D / 32], f32x16& st, f32x16& ss) {
+  using frag_t = typename Op::frag_t;
+  using G = Geo<D, Op::kES>;
+  constexpr int KS = D / 16, MB = D / 32;
+  constexpr int NG = 2 * MB;
+  constexpr int NF = NG + 2 * KS;
+  using S = LoadSchedule<NG, NF, Op::kES == 2 ? 2 : 8, Op::kES == 2 ? 1 : 2>;
+  frag_t fr[NF];
+  auto load = [&](auto fc) __attribute__((always_inline)) {
+    constexpr int f = decltype(fc)::value;
+    if constexpr (f < NG) {
+      fr[f] = grad_frag<Op, D, f>(gtile, jbg, lane, tb0, tb1);
+    } else {
+      constexpr int k = f - NG, ks = k / 2, m = k % 2;
+      fr[f] = lds_frag<Op, D>(m ? stile + G::kTileBytes : stile, fbase, jbs, ks);
+    }
+  };
+  auto mma = [&](auto fc) __attribute__((always_inline)) {
+    constexpr int f = decltype(fc)::value;
+    if constexpr (f < NG) {
+      constexpr int mb = f % MB, h = f / MB;
+      acc[mb] = mma_k16(h ? wf1 : wf0, fr[f], acc[mb]);
+    } else {
+      constexpr int k = f - NG, ks = k / 2, m = k % 2;
+      if constexpr (m == 0) st = mma_k16(fr[f], qt[ks], st);
+      else ss = mma_k16(fr[f], qs[ks], ss);
+    }
+  };
+  st = f32x16{};
+  ss = f32x16{};
+  [&]<int... I>(std::integer_sequence<int, I...>) {
+    ((
+      [&] {
+        constexpr int lo = I == 0 ? 0 : S::upto[I == 0 ? 0 : I - 1];
+        [&]<int... J>(std::integer_sequence<int, J...>) {
+          (load(std::integral_constant<int, lo + J>{}), ...);
+        }(std::make_integer_sequence<int, S::upto[I] - lo>{});
+        __builtin_amdgcn_sched_barrier(0);
+        mma(std::integral_constant<int, I>{});
+        __builtin_amdgcn_sched_barrier(0);
+      }()), ...);
+  }(std::make_integer_sequence<int, NF>{});
+}
+
+// Backward work decomposition: a workgroup of 8 waves (two per SIMD) owns kBRB = 256 rows,
+// 32 per wave, and sweeps the whole key range in key tiles of 64 rows (two 32-key blocks).
+// For each block n a wave runs
 //    M(n): gradient MFMAs of block n-1 (W(n-1) X_s) and score MFMAs of block n
 //    V(n): W(n) from the scores of block n (exp / VALU work)
-// where block n is the n-th 32-key half of the workgroup's key range.  Every SIMD holds
-// one wave of each group, so while one of its waves issues matrix instructions the
-// other issues vector instructions.  Key tile k (blocks 2k, 2k+1) lives in stage buffer
-// k % 2; it is read from A's M(2k) to B's M(2k+2), and tile k+1 is copied in during the
-// slot of A's M(2k+1) / B's V(2k) and waited for at the end of the next slot.
+// The waves drift freely between the barriers that separate key tiles, so one wave's
+// vector work overlaps its SIMD partner's matrix work.
 template <class Op, int D, bool CAUSAL, bool OUT_F32>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void relkl_bwd_kernel(const BwdArgs a) {
@@ -531,14 +717,13 @@ void relkl_bwd_kernel(const BwdArgs a) {
   constexpr int kDma = kBC * G::kCPR / (kWave * kBWaves);  // DMA instructions per wave per tile
   static_assert(kBC * G::kCPR % (kWave * kBWaves) == 0, "tile must split evenly over 8 waves");
 
-  // two stage buffers as distinct objects (see the forward)
-  __shared__ __attribute__((aligned(1024))) char lds0[kStage];
-  __shared__ __attribute__((aligned(1024))) char lds1[kStage];
+  // Stage buffers: three when they fit in the LDS (bf16 inputs), else two (fp32, d = 128).
+  constexpr int kStages = 3 * kStage <= 160 * 1024 ? 3 : 2;
+  __shared__ __attribute__((aligned(1024))) char lds[kStages * kStage];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31, hh = lane >> 5;
-  const int group = wave >> 2;
   const int N = a.N;
 
   const int w = xcd_remap(blockIdx.x, gridDim.x);
@@ -594,17 +779,21 @@ void relkl_bwd_kernel(const BwdArgs a) {
       const int r = t / G::kCPR;
       const int c = (t % G::kCPR) ^ G::swz(r);
       const int j = min(j0 + r, N - 1);
-      __builtin_amdgcn_global_load_lds(xt_c + (int64_t)j * tsn_b + c * 16,
-                                       (LDS_AS void*)(st_base + slot0 * 16), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(xs_c + (int64_t)j * ssn_b + c * 16,
-                                       (LDS_AS void*)(st_base + G::kTileBytes + slot0 * 16), 16, 0, 0);
+      lds_copy16(xt_c + (int64_t)j * tsn_b + c * 16, lds_addr(st_base + slot0 * 16));
+      lds_copy16(xs_c + (int64_t)j * ssn_b + c * 16, lds_addr(st_base + G::kTileBytes + slot0 * 16));
     }
     if (wave == 0 && lane < 32) {
       const float* src = (lane < 16 ? rst_t : rst_s) + j0 + 4 * (lane & 15);
-      __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)(st_base + 2 * G::kTileBytes), 16, 0, 0);
+      lds_copy16(src, lds_addr(st_base + 2 * G::kTileBytes));
     }
   };
-  if (NB > 0) stage_tile(0, lds0);
+  const int ntiles = NB >> 1;
+  // stage buffer of tile t (t >= 0)
+  auto buf = [&](int t) __attribute__((always_inline)) { return lds + (t % kStages) * kStage; };
+  if (ntiles > 0) stage_tile(0, buf(0));
+  // M(0)'s gradient part reads the last buffer's student tile before any copy fills it
+  for (int q = tid; q < G::kTileBytes / 16; q += kBWaves * kWave)
+    *reinterpret_cast<u32x4*>(buf(kStages - 1) + G::kTileBytes + 16 * q) = u32x4{0u, 0u, 0u, 0u};
 
   frag_t qt[KS], qs[KS];
   float rt, rs;  // own row statistics
@@ -634,41 +823,30 @@ void relkl_bwd_kernel(const BwdArgs a) {
 
   auto block_j0 = [&](int n) { return (kt_begin + (n >> 1)) * kBC + 32 * (n & 1); };
 
-  // M(n): gradient of block n-1 from buffer gb, scores of block n from buffer sb; group A
-  // starts the copy of tile (n+1)/2 into db when n is odd.
-  auto m_phase = [&](int n, const char* sb, const char* gb, char* db) __attribute__((always_inline)) {
-    if (group == 0 && (n & 1) && ((n + 1) >> 1) < (NB >> 1)) stage_tile((n + 1) >> 1, db);
-    if (n >= 1 && block_j0(n - 1) < N) {
-      const char* tile_s = gb + G::kTileBytes;
-      const int jb = (n - 1) & 1;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const frag_t b0 = grad_bfrag<Op, D>(tile_s, 32 * jb, mb, lane, tb0, tb1);
-        const frag_t b1 = grad_bfrag<Op, D>(tile_s, 32 * jb + 16, mb, lane, tb0, tb1);
-        acc[mb] = mma_k16(wf0, b0, acc[mb]);
-        acc[mb] = mma_k16(wf1, b1, acc[mb]);
-      }
-    }
-    if (n < NB && block_j0(n) < N) {
-      const int jb = n & 1;
-      st = f32x16{};
-      ss = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const frag_t at = lds_frag<Op, D>(sb, fbase, jb, ks);
-        const frag_t as = lds_frag<Op, D>(sb + G::kTileBytes, fbase, jb, ks);
-        st = mma_k16(at, qt[ks], st);
-        ss = mma_k16(as, qs[ks], ss);
-      }
-    }
-    if (group == 1 && (n & 1)) wait_vmem();
-    __syncthreads();
+  // Every wave runs M(n) then V(n) for its own rows; the two waves of a SIMD drift freely,
+  // so one wave's exp/VALU work overlaps the other's MFMAs and both keep LDS reads in
+  // flight.  Barriers only separate key tiles (two blocks each):
+  //  * three buffers: step t copies tile t+1 into the buffer of tile t-2 (last read in
+  //    step t-1) at its start and awaits it at its end;
+  //  * two buffers (fp32, d = 128): tile t+1 goes into the buffer of tile t-1, whose last
+  //    reads are the gradient MFMAs of M(2t); a barrier after M(2t) precedes the copy.
+  // The barrier ending step t publishes tile t+1 to every wave.
+
+  // M(n): gradient of block n-1, scores of block n.  Every M runs the full pipeline: M(0)
+  // contracts the initial zero W with the zero-filled student tile of the last buffer;
+  // blocks at or beyond N contract a zero W (V leaves zero fragments) with finite copies
+  // of row N-1 and their scores are never used; M(NB) computes unused scores from a buffer
+  // no copy is writing into.
+  auto m_phase = [&](int n) __attribute__((always_inline)) {
+    const char* sb = buf(n >> 1);
+    const char* gtile = (n == 0 ? buf(kStages - 1) : buf((n - 1) >> 1)) + G::kTileBytes;
+    const int jbg = 32 * ((n - 1) & 1), jbs = n & 1;
+    m_pipeline<Op, D>(gtile, jbg, sb, jbs, fbase, lane, tb0, tb1, wf0, wf1, qt, qs, acc, st, ss);
   };
 
-  // V(n): W(n) from the scores of block n and the column statistics in buffer sb; group B
-  // starts the copy of tile n/2 + 1 into db when n is even.
-  auto v_phase = [&](int n, const char* sb, char* db) __attribute__((always_inline)) {
-    if (group == 1 && !(n & 1) && ((n >> 1) + 1) < (NB >> 1)) stage_tile((n >> 1) + 1, db);
+  // V(n): W(n) from the scores of block n and the column statistics staged with its tile.
+  auto v_phase = [&](int n) __attribute__((always_inline)) {
+    const char* sb = buf(n >> 1);
     const int jb0 = block_j0(n);
     if (jb0 < N) {
       const int jb = n & 1;
@@ -694,32 +872,28 @@ void relkl_bwd_kernel(const BwdArgs a) {
       }
       wf0 = w_frag<Op>(w32[0]);
       wf1 = w_frag<Op>(w32[1]);
+    } else {
+      wf0 = frag_t{};
+      wf1 = frag_t{};
     }
-    if (group == 0 && (n & 1)) wait_vmem();
-    __syncthreads();
   };
 
   wait_vmem();
   __syncthreads();
-  if (group == 1) __syncthreads();  // group B runs one slot behind group A
-  // Block n reads tile n/2 (buffer (n/2) % 2) and the previous block's tile; the
-  // pattern of buffers repeats every 4 blocks, written out so that every buffer is a
-  // known object in each phase.
-  for (int n = 0; n <= NB; n += 4) {
-    m_phase(n, lds0, lds1, lds1);
-    if (n == NB) break;
-    v_phase(n, lds0, lds1);
-    m_phase(n + 1, lds0, lds0, lds1);
-    if (n + 1 == NB) break;
-    v_phase(n + 1, lds0, lds1);
-    m_phase(n + 2, lds1, lds0, lds0);
-    if (n + 2 == NB) break;
-    v_phase(n + 2, lds1, lds0);
-    m_phase(n + 3, lds1, lds1, lds0);
-    if (n + 3 == NB) break;
-    v_phase(n + 3, lds1, lds0);
+  for (int t = 0; t < ntiles; ++t) {
+    if (kStages == 3 && t + 1 < ntiles) stage_tile(t + 1, buf(t + 1));
+    m_phase(2 * t);
+    if (kStages == 2) {
+      lds_barrier();
+      if (t + 1 < ntiles) stage_tile(t + 1, buf(t + 1));
+    }
+    v_phase(2 * t);
+    m_phase(2 * t + 1);
+    v_phase(2 * t + 1);
+    wait_vmem();
+    lds_barrier();
   }
-  if (group == 0) __syncthreads();  // same number of barriers in both groups
+  m_phase(NB);
 
   // Scale and write: acc[mb][r] = dX[i][d] * 2^14 / (scale g) for
   // i = ib0 + 8 (r/4) + 4 hh + (r%4), d = 32 mb + l32.
