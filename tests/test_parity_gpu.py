@@ -186,3 +186,26 @@ def test_autograd_function():
     fo, dxo = oracle_fwd_bwd(x_t.cpu(), x_s.detach().cpu(), True, g=2.5)
     assert float(loss.item()) == pytest.approx(fo["loss"], rel=1e-5)
     assert rel_l2(np64(x_s.grad), dxo) <= GRAD_RL2[torch.float32]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+def test_growing_row_maximum(causal, d, dtype):
+    """Token norms that grow along the sequence: every row's maximum logit keeps rising
+    across key blocks by far more than 64 in log2 units, so the forward's fast update
+    (which keeps a row's exponent bias) must keep handing blocks to its exact rescaling
+    path.  Rows are alpha_j u + noise with alpha_j rising from 1 to 40."""
+    n = 700
+    banner(f"growing maxima N={n} d={d} causal={causal} {dtype}")
+    gen = torch.Generator().manual_seed(7)
+    u = torch.randn(d, generator=gen, dtype=torch.float64)
+    u = u / u.norm()
+    alpha = 1.0 + 39.0 * (torch.arange(n, dtype=torch.float64) / (n - 1)) ** 2
+    noise = torch.randn((1, 2, n, d), generator=gen, dtype=torch.float64)
+    x_t = alpha[None, None, :, None] * u + 0.3 * noise
+    x_s = x_t + 0.05 * torch.randn((1, 2, n, d), generator=gen, dtype=torch.float64)
+    x_t, x_s = x_t.to(dtype), x_s.to(dtype)
+    f, dx = gpu_fwd_bwd(x_t, x_s, causal)
+    fo, dxo = oracle_fwd_bwd(x_t, x_s, causal)
+    assert_parity(f, dx, fo, dxo, dtype, "growing", x_s=x_s, scale=oracle.default_scale(d))
