@@ -133,11 +133,13 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) {
 }
 
 // LDS copy of 16 bytes per lane (lane l writes lds_base + 16 l), issued as inline assembly
-// so that the compiler does not track it.  The backward reads stage buffers chosen at run
-// time; tracking the copies, the compiler would wait for all of them before any LDS read
-// it cannot prove disjoint from a copy target.  Completion is awaited explicitly with
-// wait_vmem().  The s_nop covers the one wait state needed between writing M0 and the
-// copy.
+// so that the compiler does not track it.  Tracking the copies, the compiler waits for all
+// of them before any LDS read it cannot prove disjoint from a copy target (the backward
+// picks its stage buffers at run time), and it stops counting LDS reads individually:
+// every read then waits for all earlier ones (lgkmcnt(0)), which breaks the read-ahead of
+// the matrix pipelines.  Completion is awaited explicitly with wait_vmem() before the
+// barrier that publishes a tile.  The s_nop covers the one wait state needed between
+// writing M0 and the copy.
 __device__ __forceinline__ void lds_copy16(const void* g, uint32_t lds_base) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds_base) : "memory");
 }
@@ -194,7 +196,7 @@ __device__ __forceinline__ void dma_tile(const char* base, int64_t sn_bytes, int
     const int c = (t % G::kCPR) ^ G::swz(r);
     const int j = min(j0 + r, N - 1);
     const char* g = base + (int64_t)j * sn_bytes + c * 16;
-    __builtin_amdgcn_global_load_lds(g, (LDS_AS void*)(lds + slot0 * 16), 16, 0, 0);
+    lds_copy16(g, lds_addr(lds + slot0 * 16));
   }
 }
 
@@ -397,8 +399,7 @@ void relkl_fwd_kernel(const FwdArgs a) {
   constexpr int KS = D / 16;  // 16-deep steps over d
   constexpr int kStage = 2 * G::kTileBytes;
 
-  // two stage buffers as distinct objects, so the compiler can tell the DMA into one
-  // from the reads of the other and does not wait for the DMA before those reads
+  // two stage buffers: a step reads one while its copies fill the other
   __shared__ __attribute__((aligned(1024))) char lds0[kStage];
   __shared__ __attribute__((aligned(1024))) char lds1[kStage];
   __shared__ double red[kWaves];
@@ -473,7 +474,10 @@ void relkl_fwd_kernel(const FwdArgs a) {
       if (jb0 >= N) break;
       if (CAUSAL && jb0 > ib0 + 31) break;  // above every row of the wave
       f32x16 st, ss;
+      // the LDS-bound matrix part issues ahead of the partner wave's vector work
+      __builtin_amdgcn_s_setprio(1);
       score_pipeline<In, D>(tile_t, tile_s, fbase, jb, qt, qs, st, ss);
+      __builtin_amdgcn_s_setprio(0);
       const bool need_mask = (CAUSAL && jb0 + 31 > ib0) || (jb0 + 32 > N);
       if (need_mask)
         online_update<true, CAUSAL>(st, ss, jb0, row, hh, N, c2, b_t, l_t, acc_a, b_s, l_s);
@@ -838,6 +842,7 @@ void relkl_bwd_kernel(const BwdArgs a) {
   // of row N-1 and their scores are never used; M(NB) computes unused scores from a buffer
   // no copy is writing into.
   auto m_phase = [&](int n) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(1);  // matrix phases issue ahead of a partner's vector work
     const char* sb = buf(n >> 1);
     const char* gtile = (n == 0 ? buf(kStages - 1) : buf((n - 1) >> 1)) + G::kTileBytes;
     const int jbg = 32 * ((n - 1) & 1), jbs = n & 1;
@@ -846,6 +851,7 @@ void relkl_bwd_kernel(const BwdArgs a) {
 
   // V(n): W(n) from the scores of block n and the column statistics staged with its tile.
   auto v_phase = [&](int n) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(0);
     const char* sb = buf(n >> 1);
     const int jb0 = block_j0(n);
     if (jb0 < N) {
