@@ -26,7 +26,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["Workload", "Relation", "WORKLOADS", "make_inputs", "rope", "default_scale"]
+__all__ = ["Workload", "Relation", "RopeRelation", "WORKLOADS", "make_inputs",
+           "make_rope_inputs", "rope", "rope_tables", "default_scale"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -57,6 +58,19 @@ class Relation:
     head_map: Optional[list] = None
 
 
+@dataclasses.dataclass
+class RopeRelation:
+    """Inputs of the RoPE-fused call: activations before the rotation and the fp32
+    [N, d/2] cos / sin tables of each side (None: that side is not rotated)."""
+    name: str
+    x_t: torch.Tensor    # [B, H_in, N, d], before RoPE
+    x_s: torch.Tensor
+    cos_t: Optional[torch.Tensor] = None
+    sin_t: Optional[torch.Tensor] = None
+    cos_s: Optional[torch.Tensor] = None
+    sin_s: Optional[torch.Tensor] = None
+
+
 WORKLOADS = {
     # Q/Q only, fp32, student = teacher + 0.1 N(0,1), no RoPE.
     "tiny": Workload("tiny", 1, 1, 1, 256, 64, "fp32", (True,), ("qq",), None, None, 0.1),
@@ -80,15 +94,21 @@ def default_scale(d: int) -> float:
     return float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32).item())
 
 
+def rope_tables(n: int, d: int, base: float, pos_div: float, dtype=torch.float32):
+    """Cosine and sine tables [n, d/2] of the RoPE recipe: token p at position p / pos_div,
+    frequency k at base^(-2k/d); angles and cos/sin in float64, then cast to ``dtype``."""
+    k = torch.arange(d // 2, dtype=torch.float64)
+    inv_freq = base ** (-2.0 * k / d)
+    pos = torch.arange(n, dtype=torch.float64) / pos_div
+    ang = pos[:, None] * inv_freq[None, :]
+    return torch.cos(ang).to(dtype), torch.sin(ang).to(dtype)
+
+
 def rope(x: torch.Tensor, base: float, pos_div: float) -> torch.Tensor:
     """Rotate-half RoPE in float64 at positions arange(N) / pos_div; returns float64."""
     n, d = x.shape[-2], x.shape[-1]
     half = d // 2
-    k = torch.arange(half, dtype=torch.float64)
-    inv_freq = base ** (-2.0 * k / d)
-    pos = torch.arange(n, dtype=torch.float64) / pos_div
-    ang = pos[:, None] * inv_freq[None, :]
-    cos, sin = torch.cos(ang), torch.sin(ang)
+    cos, sin = rope_tables(n, d, base, pos_div, dtype=torch.float64)
     x64 = x.to(torch.float64)
     x1, x2 = x64[..., :half], x64[..., half:]
     return torch.cat((x1 * cos - x2 * sin, x2 * cos + x1 * sin), dim=-1)
@@ -141,4 +161,49 @@ def make_inputs(wl: Workload | str, seed: int = 0, *, B: Optional[int] = None,
         else:
             raise ValueError(f"unknown relation {name!r}")
         out.append(Relation(name, x_t.contiguous(), x_s.contiguous()))
+    return out
+
+
+def make_rope_inputs(wl: Workload | str, seed: int = 0, *, B: Optional[int] = None,
+                     Hq: Optional[int] = None, Hkv: Optional[int] = None,
+                     N: Optional[int] = None, relations: Optional[tuple] = None):
+    """The same draws as ``make_inputs``, handed over before the rotation: Q/K relations
+    carry the teacher's and the student's RoPE tables (fp32), V and the tiny workload none.
+    The teacher's and student's Q (and K) are the same pre-RoPE activations."""
+    if isinstance(wl, str):
+        wl = WORKLOADS[wl]
+    b = wl.B if B is None else B
+    hq = wl.Hq if Hq is None else Hq
+    hkv = wl.Hkv if Hkv is None else Hkv
+    n = wl.N if N is None else N
+    d = wl.d
+    dt = wl.torch_dtype
+    rels = wl.relations if relations is None else relations
+    gen = torch.Generator().manual_seed(seed)
+
+    def draw(h):
+        return torch.randn((b, h, n, d), generator=gen, dtype=torch.float32)
+
+    if wl.teacher_rope is None:
+        x = draw(hq)
+        noise = draw(hq)
+        x_t = x.to(dt)
+        x_s = (x.to(torch.float64) + wl.noise * noise.to(torch.float64)).to(dt)
+        return [r for r in [RopeRelation("qq", x_t.contiguous(), x_s.contiguous())]
+                if r.name in rels]
+
+    x_q, x_k, x_v, noise_v = draw(hq), draw(hkv), draw(hkv), draw(hkv)
+    ct, st = rope_tables(n, d, *wl.teacher_rope)
+    cs, ss = rope_tables(n, d, *wl.student_rope)
+    out = []
+    for name in rels:
+        if name in ("qq", "kk"):
+            x = (x_q if name == "qq" else x_k).to(dt).contiguous()
+            out.append(RopeRelation(name, x, x, ct, st, cs, ss))
+        elif name == "vv":
+            x_t = x_v.to(dt)
+            x_s = (x_v.to(torch.float64) + wl.noise * noise_v.to(torch.float64)).to(dt)
+            out.append(RopeRelation(name, x_t.contiguous(), x_s.contiguous()))
+        else:
+            raise ValueError(f"unknown relation {name!r}")
     return out
