@@ -97,7 +97,26 @@ size_t fwd_workspace(const lard_relkl_desc* d) {
 }
 
 ReserveLayout reserve_of(const lard_relkl_desc* d) {
-  return reserve_layout((int64_t)d->B * d->H, d->N, d->d, d->dtype == LARD_BF16);
+  return reserve_layout((int64_t)d->B * d->H, d->N, d->d, d->dtype == LARD_BF16 ? 2 : 0);
+}
+
+// RoPE-fused entry points: rotated copies of both sides, fp16 (bf16 inputs) or fp32.
+ReserveLayout rope_reserve_of(const lard_relkl_desc* d) {
+  return reserve_layout((int64_t)d->B * d->H, d->N, d->d, d->dtype == LARD_BF16 ? 2 : 4);
+}
+
+// Tables of one side: both null (not rotated) or both set, 16-byte aligned.
+lard_status check_tables(const float* c, const float* s) {
+  if ((c == nullptr) != (s == nullptr)) return LARD_ERR_INVALID_ARGUMENT;
+  if (c && (!aligned(c, 16) || !aligned(s, 16))) return LARD_ERR_INVALID_ARGUMENT;
+  return LARD_OK;
+}
+
+lard_status check_rope(const lard_rope_desc* r) {
+  if (!r) return LARD_ERR_INVALID_ARGUMENT;
+  const lard_status s = check_tables(r->cos_teacher, r->sin_teacher);
+  if (s != LARD_OK) return s;
+  return check_tables(r->cos_student, r->sin_student);
 }
 
 size_t bwd_workspace(const lard_relkl_desc* d) {
@@ -228,6 +247,143 @@ lard_status lard_relkl_bwd(const lard_relkl_desc* desc, const void* x_teacher,
   fill_map(a.map, desc);
   const bool out_f32 = grad->dtype == LARD_FP32;
   int e = launch_bwd(a, desc->dtype == LARD_BF16, desc->d, desc->causal == 1, out_f32, stream);
+  if (e != 0) return LARD_ERR_HIP;
+  if (a.splits > 1) {
+    ReduceArgs r;
+    memset(&r, 0, sizeof(r));
+    r.partial = a.partial;
+    r.dx = dx_student;
+    r.g_sb = a.g_sb; r.g_sh = a.g_sh; r.g_sn = a.g_sn;
+    r.B = a.B; r.H = a.H; r.N = a.N; r.d = desc->d;
+    r.rows_pad = a.row_tiles * kBRB;
+    r.splits = a.splits;
+    r.map = a.map;
+    e = launch_splitk_reduce(r, out_f32, stream);
+    if (e != 0) return LARD_ERR_HIP;
+  }
+  return LARD_OK;
+}
+
+size_t lard_relkl_rope_reserve_size(const lard_relkl_desc* desc, lard_status* status) {
+  const lard_status s = check_desc(desc);
+  if (status) *status = s;
+  if (s != LARD_OK) return 0;
+  return rope_reserve_of(desc).total;
+}
+
+lard_status lard_relkl_rope_fwd(const lard_relkl_desc* desc, const lard_rope_desc* rope,
+                                const void* x_teacher, const void* x_student,
+                                float* lse_teacher, float* lse_student, float* row_kl,
+                                float* loss, void* reserve, size_t reserve_bytes,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  lard_status s = check_desc(desc);
+  if (s != LARD_OK) return s;
+  s = check_rope(rope);
+  if (s != LARD_OK) return s;
+  if (!x_teacher || !x_student || !lse_teacher || !lse_student || !loss || !workspace ||
+      !reserve)
+    return LARD_ERR_INVALID_ARGUMENT;
+  if (!aligned(x_teacher, 16) || !aligned(x_student, 16) || !aligned(workspace, 8) ||
+      !aligned(reserve, 256) || !aligned(lse_teacher, 4) || !aligned(lse_student, 4) ||
+      !aligned(loss, 4) || (row_kl && !aligned(row_kl, 4)))
+    return LARD_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < fwd_workspace(desc)) return LARD_ERR_WORKSPACE_TOO_SMALL;
+  const ReserveLayout R = rope_reserve_of(desc);
+  if (reserve_bytes < R.total) return LARD_ERR_WORKSPACE_TOO_SMALL;
+  const bool bf16 = desc->dtype == LARD_BF16;
+  char* rb = static_cast<char*>(reserve);
+
+  // 1. rotated copies of both sides into the reserve
+  PrepArgs p;
+  memset(&p, 0, sizeof(p));
+  p.x_t = x_teacher;
+  p.x_s = x_student;
+  p.t_sb = desc->t_stride_b; p.t_sh = desc->t_stride_h; p.t_sn = desc->t_stride_n;
+  p.s_sb = desc->s_stride_b; p.s_sh = desc->s_stride_h; p.s_sn = desc->s_stride_n;
+  p.B = desc->B; p.H = desc->H; p.N = desc->N;
+  p.cos_t = rope->cos_teacher; p.sin_t = rope->sin_teacher;
+  p.cos_s = rope->cos_student; p.sin_s = rope->sin_student;
+  p.c_t = rb + R.x16_t;
+  p.c_s = rb + R.x16_s;
+  fill_map(p.map, desc);
+  int e = launch_rope_prep(p, bf16, desc->d, stream);
+  if (e != 0) return LARD_ERR_HIP;
+
+  // 2. the forward on the copies: dense [unit][N][d], read through the identity map
+  FwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.x_t = rb + R.x16_t;
+  a.x_s = rb + R.x16_s;
+  const int64_t sn = desc->d, sh = (int64_t)desc->N * desc->d, sb = (int64_t)desc->H * sh;
+  a.t_sb = sb; a.t_sh = sh; a.t_sn = sn;
+  a.s_sb = sb; a.s_sh = sh; a.s_sn = sn;
+  a.B = desc->B; a.H = desc->H; a.N = desc->N;
+  a.row_tiles = row_tiles_of(desc);
+  a.scale = desc->scale;
+  a.c2 = desc->scale * 1.4426950408889634f;
+  a.lse_t = lse_teacher;
+  a.lse_s = lse_student;
+  a.row_kl = row_kl;
+  a.partial = static_cast<double*>(workspace);
+  a.npad = (int32_t)R.npad;
+  a.r_t = reinterpret_cast<float*>(rb + R.r_t);
+  a.r_s = reinterpret_cast<float*>(rb + R.r_s);
+  for (int h = 0; h < LARD_MAX_HEADS; ++h) a.map.head_map[h] = h < desc->H ? h : 0;
+  e = launch_fwd(a, bf16, desc->d, desc->causal == 1, loss, stream, /*f16_copies=*/bf16);
+  return e == 0 ? LARD_OK : LARD_ERR_HIP;
+}
+
+lard_status lard_relkl_rope_bwd(const lard_relkl_desc* desc, const lard_rope_desc* rope,
+                                const void* reserve, size_t reserve_bytes,
+                                const float* grad_loss, const lard_grad_desc* grad,
+                                void* dx_student, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  lard_status s = check_desc(desc);
+  if (s != LARD_OK) return s;
+  s = check_rope(rope);
+  if (s != LARD_OK) return s;
+  if (!grad || !reserve || !grad_loss || !dx_student) return LARD_ERR_INVALID_ARGUMENT;
+  if (grad->dtype != LARD_FP32 && grad->dtype != LARD_BF16) return LARD_ERR_INVALID_ARGUMENT;
+  if (grad->dtype == LARD_BF16 && desc->dtype != LARD_BF16) return LARD_ERR_UNSUPPORTED;
+  s = check_strides(grad->dtype, grad->stride_b, grad->stride_h, grad->stride_n);
+  if (s != LARD_OK) return s;
+  if (desc->N > 1 && grad->stride_n < desc->d) return LARD_ERR_INVALID_ARGUMENT;
+  if (!aligned(dx_student, 16) || !aligned(reserve, 256) || !aligned(grad_loss, 4))
+    return LARD_ERR_INVALID_ARGUMENT;
+  const ReserveLayout R = rope_reserve_of(desc);
+  if (reserve_bytes < R.total) return LARD_ERR_WORKSPACE_TOO_SMALL;
+  const size_t need = bwd_workspace(desc);
+  if (need > 0 && (!workspace || !aligned(workspace, 16))) return LARD_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < need) return LARD_ERR_WORKSPACE_TOO_SMALL;
+  const bool bf16 = desc->dtype == LARD_BF16;
+  const char* rb = static_cast<const char*>(reserve);
+
+  BwdArgs a;
+  memset(&a, 0, sizeof(a));
+  // operands: the rotated copies (fp16 through x16_*, fp32 through x_* read densely)
+  a.x_t = rb + R.x16_t;
+  a.x_s = rb + R.x16_s;
+  a.x_unit_dense = 1;
+  a.g_sb = grad->stride_b; a.g_sh = grad->stride_h; a.g_sn = grad->stride_n;
+  a.B = desc->B; a.H = desc->H; a.N = desc->N;
+  a.row_tiles = bwd_row_tiles_of(desc);
+  a.key_tiles = key_tiles_of(desc);
+  a.splits = choose_splits(desc);
+  a.scale = desc->scale;
+  a.c2 = desc->scale * 1.4426950408889634f;
+  a.npad = (int32_t)R.npad;
+  a.x16_t = bf16 ? reinterpret_cast<const uint16_t*>(rb + R.x16_t) : nullptr;
+  a.x16_s = bf16 ? reinterpret_cast<const uint16_t*>(rb + R.x16_s) : nullptr;
+  a.r_t = reinterpret_cast<const float*>(rb + R.r_t);
+  a.r_s = reinterpret_cast<const float*>(rb + R.r_s);
+  a.grad_loss = grad_loss;
+  a.rope_cos = rope->cos_student;
+  a.rope_sin = rope->sin_student;
+  a.dx = dx_student;
+  a.partial = static_cast<float*>(workspace);
+  fill_map(a.map, desc);  // output placement only: operands are read per unit
+  const bool out_f32 = grad->dtype == LARD_FP32;
+  int e = launch_bwd(a, bf16, desc->d, desc->causal == 1, out_f32, stream);
   if (e != 0) return LARD_ERR_HIP;
   if (a.splits > 1) {
     ReduceArgs r;

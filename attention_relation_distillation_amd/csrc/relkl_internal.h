@@ -21,9 +21,10 @@ constexpr int kBC = 64;                   // rows of one key tile staged in LDS
 inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
 // Phase-1 state the forward leaves for the backward ("reserve"), per relation head unit:
-//  * bf16 inputs only: IEEE fp16 copies of the teacher and student rows, dense
-//    [units][N][d] each (the backward's operands; bf16 -> fp16 is exact for
-//    2^-17 <= |x| < 65504);
+//  * copies of the teacher and student rows, dense [units][N][d] each: IEEE fp16 copies
+//    of bf16 inputs (the backward's operands; bf16 -> fp16 is exact for
+//    2^-17 <= |x| < 65504), and for the RoPE-fused entry points the rotated rows, in fp16
+//    (bf16 inputs) or fp32 (fp32 inputs); none for fp32 inputs otherwise;
 //  * row statistics in log2 units, r = log2(sum_j 2^(S_ij c2 + b_i)) - b_i - 14, dense
 //    [units][Npad] with Npad = N rounded up to kBC, for teacher and student, so that
 //    R(i, j) * 2^14 = exp2(S_ij c2 - r_i).
@@ -32,10 +33,11 @@ struct ReserveLayout {
   int64_t npad;
 };
 
-inline ReserveLayout reserve_layout(int64_t units, int64_t N, int64_t d, bool fp16_copies) {
+// copy_bytes: bytes per element of the row copies (0: none, 2: fp16, 4: fp32).
+inline ReserveLayout reserve_layout(int64_t units, int64_t N, int64_t d, int copy_bytes) {
   ReserveLayout L;
   L.npad = round_up(N, kBC);
-  const size_t copy = fp16_copies ? (size_t)round_up(units * N * d * 2, 256) : 0;
+  const size_t copy = (size_t)round_up(units * N * d * copy_bytes, 256);
   const size_t stats = (size_t)round_up(units * L.npad * 4, 256);
   L.x16_t = 0;
   L.x16_s = copy;
@@ -88,8 +90,27 @@ struct BwdArgs {
   const float* r_t;
   const float* r_s;
   const float* grad_loss;
+  const float* rope_cos;  // student RoPE tables [N][d/2] (fused entry points) or null:
+  const float* rope_sin;  // the gradient is rotated back before it is written
+  int32_t x_unit_dense;   // fp32 path: x_t / x_s are dense [unit][N][d] copies
   void* dx;            // final gradient (splits == 1)
   float* partial;      // [splits][B*H][row_tiles*kBR][d] (splits > 1)
+  UnitMap map;
+};
+
+// Rotation of the inputs into the reserve for the RoPE-fused entry points.
+struct PrepArgs {
+  const void* x_t;
+  const void* x_s;
+  int64_t t_sb, t_sh, t_sn;
+  int64_t s_sb, s_sh, s_sn;
+  int32_t B, H, N;
+  const float* cos_t;  // [N][d/2] tables, or null (side not rotated)
+  const float* sin_t;
+  const float* cos_s;
+  const float* sin_s;
+  void* c_t;           // reserve copies, dense [units][N][d]
+  void* c_s;
   UnitMap map;
 };
 
@@ -105,10 +126,12 @@ struct ReduceArgs {
 
 // Each returns a hipError_t value (0 on success).  `in_bf16`: input dtype; `out_f32`:
 // gradient dtype (fp32 or the input dtype).
+// f16_copies: the inputs are the reserve's fp16 copies (RoPE-fused path, bf16 inputs).
 int launch_fwd(const FwdArgs& a, bool in_bf16, int d, bool causal, float* loss,
-               void* stream);
+               void* stream, bool f16_copies = false);
 int launch_bwd(const BwdArgs& a, bool in_bf16, int d, bool causal, bool out_f32,
                void* stream);
 int launch_splitk_reduce(const ReduceArgs& a, bool out_f32, void* stream);
+int launch_rope_prep(const PrepArgs& a, bool in_bf16, int d, void* stream);
 
 }  // namespace lard

@@ -38,6 +38,7 @@
 #include <stdlib.h>
 
 #include <array>
+#include <type_traits>
 #include <utility>
 
 #include "relkl_internal.h"
@@ -46,6 +47,7 @@ namespace lard {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
@@ -442,8 +444,9 @@ void relkl_fwd_kernel(const FwdArgs a) {
       qs[ks] = frag_t{};
     }
   }
-  if constexpr (In::kES == 2) {
-    // reserve: fp16 copies of this lane's part of its row
+  if constexpr (std::is_same_v<In, Bf16In>) {
+    // reserve: fp16 copies of this lane's part of its row (inputs that are already fp16
+    // copies, made by rope_prep_kernel, are in the reserve)
     if (row < N) {
       const int64_t o = ((int64_t)unit * N + row) * D + 8 * hh;
 #pragma unroll
@@ -747,6 +750,12 @@ void relkl_bwd_kernel(const BwdArgs a) {
     xs = a.x16_s + (int64_t)unit * N * D;
     tsn = D;
     ssn = D;
+  } else if (a.x_unit_dense) {
+    // fp32 copies in the reserve (rotated inputs), dense [unit][N][D]
+    xt = reinterpret_cast<const elem_t*>(a.x_t) + (int64_t)unit * N * D;
+    xs = reinterpret_cast<const elem_t*>(a.x_s) + (int64_t)unit * N * D;
+    tsn = D;
+    ssn = D;
   } else {
     xt = reinterpret_cast<const elem_t*>(a.x_t) + b * a.t_sb + hin * a.t_sh;
     xs = reinterpret_cast<const elem_t*>(a.x_s) + b * a.s_sb + hin * a.s_sh;
@@ -904,6 +913,25 @@ void relkl_bwd_kernel(const BwdArgs a) {
   // Scale and write: acc[mb][r] = dX[i][d] * 2^14 / (scale g) for
   // i = ib0 + 8 (r/4) + 4 hh + (r%4), d = 32 mb + l32.
   const float factor = a.scale * a.grad_loss[0] * (1.0f / 16384.0f);
+  if (a.rope_cos != nullptr) {
+    // Gradient before the student's rotation: the transposed rotate-half rotation maps
+    // (g_k, g_{k+D/2}) to (g_k c + g_{k+D/2} s, g_{k+D/2} c - g_k s) with the cos / sin of
+    // row i, frequency k.  Dimensions k and k + D/2 sit in blocks mb and mb + MB/2 of
+    // the same lane.
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = ib0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+      if (i >= N) continue;
+#pragma unroll
+      for (int mb = 0; mb < MB / 2; ++mb) {
+        const int64_t t = (int64_t)i * (D / 2) + 32 * mb + l32;
+        const float c = a.rope_cos[t], sn = a.rope_sin[t];
+        const float g1 = acc[mb][r], g2 = acc[mb + MB / 2][r];
+        acc[mb][r] = fmaf(g1, c, g2 * sn);
+        acc[mb + MB / 2][r] = fmaf(g2, c, -(g1 * sn));
+      }
+    }
+  }
   if (a.splits == 1) {
     const bool full = ib0 + 32 <= N;
     char* gbase = reinterpret_cast<char*>(a.dx) + (b * a.g_sb + hin * a.g_sh) * (OUT_F32 ? 4 : 2);
@@ -962,6 +990,81 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const ReduceArgs a) 
   }
 }
 
+// ------------------------------------------------------------------ RoPE prep
+// Rotated copies of the teacher and student rows for the RoPE-fused entry points: for
+// token p and frequency k < D/2 (rotate-half pairing of k with k + D/2)
+//   y_k = x_k cos[p][k] - x_{k+D/2} sin[p][k],   y_{k+D/2} = x_{k+D/2} cos[p][k] + x_k sin[p][k]
+// each evaluated in fp32 as one fused multiply-add on a rounded product, then rounded to
+// the input dtype, as the rotation inside the model would leave it: bf16 (nearest even),
+// stored as the exactly equal IEEE fp16 value the matrix cores take, or fp32.  Written
+// into the reserve, dense [unit][N][D]; a side without tables is copied unrotated.  One
+// thread per (side, unit, row, group of 4 frequencies): consecutive threads cover
+// consecutive frequencies of one row, so each half-row is read and written in one run.
+template <bool IN_BF16, int D>
+__global__ __launch_bounds__(256) void rope_prep_kernel(const PrepArgs a) {
+  constexpr int G4 = D / 8;  // groups of 4 frequencies per row
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per_side = (int64_t)a.B * a.H * a.N * G4;
+  if (q >= 2 * per_side) return;
+  const int side = (int)(q / per_side);
+  const int64_t rq = q - side * per_side;
+  const int g = (int)(rq % G4);
+  const int64_t rowlin = rq / G4;
+  const int p = (int)(rowlin % a.N);
+  const int unit = (int)(rowlin / a.N);
+  const int b = unit / a.H, h = unit % a.H;
+  const int hin = a.map.head_map[h];
+  const void* x = side ? a.x_s : a.x_t;
+  const int64_t sb = side ? a.s_sb : a.t_sb, sh = side ? a.s_sh : a.t_sh;
+  const int64_t sn = side ? a.s_sn : a.t_sn;
+  const float* cs = side ? a.cos_s : a.cos_t;
+  const float* sn_tab = side ? a.sin_s : a.sin_t;
+  const int64_t src = b * sb + hin * sh + (int64_t)p * sn + 4 * g;
+  f32x4 x1, x2;
+  if constexpr (IN_BF16) {
+    const uint16_t* xp = reinterpret_cast<const uint16_t*>(x) + src;
+    const u32x2 v1 = *reinterpret_cast<const u32x2*>(xp);
+    const u32x2 v2 = *reinterpret_cast<const u32x2*>(xp + D / 2);
+    x1 = f32x4{__uint_as_float(v1[0] << 16), __uint_as_float(v1[0] & 0xffff0000u),
+               __uint_as_float(v1[1] << 16), __uint_as_float(v1[1] & 0xffff0000u)};
+    x2 = f32x4{__uint_as_float(v2[0] << 16), __uint_as_float(v2[0] & 0xffff0000u),
+               __uint_as_float(v2[1] << 16), __uint_as_float(v2[1] & 0xffff0000u)};
+  } else {
+    const float* xp = reinterpret_cast<const float*>(x) + src;
+    x1 = *reinterpret_cast<const f32x4*>(xp);
+    x2 = *reinterpret_cast<const f32x4*>(xp + D / 2);
+  }
+  f32x4 y1 = x1, y2 = x2;
+  if (cs != nullptr) {
+    const int64_t t = (int64_t)p * (D / 2) + 4 * g;
+    const f32x4 c = *reinterpret_cast<const f32x4*>(cs + t);
+    const f32x4 sv = *reinterpret_cast<const f32x4*>(sn_tab + t);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      y1[e] = fmaf(x1[e], c[e], -(x2[e] * sv[e]));
+      y2[e] = fmaf(x2[e], c[e], x1[e] * sv[e]);
+    }
+  }
+  const int64_t dst = ((int64_t)unit * a.N + p) * D + 4 * g;
+  if constexpr (IN_BF16) {
+    uint16_t* cp = reinterpret_cast<uint16_t*>(side ? a.c_s : a.c_t) + dst;
+    f32x4 r1, r2;  // the bf16 values, then their fp16 bit patterns (exact below 65504)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      r1[e] = __uint_as_float((uint32_t)f32_to_bf16_rne(y1[e]) << 16);
+      r2[e] = __uint_as_float((uint32_t)f32_to_bf16_rne(y2[e]) << 16);
+    }
+    const f16x4 h1 = __builtin_convertvector(r1, f16x4);
+    const f16x4 h2 = __builtin_convertvector(r2, f16x4);
+    *reinterpret_cast<u32x2*>(cp) = __builtin_bit_cast(u32x2, h1);
+    *reinterpret_cast<u32x2*>(cp + D / 2) = __builtin_bit_cast(u32x2, h2);
+  } else {
+    float* cp = reinterpret_cast<float*>(side ? a.c_s : a.c_t) + dst;
+    *reinterpret_cast<f32x4*>(cp) = y1;
+    *reinterpret_cast<f32x4*>(cp + D / 2) = y2;
+  }
+}
+
 // ------------------------------------------------------------------ launchers
 static bool fault_injected() {
   const char* v = getenv("LARD_FAULT_INJECT");
@@ -978,9 +1081,16 @@ static int launch_fwd_t(const FwdArgs& a, float* loss, hipStream_t s) {
   return (int)hipGetLastError();
 }
 
-int launch_fwd(const FwdArgs& a, bool in_bf16, int d, bool causal, float* loss, void* stream) {
+int launch_fwd(const FwdArgs& a, bool in_bf16, int d, bool causal, float* loss, void* stream,
+               bool f16_copies) {
   if (fault_injected()) return (int)hipErrorLaunchFailure;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (in_bf16 && f16_copies) {
+    if (d == 128) return causal ? launch_fwd_t<F16Op, 128, true>(a, loss, s)
+                                : launch_fwd_t<F16Op, 128, false>(a, loss, s);
+    return causal ? launch_fwd_t<F16Op, 64, true>(a, loss, s)
+                  : launch_fwd_t<F16Op, 64, false>(a, loss, s);
+  }
   if (in_bf16) {
     if (d == 128) return causal ? launch_fwd_t<Bf16In, 128, true>(a, loss, s)
                                 : launch_fwd_t<Bf16In, 128, false>(a, loss, s);
@@ -1017,6 +1127,21 @@ int launch_bwd(const BwdArgs& a, bool in_bf16, int d, bool causal, bool out_f32,
   // fp32 inputs always give an fp32 gradient
   return d == 128 ? launch_bwd_d<F32In, 128>(a, causal, true, s)
                   : launch_bwd_d<F32In, 64>(a, causal, true, s);
+}
+
+int launch_rope_prep(const PrepArgs& a, bool in_bf16, int d, void* stream) {
+  if (fault_injected()) return (int)hipErrorLaunchFailure;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int64_t total = 2LL * a.B * a.H * a.N * (d / 8);
+  const int grid = (int)((total + 255) / 256);
+  if (in_bf16) {
+    if (d == 128) hipLaunchKernelGGL((rope_prep_kernel<true, 128>), dim3(grid), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((rope_prep_kernel<true, 64>), dim3(grid), dim3(256), 0, s, a);
+  } else {
+    if (d == 128) hipLaunchKernelGGL((rope_prep_kernel<false, 128>), dim3(grid), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((rope_prep_kernel<false, 64>), dim3(grid), dim3(256), 0, s, a);
+  }
+  return (int)hipGetLastError();
 }
 
 int launch_splitk_reduce(const ReduceArgs& a, bool out_f32, void* stream) {

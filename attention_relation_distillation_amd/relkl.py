@@ -18,7 +18,8 @@ from typing import Optional, Sequence
 import torch
 
 __all__ = ["LardError", "library_path", "load_library", "relkl_fwd", "relkl_bwd",
-           "relation_kl", "workspace_size", "reserve_size", "LARD_MAX_HEADS"]
+           "relation_kl", "workspace_size", "reserve_size", "rope_reserve_size",
+           "rope_relkl_fwd", "rope_relkl_bwd", "rope_relation_kl", "LARD_MAX_HEADS"]
 
 LARD_FP32 = 0
 LARD_BF16 = 1
@@ -47,6 +48,13 @@ class _Desc(ctypes.Structure):
         ("H", ctypes.c_int32), ("causal", ctypes.c_int32),
         ("head_map", ctypes.POINTER(ctypes.c_int32)),
         ("scale", ctypes.c_float),
+    ]
+
+
+class _RopeDesc(ctypes.Structure):
+    _fields_ = [
+        ("cos_teacher", ctypes.c_void_p), ("sin_teacher", ctypes.c_void_p),
+        ("cos_student", ctypes.c_void_p), ("sin_student", ctypes.c_void_p),
     ]
 
 
@@ -87,6 +95,15 @@ def load_library():
     lib.lard_relkl_bwd.restype = ctypes.c_int
     lib.lard_relkl_bwd.argtypes = [ctypes.POINTER(_Desc), vp, vp, vp, sz, vp,
                                    ctypes.POINTER(_GradDesc), vp, vp, sz, vp]
+    lib.lard_relkl_rope_reserve_size.restype = sz
+    lib.lard_relkl_rope_reserve_size.argtypes = [ctypes.POINTER(_Desc),
+                                                 ctypes.POINTER(ctypes.c_int)]
+    lib.lard_relkl_rope_fwd.restype = ctypes.c_int
+    lib.lard_relkl_rope_fwd.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(_RopeDesc), vp,
+                                        vp, vp, vp, vp, vp, vp, sz, vp, sz, vp]
+    lib.lard_relkl_rope_bwd.restype = ctypes.c_int
+    lib.lard_relkl_rope_bwd.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(_RopeDesc), vp,
+                                        sz, vp, ctypes.POINTER(_GradDesc), vp, vp, sz, vp]
     lib.lard_status_string.restype = ctypes.c_char_p
     lib.lard_status_string.argtypes = [ctypes.c_int]
     lib.lard_version.restype = ctypes.c_int
@@ -258,3 +275,128 @@ def relation_kl(x_t: torch.Tensor, x_s: torch.Tensor, *, causal: bool = True,
     tensor).  Differentiable with respect to x_s; the teacher is treated as frozen."""
     return _RelationKL.apply(x_t.detach(), x_s, causal, scale,
                              None if head_map is None else tuple(int(v) for v in head_map))
+
+
+# ------------------------------------------------------------------ RoPE-fused entry points
+def _rope_desc(x: torch.Tensor, tables) -> _RopeDesc:
+    """tables: (cos_t, sin_t, cos_s, sin_s), each an fp32 [N, d/2] device tensor or None."""
+    n, d = x.shape[2], x.shape[3]
+    ptrs = []
+    for t in tables:
+        if t is None:
+            ptrs.append(None)
+            continue
+        if (t.dtype != torch.float32 or tuple(t.shape) != (n, d // 2) or not t.is_contiguous()
+                or t.device != x.device):
+            raise LardError(1, f"RoPE tables must be contiguous fp32 [{n}, {d // 2}] tensors "
+                               "on the inputs' device")
+        ptrs.append(t.data_ptr())
+    return _RopeDesc(*ptrs)
+
+
+def rope_reserve_size(x_t, x_s, *, causal=True, scale=None, head_map=None) -> int:
+    lib = load_library()
+    desc, _keep = _make_desc(x_t, x_s, causal, scale, head_map)
+    st = ctypes.c_int(0)
+    n = lib.lard_relkl_rope_reserve_size(ctypes.byref(desc), ctypes.byref(st))
+    _check(st.value)
+    return int(n)
+
+
+def rope_relkl_fwd(x_t: torch.Tensor, x_s: torch.Tensor, cos_t=None, sin_t=None, cos_s=None,
+                   sin_s=None, *, causal: bool = True, scale: Optional[float] = None,
+                   head_map: Optional[Sequence[int]] = None, want_row_kl: bool = False,
+                   stream=None):
+    """RoPE-fused forward on pre-rotation inputs; returns the same dict as relkl_fwd (its
+    reserve holds the rotated rows and is what rope_relkl_bwd needs)."""
+    lib = load_library()
+    desc, keep = _make_desc(x_t, x_s, causal, scale, head_map)
+    rdesc = _rope_desc(x_t, (cos_t, sin_t, cos_s, sin_s))
+    _require_gpu(x_t)
+    b, n = desc.B, desc.N
+    dev = x_t.device
+    lse_t = torch.empty((b, desc.H, n), dtype=torch.float32, device=dev)
+    lse_s = torch.empty((b, desc.H, n), dtype=torch.float32, device=dev)
+    row_kl = torch.empty((b, desc.H, n), dtype=torch.float32, device=dev) if want_row_kl else None
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    st = ctypes.c_int(0)
+    ws_bytes = lib.lard_relkl_workspace_size(ctypes.byref(desc), 0, ctypes.byref(st))
+    _check(st.value)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    rs_bytes = lib.lard_relkl_rope_reserve_size(ctypes.byref(desc), ctypes.byref(st))
+    _check(st.value)
+    reserve = torch.empty(max(rs_bytes, 256), dtype=torch.uint8, device=dev)
+    _check(lib.lard_relkl_rope_fwd(ctypes.byref(desc), ctypes.byref(rdesc), x_t.data_ptr(),
+                                   x_s.data_ptr(), lse_t.data_ptr(), lse_s.data_ptr(),
+                                   row_kl.data_ptr() if row_kl is not None else None,
+                                   loss.data_ptr(), reserve.data_ptr(), reserve.numel(),
+                                   ws.data_ptr(), ws.numel(), _stream_handle(dev, stream)))
+    del keep
+    return {"loss": loss, "lse_t": lse_t, "lse_s": lse_s, "row_kl": row_kl, "reserve": reserve}
+
+
+def rope_relkl_bwd(x_s: torch.Tensor, reserve: torch.Tensor, grad_loss: torch.Tensor,
+                   cos_t=None, sin_t=None, cos_s=None, sin_s=None, *, causal: bool = True,
+                   scale: Optional[float] = None, head_map: Optional[Sequence[int]] = None,
+                   dx: Optional[torch.Tensor] = None, dx_dtype: Optional[torch.dtype] = None,
+                   stream=None) -> torch.Tensor:
+    """RoPE-fused backward: gradient of grad_loss * loss with respect to the student's
+    pre-rotation input x_s (x_s gives the shape, dtype and device; its values are not
+    read: the rotated operands come from the reserve)."""
+    lib = load_library()
+    desc, keep = _make_desc(x_s, x_s, causal, scale, head_map)
+    rdesc = _rope_desc(x_s, (cos_t, sin_t, cos_s, sin_s))
+    _require_gpu(x_s)
+    dev = x_s.device
+    if reserve.dtype != torch.uint8 or not reserve.is_contiguous() or reserve.device != dev:
+        raise LardError(1, "reserve must be the uint8 device buffer returned by rope_relkl_fwd")
+    if (grad_loss.dtype != torch.float32 or grad_loss.numel() != 1 or grad_loss.device != dev):
+        raise LardError(1, "grad_loss must be a one-element fp32 tensor on the inputs' device")
+    grad_loss = grad_loss.contiguous()
+    if dx is None:
+        out_dtype = x_s.dtype if dx_dtype is None else dx_dtype
+        subset = head_map is not None and sorted(int(v) for v in head_map) != list(range(desc.H_in))
+        dx = (torch.zeros if subset else torch.empty)(x_s.shape, dtype=out_dtype, device=dev)
+    if dx.shape != x_s.shape or dx.stride(-1) != 1 or dx.device != dev:
+        raise LardError(1, "dx must match x_s in shape, with a contiguous last dimension")
+    gdesc = _GradDesc(dtype=_dtype_code(dx.dtype), reserved=0, stride_b=dx.stride(0),
+                      stride_h=dx.stride(1), stride_n=dx.stride(2))
+    st = ctypes.c_int(0)
+    ws_bytes = lib.lard_relkl_workspace_size(ctypes.byref(desc), 1, ctypes.byref(st))
+    _check(st.value)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    _check(lib.lard_relkl_rope_bwd(ctypes.byref(desc), ctypes.byref(rdesc), reserve.data_ptr(),
+                                   reserve.numel(), grad_loss.data_ptr(), ctypes.byref(gdesc),
+                                   dx.data_ptr(), ws.data_ptr(), ws.numel(),
+                                   _stream_handle(dev, stream)))
+    del keep
+    return dx
+
+
+class _RopeRelationKL(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, x_t, x_s, cos_t, sin_t, cos_s, sin_s, causal, scale, head_map):
+        out = rope_relkl_fwd(x_t, x_s, cos_t, sin_t, cos_s, sin_s, causal=causal, scale=scale,
+                             head_map=head_map)
+        ctx.save_for_backward(x_s, out["reserve"])
+        ctx.tables = (cos_t, sin_t, cos_s, sin_s)
+        ctx.causal, ctx.scale, ctx.head_map = causal, scale, head_map
+        return out["loss"]
+
+    @staticmethod
+    def backward(ctx, grad):
+        x_s, reserve = ctx.saved_tensors
+        g = grad if grad.dtype == torch.float32 else grad.float()
+        dx = rope_relkl_bwd(x_s, reserve, g, *ctx.tables, causal=ctx.causal, scale=ctx.scale,
+                            head_map=ctx.head_map)
+        return None, dx, None, None, None, None, None, None, None
+
+
+def rope_relation_kl(x_t: torch.Tensor, x_s: torch.Tensor, cos_t=None, sin_t=None, cos_s=None,
+                     sin_s=None, *, causal: bool = True, scale: Optional[float] = None,
+                     head_map: Optional[Sequence[int]] = None):
+    """relation_kl with each side's rotate-half RoPE applied inside the operation: x_t and
+    x_s are the activations before the rotation, the tables fp32 [N, d/2] cos / sin per
+    token (None: that side is not rotated).  Differentiable with respect to x_s."""
+    return _RopeRelationKL.apply(x_t.detach(), x_s, cos_t, sin_t, cos_s, sin_s, causal, scale,
+                                 None if head_map is None else tuple(int(v) for v in head_map))

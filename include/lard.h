@@ -150,6 +150,69 @@ lard_status lard_relkl_bwd(const lard_relkl_desc* desc, const void* x_teacher,
                            void* dx_student, void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/*
+ * RoPE-fused entry points.  The pages distil the relations of queries and keys after the
+ * rotary embedding -- the teacher with its native RoPE, the student with a rescaled one --
+ * and send the gradient to the student's Q/K/V projections (verdict page,
+ * pith_extraction.key_machinery; arXiv abstract).  These entry points take the
+ * activations BEFORE the rotation, rotate them inside the operation, and return the
+ * gradient with respect to the student's pre-rotation input.
+ *
+ * The rotation (rotate-half pairing of dimension k with k + d/2, the reading taken where
+ * the pages leave it open): for token p and k < d/2,
+ *     X[p, k]       = Xpre[p, k] cos[p][k] - Xpre[p, k + d/2] sin[p][k]
+ *     X[p, k + d/2] = Xpre[p, k + d/2] cos[p][k] + Xpre[p, k] sin[p][k]
+ * and the loss is the one of lard_relkl_fwd on (X_teacher, X_student).  The returned
+ * gradient is dXpre = R^T dX_s, i.e. (g_k c + g_{k+d/2} s, g_{k+d/2} c - g_k s).
+ *
+ * Tables: device fp32, dense [N][d/2] (row p holds the cos / sin of token p's angles;
+ * the caller's recipe -- base, position interpolation, NTK base -- lives entirely in
+ * them), 16-byte aligned.  Each side's pair is either both non-NULL or both NULL (that
+ * side is not rotated, e.g. the V relation).  Every relation head uses the same tables.
+ *
+ * The reserve holds the rotated rows of both sides (IEEE fp16, round to nearest even, for
+ * bf16 inputs; fp32 for fp32 inputs) plus the row statistics; size from
+ * lard_relkl_rope_reserve_size.  Workspaces are those of lard_relkl_workspace_size.  For
+ * bf16 inputs the rotated values must stay below 65504 in magnitude (|x| < 46000 is
+ * enough); the matrix work runs on the fp16 copies, so the loss carries the rounding of
+ * the rotated rows to fp16 (2^-11 relative per element) on top of the plain path's.
+ * Validation, ownership, stream and error conventions are those of the plain entry points.
+ */
+typedef struct lard_rope_desc {
+  const float* cos_teacher;  /* device fp32 [N][d/2] or NULL */
+  const float* sin_teacher;  /* device fp32 [N][d/2] or NULL (NULL iff cos_teacher is) */
+  const float* cos_student;
+  const float* sin_student;
+} lard_rope_desc;
+
+/* Bytes of the reserve the RoPE-fused forward writes: 2 * c * B * H * N * d (c = 2 for
+ * bf16, 4 for fp32 inputs) plus 2 * 4 * B * H * roundup(N, 64), each part rounded up to
+ * 256 bytes.  Returns 0 and sets *status on an invalid descriptor. */
+size_t lard_relkl_rope_reserve_size(const lard_relkl_desc* desc, lard_status* status);
+
+/*
+ * RoPE-fused forward.  x_teacher, x_student: pre-rotation inputs (desc layout and dtype).
+ * Outputs, reserve and workspace as for lard_relkl_fwd (reserve sized by
+ * lard_relkl_rope_reserve_size).
+ */
+lard_status lard_relkl_rope_fwd(const lard_relkl_desc* desc, const lard_rope_desc* rope,
+                                const void* x_teacher, const void* x_student,
+                                float* lse_teacher, float* lse_student, float* row_kl,
+                                float* loss, void* reserve, size_t reserve_bytes,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * RoPE-fused backward: the gradient of g * loss with respect to the student's
+ * PRE-rotation input, written like lard_relkl_bwd's (heads outside head_map untouched).
+ * Needs only the reserve the fused forward wrote (it holds the rotated operands) and the
+ * same `rope` tables (the student's rotate the gradient back).
+ */
+lard_status lard_relkl_rope_bwd(const lard_relkl_desc* desc, const lard_rope_desc* rope,
+                                const void* reserve, size_t reserve_bytes,
+                                const float* grad_loss, const lard_grad_desc* grad,
+                                void* dx_student, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* lard_status_string(lard_status status);
 

@@ -20,9 +20,17 @@ part of the operation:
       X[p, k + d/2] = Xpre[p, k + d/2] cos[p, k] + Xpre[p, k] sin[p, k]
   (the complex product (Xpre[p, k] + i Xpre[p, k + d/2]) e^{i angle}).  A side without
   tables is not rotated (the V relation).
+* The rotated rows are the relation inputs in the activations' own dtype, exactly as when
+  the model applies RoPE itself and hands the result to the plain relation KL: each
+  rotated element is evaluated in fp32 as one fused multiply-add on a rounded product
+  (``x_k cos - (x_{k+d/2} sin)``, ``x_{k+d/2} cos + (x_k sin)``), the precision the
+  kernel evaluates it in, so that both sides round the same value, and then rounded to
+  the input dtype (bf16: to nearest, ties to even).  ``dtype=None`` keeps the exact
+  float64 rotation instead (used by the pins that differentiate through it).
 * The loss is the relation KL of ``oracle.relkl`` on the rotated inputs.
 * The gradient with respect to the student's pre-rotation input is the transposed
-  rotation of the gradient with respect to X_s:
+  rotation of the gradient with respect to X_s (the rounding to the dtype passes the
+  gradient through unchanged, as a dtype cast does under automatic differentiation):
       dXpre[p, k]       = dX[p, k] cos[p, k] + dX[p, k + d/2] sin[p, k]
       dXpre[p, k + d/2] = dX[p, k + d/2] cos[p, k] - dX[p, k] sin[p, k]
 
@@ -36,7 +44,7 @@ import numpy as np
 
 from . import relkl
 
-__all__ = ["rotate", "rotate_back", "forward", "backward"]
+__all__ = ["rotate", "rotate_back", "round_bf16", "rotate_in_dtype", "forward", "backward"]
 
 
 def _tab(t):
@@ -65,17 +73,57 @@ def rotate_back(g, cos, sin) -> np.ndarray:
     return np.concatenate((g1 * cos + g2 * sin, g2 * cos - g1 * sin), axis=-1)
 
 
+def round_bf16(v) -> np.ndarray:
+    """Round to the nearest bf16 value (8 significant bits), ties to even, for values in
+    the normal range: v = m 2^e with 1/2 <= |m| < 1, m rounded to a multiple of 2^-8."""
+    v = np.asarray(v, dtype=np.float64)
+    m, e = np.frexp(v)
+    return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
+
+
+def _f32(v):
+    return np.asarray(v, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def rotate_in_dtype(x, cos, sin, dtype) -> np.ndarray:
+    """The rotated rows as the operation uses them: every element evaluated in fp32 as one
+    fused multiply-add on a rounded product, then rounded to ``dtype`` ("bf16" or "fp32");
+    dtype None gives the exact rotation.  Inputs and tables must hold values of the given
+    dtype and of fp32 respectively (as the device receives them).
+
+    The fused multiply-add is computed in float64 (the fp32 product is exact there) and
+    rounded to fp32; this double rounding can differ from a true fused one only when the
+    float64 result lands on an fp32 halfway point, about once in 2^29 elements."""
+    if dtype is None or (cos is None and sin is None):
+        return rotate(x, cos, sin)
+    x = np.asarray(x, dtype=np.float64)
+    cos, sin = _tab(cos), _tab(sin)
+    h = x.shape[-1] // 2
+    x1, x2 = x[..., :h], x[..., h:]
+    y1 = _f32(x1 * cos - _f32(x2 * sin))
+    y2 = _f32(x2 * cos + _f32(x1 * sin))
+    y = np.concatenate((y1, y2), axis=-1)
+    if dtype == "bf16":
+        return round_bf16(y)
+    if dtype == "fp32":
+        return y
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
 def forward(x_t, x_s, scale: float, causal: bool, cos_t=None, sin_t=None, cos_s=None,
-            sin_s=None, head_map=None, chunk: int | None = None):
-    """Forward on pre-rotation [B, H_in, N, d] inputs; same outputs as ``relkl.forward``."""
-    return relkl.forward(rotate(x_t, cos_t, sin_t), rotate(x_s, cos_s, sin_s), scale, causal,
+            sin_s=None, head_map=None, chunk: int | None = None, dtype=None):
+    """Forward on pre-rotation [B, H_in, N, d] inputs; same outputs as ``relkl.forward``.
+    ``dtype`` ("bf16" / "fp32") rounds the rotated rows as the operation does."""
+    return relkl.forward(rotate_in_dtype(x_t, cos_t, sin_t, dtype),
+                         rotate_in_dtype(x_s, cos_s, sin_s, dtype), scale, causal,
                          head_map=head_map, chunk=chunk)
 
 
 def backward(x_t, x_s, scale: float, causal: bool, g: float = 1.0, cos_t=None, sin_t=None,
-             cos_s=None, sin_s=None, head_map=None, chunk: int | None = None):
+             cos_s=None, sin_s=None, head_map=None, chunk: int | None = None, dtype=None):
     """Gradient of g * loss w.r.t. the student's pre-rotation input, float64 [B, H_in, N, d]
     (heads outside head_map stay zero)."""
-    d_rot = relkl.backward(rotate(x_t, cos_t, sin_t), rotate(x_s, cos_s, sin_s), scale, causal,
+    d_rot = relkl.backward(rotate_in_dtype(x_t, cos_t, sin_t, dtype),
+                           rotate_in_dtype(x_s, cos_s, sin_s, dtype), scale, causal,
                            g, head_map=head_map, chunk=chunk)
     return rotate_back(d_rot, cos_s, sin_s)

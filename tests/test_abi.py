@@ -9,7 +9,7 @@ import pytest
 import torch
 
 from attention_relation_distillation_amd import relkl
-from attention_relation_distillation_amd.relkl import _Desc, _GradDesc
+from attention_relation_distillation_amd.relkl import _Desc, _GradDesc, _RopeDesc
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 OK, INVALID, UNSUPPORTED, WS_SMALL, HIP = 0, 1, 2, 3, 4
@@ -30,7 +30,9 @@ def declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) >= {"lard_relkl_fwd", "lard_relkl_bwd", "lard_relkl_workspace_size",
-                          "lard_relkl_reserve_size", "lard_status_string", "lard_version"}
+                          "lard_relkl_reserve_size", "lard_status_string", "lard_version",
+                          "lard_relkl_rope_reserve_size", "lard_relkl_rope_fwd",
+                          "lard_relkl_rope_bwd"}
     for n in names:
         assert hasattr(lib, n), n
     assert lib.lard_version() >= 10000
@@ -187,3 +189,63 @@ def test_python_layer_refuses_cpu_tensors():
     with pytest.raises(relkl.LardError):
         relkl.relkl_fwd(torch.zeros(1, 1, 8, 64, dtype=torch.float16),
                         torch.zeros(1, 1, 8, 64, dtype=torch.float16))
+
+
+# ------------------------------------------------------------------ RoPE-fused entry points
+def rope_fwd(lib, desc, rope, rs=FAKE, nrs=1 << 30):
+    return lib.lard_relkl_rope_fwd(ctypes.byref(desc), ctypes.byref(rope) if rope else None,
+                                   FAKE, FAKE, FAKE, FAKE, None, FAKE, rs, nrs, FAKE, 1 << 20,
+                                   None)
+
+
+def rope_bwd(lib, desc, rope, rs=FAKE, nrs=1 << 30):
+    g = _GradDesc(dtype=1, reserved=0, stride_b=4 * 100 * 128, stride_h=100 * 128, stride_n=128)
+    return lib.lard_relkl_rope_bwd(ctypes.byref(desc), ctypes.byref(rope) if rope else None,
+                                   rs, nrs, FAKE, ctypes.byref(g), FAKE, FAKE, 1 << 30, None)
+
+
+def test_rope_reserve_size(lib):
+    st = ctypes.c_int(-1)
+    stats = 2 * (((4 * 128 * 4) + 255) // 256 * 256)
+    n = lib.lard_relkl_rope_reserve_size(ctypes.byref(good_desc()), ctypes.byref(st))
+    assert st.value == OK and n == 2 * (((4 * 100 * 128 * 2) + 255) // 256 * 256) + stats
+    # fp32 inputs keep fp32 rotated copies
+    n = lib.lard_relkl_rope_reserve_size(ctypes.byref(good_desc(dtype=0)), ctypes.byref(st))
+    assert st.value == OK and n == 2 * (((4 * 100 * 128 * 4) + 255) // 256 * 256) + stats
+    assert lib.lard_relkl_rope_reserve_size(ctypes.byref(good_desc(N=0)), ctypes.byref(st)) == 0
+    assert st.value == INVALID
+
+
+def test_rope_validation(lib):
+    d = good_desc()
+    both = _RopeDesc(FAKE, FAKE, FAKE, FAKE)
+    assert rope_fwd(lib, d, None) == INVALID                          # no rope descriptor
+    assert rope_fwd(lib, d, _RopeDesc(FAKE, None, None, None)) == INVALID  # cos without sin
+    assert rope_fwd(lib, d, _RopeDesc(None, None, None, FAKE)) == INVALID
+    assert rope_fwd(lib, d, _RopeDesc(FAKE + 4, FAKE, None, None)) == INVALID  # misaligned
+    assert rope_bwd(lib, d, _RopeDesc(None, None, FAKE, FAKE + 8)) == INVALID
+    plain = lib.lard_relkl_reserve_size(ctypes.byref(d), None)
+    need = lib.lard_relkl_rope_reserve_size(ctypes.byref(d), None)
+    assert rope_fwd(lib, d, both, nrs=need - 1) == WS_SMALL
+    assert rope_bwd(lib, d, both, nrs=need - 1) == WS_SMALL
+    assert rope_fwd(lib, d, both, rs=FAKE + 64) == INVALID            # reserve alignment
+    d32 = good_desc(dtype=0)
+    # the fp32 reserve of the plain path has no copies: too small for the fused path
+    assert rope_fwd(lib, d32, both, nrs=lib.lard_relkl_reserve_size(ctypes.byref(d32), None)) == WS_SMALL
+    assert plain == need  # bf16: the same fp16 copies, rotated
+
+
+def test_rope_fault_injection_maps_to_hip_error(lib, monkeypatch):
+    monkeypatch.setenv("LARD_FAULT_INJECT", "1")
+    both = _RopeDesc(FAKE, FAKE, FAKE, FAKE)
+    assert rope_fwd(lib, good_desc(), both) == HIP
+    assert rope_bwd(lib, good_desc(), both) == HIP
+    assert rope_fwd(lib, good_desc(), _RopeDesc(None, None, None, None)) == HIP
+
+
+def test_rope_python_layer_checks_tables():
+    x = torch.zeros(1, 1, 8, 64)
+    with pytest.raises(RuntimeError, match="GPU"):
+        relkl.rope_relkl_fwd(x, x)
+    with pytest.raises(relkl.LardError):
+        relkl.rope_relkl_fwd(x, x, torch.zeros(8, 31), torch.zeros(8, 31))

@@ -138,3 +138,66 @@ def test_each_side_takes_its_own_tables(causal):
     assert abs(diff["loss"] - swap["loss"]) > 1e-6 * diff["loss"]  # KL is not symmetric
     only_t = rope.forward(x, x, 0.4, causal, ca, sa, None, None)
     assert only_t["loss"] > 1e-3
+
+
+def test_round_bf16_matches_torch_on_fp32_values():
+    """Nearest-even rounding to bf16 agrees with torch's float32 -> bfloat16 conversion,
+    including constructed halfway cases (which round to the even neighbour)."""
+    r = np.random.default_rng(20)
+    v = (r.standard_normal(200000) * np.exp(r.uniform(-8, 8, 200000))).astype(np.float32)
+    bits = v.view(np.uint32)
+    half = ((bits & np.uint32(0xFFFF0000)) | np.uint32(0x8000)).view(np.float32)  # exact ties
+    for arr in (v, half):
+        ref = torch.from_numpy(arr.copy()).to(torch.bfloat16).double().numpy()
+        np.testing.assert_array_equal(rope.round_bf16(arr.astype(np.float64)), ref)
+    # ties go to the even significand
+    assert rope.round_bf16(np.array([1.0 + 2.0 ** -8]))[0] == 1.0
+    assert rope.round_bf16(np.array([1.0 + 3 * 2.0 ** -8]))[0] == 1.0 + 2.0 ** -6
+
+
+def test_rotation_in_dtype_is_the_rounded_exact_rotation():
+    """The fp32 evaluation stays within an fp32 rounding of the exact rotation, and the
+    bf16 rows are the exact rotation rounded to bf16 except where the exact value sits
+    within that fp32 error of a bf16 rounding boundary (then one bf16 step away)."""
+    n, d = 400, 64
+    r = np.random.default_rng(21)
+    x = torch.from_numpy(r.standard_normal((n, d))).to(torch.bfloat16).double().numpy()
+    ang = r.uniform(-3, 3, (n, d // 2))
+    c = np.cos(ang).astype(np.float32).astype(np.float64)
+    s = np.sin(ang).astype(np.float32).astype(np.float64)
+    exact = rope.rotate(x, c, s)
+    f32 = rope.rotate_in_dtype(x, c, s, "fp32")
+    # two fp32 roundings: of the product and of the fused result (|cos|, |sin| <= 1)
+    mag = np.concatenate([np.abs(x[:, : d // 2]) + np.abs(x[:, d // 2:])] * 2, axis=-1)
+    assert np.all(np.abs(f32 - exact) <= 2.0 ** -23 * mag)
+    b16 = rope.rotate_in_dtype(x, c, s, "bf16")
+    mism = b16 != rope.round_bf16(exact)
+    assert mism.mean() < 1e-3
+    ulp = np.ldexp(1.0, np.frexp(exact)[1] - 8)
+    assert np.all(np.abs(b16 - exact)[mism] <= ulp[mism])
+    assert np.all(b16 == rope.round_bf16(b16))  # already bf16 values
+
+
+def test_bf16_fused_loss_equals_unfused_pipeline():
+    """The fused loss in bf16 equals the plain loss on the same pre-RoPE bf16 activations
+    rotated the way a model does it outside the operation (torch fp32 products and sums,
+    then a cast to bf16), up to the rare elements where the two fp32 evaluations round to
+    different bf16 neighbours."""
+    (r,) = workloads.make_rope_inputs("llama2_4k", N=300, Hq=1, Hkv=1, relations=("qq",))
+
+    def model_rope(x, c, s_):
+        x = x.float()
+        h = x.shape[-1] // 2
+        y = torch.cat((x[..., :h] * c - x[..., h:] * s_, x[..., h:] * c + x[..., :h] * s_), -1)
+        return y.to(torch.bfloat16).double().numpy()
+
+    ut = model_rope(r.x_t, r.cos_t, r.sin_t)
+    us = model_rope(r.x_s, r.cos_s, r.sin_s)
+    fused_t = rope.rotate_in_dtype(r.x_t.double().numpy(), r.cos_t.double().numpy(),
+                                   r.sin_t.double().numpy(), "bf16")
+    assert (fused_t != ut).mean() < 1e-3  # the roundings agree almost everywhere
+    tabs = [t.double().numpy() for t in (r.cos_t, r.sin_t, r.cos_s, r.sin_s)]
+    sc = oracle.default_scale(128)
+    a = rope.forward(r.x_t.double().numpy(), r.x_s.double().numpy(), sc, True, *tabs, dtype="bf16")
+    b = oracle.forward(ut, us, sc, True)
+    assert abs(a["loss"] - b["loss"]) <= 1e-9 * b["loss"]
