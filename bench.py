@@ -145,6 +145,49 @@ def mem_sweep(relkl, torch, dev, d=128, H=32, ns=(4096, 8192, 16384, 32768)):
             "fit_intercept_mb": round((my - slope * mx) / 1e6, 3)}
 
 
+def rope_fused_timing(relkl, workloads, wl, dev, causal, steps, tokens, plain_ms):
+    """The RoPE-fused path on the same workload: activations before the rotation and the
+    teacher's / student's fp32 tables (Q/Q and K/K; V/V without), forward + backward of
+    every relation per step, timed like the main line after one untimed step."""
+    import torch
+    rels = workloads.make_rope_inputs(wl)
+    gpu = []
+    for r in rels:
+        tabs = [None if t is None else t.to(dev) for t in (r.cos_t, r.sin_t, r.cos_s, r.sin_s)]
+        gpu.append((r.name, r.x_t.to(dev), r.x_s.to(dev), tabs))
+    gl = torch.ones((), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    log = []
+
+    def step(record):
+        for name, xt, xs, tabs in gpu:
+            if record:
+                ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                ev[0].record(stream)
+            f = relkl.rope_relkl_fwd(xt, xs, *tabs, causal=causal)
+            if record:
+                ev[1].record(stream)
+            relkl.rope_relkl_bwd(xs, f["reserve"], gl, *tabs, causal=causal)
+            if record:
+                ev[2].record(stream)
+                log.append(ev)
+
+    step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(True)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    fwd = sum(e[0].elapsed_time(e[1]) for e in log) / steps
+    bwd = sum(e[1].elapsed_time(e[2]) for e in log) / steps
+    return {"metric": "relation-KL fwd+bwd tokens/s with RoPE applied inside the operation",
+            "value": round(tokens / (ms / 1e3), 1), "unit": "tokens/s", "steps": steps,
+            "ms_per_step": round(ms, 3), "fwd_ms": round(fwd, 3), "bwd_ms": round(bwd, 3),
+            "vs_plain_step": round(ms / plain_ms, 4),
+            "rotated": [r.name for r in rels if r.cos_t is not None]}
+
+
 def stats_ms(v):
     return {"median": round(statistics.median(v), 3), "min": round(min(v), 3)}
 
@@ -159,6 +202,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="host time the oracle sample is sized to")
     ap.add_argument("--no-mem-sweep", action="store_true")
+    ap.add_argument("--rope-steps", type=int, default=5,
+                    help="timed steps of the RoPE-fused path on the same workload (0: skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="before the steps, copy a MIB-MiB buffer three times (a plain copy "
                          "kernel of known size, for scaling HBM byte counters)")
@@ -296,6 +341,11 @@ def main():
         "kernel_sources": kernel_source_digest(),
         "cpu_baseline": None,
     }
+
+    if args.rope_steps > 0:
+        out["next_rows"] = {"rope_fused": rope_fused_timing(relkl, workloads, wl, dev, causal,
+                                                             args.rope_steps, tokens, ms_per_step)}
+        print("[bench] RoPE-fused timing done", file=sys.stderr, flush=True)
 
     if not args.no_mem_sweep:
         del gpu
