@@ -230,28 +230,40 @@ __device__ __forceinline__ typename In::frag_t lds_frag(const char* tile, int ba
 
 // ------------------------------------------------------------------ LDS read pipelines
 // A single wave only sustains about 30 B/clk of LDS reads with a few reads in flight, while
-// its MFMAs consume a 1 KB fragment per 32 cycles; so matrix phases request fragments as
-// far ahead of their MFMAs as the LGKM counter allows: before each MFMA, further fragments
-// are requested while at most kMaxLdsOps reads are outstanding (the counter tracks 15).
-constexpr int kMaxLdsOps = 8;
+// its MFMAs consume a 1 KB fragment per 32 cycles; so matrix phases request fragments far
+// ahead of their MFMAs: before each MFMA, further fragments are requested while at most
+// MAXOPS reads are outstanding (the LGKM counter tracks 15).  Measured best at 32 heads x
+// 32K: 12 in the forward (2% faster than 6 or 8, 14 no better) and 6 in the backward, whose
+// phases hold more registers (0.4% faster than 8; 12 was 2% slower).
+constexpr int kFwdLdsOps = 12;
+constexpr int kBwdLdsOps = 6;
 
-template <int NG, int NF, int OPS_G, int OPS_S>
+template <int NG, int NF, int OPS_G, int OPS_S, int MAXOPS>
 struct LoadSchedule {
   // LDS instructions of fragment k: OPS_G per gradient fragment, OPS_S per score fragment
   static constexpr int ops(int k) { return k < NG ? OPS_G : OPS_S; }
-  // upto[f]: fragments [0, upto[f]) are requested before the MFMA of fragment f
+  // upto[f]: fragments [0, upto[f]) are requested before the MFMA of fragment f.  The
+  // fragment an MFMA consumes is always requested before it, even when its reads alone
+  // exceed MAXOPS (an fp32 gradient fragment takes 8).
   static constexpr std::array<int, NF> make() {
     std::array<int, NF> a{};
     int issued = 0;
     for (int f = 0; f < NF; ++f) {
       int inflight = 0;
       for (int k = f; k < issued; ++k) inflight += ops(k);
-      while (issued < NF && inflight + ops(issued) <= kMaxLdsOps) inflight += ops(issued++);
+      while (issued < NF && inflight + ops(issued) <= MAXOPS) inflight += ops(issued++);
+      if (issued < f + 1) issued = f + 1;
       a[f] = issued;
     }
     return a;
   }
   static constexpr std::array<int, NF> upto = make();
+  static constexpr bool covers() {
+    for (int f = 0; f < NF; ++f)
+      if (upto[f] < f + 1) return false;
+    return true;
+  }
+  static_assert(covers(), "every MFMA's fragment is requested before it");
 };
 
 // ------------------------------------------------------------------ forward
@@ -356,8 +368,8 @@ __device__ __forceinline__ u32x4 bf16x8_to_f16x8_bits(const bf16x8& v) {
 }
 
 // Score contraction of one 32 x 32 block of the forward as a software pipeline: the LDS
-// reads of the key fragments run ahead of their MFMAs with at most kMaxLdsOps reads in
-// flight (see the backward's matrix phase).
+// reads of the key fragments run ahead of their MFMAs with at most kFwdLdsOps reads in
+// flight.
 template <class In, int D>
 __device__ __forceinline__ void score_pipeline(const char* tile_t, const char* tile_s, int fbase,
                                                int jb, const typename In::frag_t (&qt)[D / 16],
@@ -365,7 +377,7 @@ __device__ __forceinline__ void score_pipeline(const char* tile_t, const char* t
                                                f32x16& st, f32x16& ss) {
   using frag_t = typename In::frag_t;
   constexpr int KS = D / 16, NF = 2 * KS;
-  using S = LoadSchedule<0, NF, 1, In::kES == 2 ? 1 : 2>;
+  using S = LoadSchedule<0, NF, 1, In::kES == 2 ? 1 : 2, kFwdLdsOps>;
   frag_t fr[NF];
   auto load = [&](auto fc) __attribute__((always_inline)) {
     constexpr int f = decltype(fc)::value, ks = f / 2, m = f % 2;
@@ -666,7 +678,7 @@ __device__ __forceinline__ void m_pipeline(const char* gtile, int jbg, const cha
   constexpr int KS = D / 16, MB = D / 32;
   constexpr int NG = 2 * MB;
   constexpr int NF = NG + 2 * KS;
-  using S = LoadSchedule<NG, NF, Op::kES == 2 ? 2 : 8, Op::kES == 2 ? 1 : 2>;
+  using S = LoadSchedule<NG, NF, Op::kES == 2 ? 2 : 8, Op::kES == 2 ? 1 : 2, kBwdLdsOps>;
   frag_t fr[NF];
   auto load = [&](auto fc) __attribute__((always_inline)) {
     constexpr int f = decltype(fc)::value;
