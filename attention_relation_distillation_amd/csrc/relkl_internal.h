@@ -29,21 +29,26 @@ inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 //    [units][Npad] with Npad = N rounded up to kBC, for teacher and student, so that
 //    R(i, j) * 2^14 = exp2(S_ij c2 - r_i).
 struct ReserveLayout {
-  size_t x16_t, x16_s, r_t, r_s, total;
+  size_t x16_t, x16_s, y16_t, y16_s, r_t, r_s, total;
   int64_t npad;
 };
 
-// copy_bytes: bytes per element of the row copies (0: none, 2: fp16, 4: fp32).
-inline ReserveLayout reserve_layout(int64_t units, int64_t N, int64_t d, int copy_bytes) {
+// copy_bytes: bytes per element of the row copies (0: none, 2: fp16, 4: fp32); cross: the
+// key-side matrices get copies too (y16_*), otherwise y16_* equal x16_*.
+inline ReserveLayout reserve_layout(int64_t units, int64_t N, int64_t d, int copy_bytes,
+                                    bool cross = false) {
   ReserveLayout L;
   L.npad = round_up(N, kBC);
   const size_t copy = (size_t)round_up(units * N * d * copy_bytes, 256);
   const size_t stats = (size_t)round_up(units * L.npad * 4, 256);
+  const size_t ncopy = cross ? 4 : 2;
   L.x16_t = 0;
   L.x16_s = copy;
-  L.r_t = 2 * copy;
-  L.r_s = 2 * copy + stats;
-  L.total = 2 * copy + 2 * stats;
+  L.y16_t = cross ? 2 * copy : L.x16_t;
+  L.y16_s = cross ? 3 * copy : L.x16_s;
+  L.r_t = ncopy * copy;
+  L.r_s = ncopy * copy + stats;
+  L.total = ncopy * copy + 2 * stats;
   return L;
 }
 
@@ -52,8 +57,10 @@ struct UnitMap {
 };
 
 struct FwdArgs {
-  const void* x_t;
+  const void* x_t;    // own (query-side) rows
   const void* x_s;
+  const void* y_t;    // key-side rows with x's layout (cross relation), or null: x itself
+  const void* y_s;
   int64_t t_sb, t_sh, t_sn;
   int64_t s_sb, s_sh, s_sn;
   int32_t B, H, N;
@@ -73,8 +80,10 @@ struct FwdArgs {
 };
 
 struct BwdArgs {
-  const void* x_t;    // inputs (read by the fp32 path)
+  const void* x_t;    // own rows (read by the fp32 path)
   const void* x_s;
+  const void* y_t;    // staged rows, fp32 path with x_unit_dense (cross relation: the other
+  const void* y_s;    // matrix; the relation: x)
   int64_t t_sb, t_sh, t_sn;
   int64_t s_sb, s_sh, s_sn;
   int64_t g_sb, g_sh, g_sn;  // gradient strides (elements)
@@ -85,10 +94,14 @@ struct BwdArgs {
   int32_t npad;
   float scale;
   float c2;
-  const uint16_t* x16_t;  // reserve fp16 copies (bf16 path)
+  const uint16_t* x16_t;  // reserve fp16 copies of the own rows (bf16 path)
   const uint16_t* x16_s;
-  const float* r_t;
+  const uint16_t* y16_t;  // ... and of the staged rows (the same for the relation)
+  const uint16_t* y16_s;
+  const float* r_t;       // log2 statistics of the own rows
   const float* r_s;
+  const float* rc_t;      // ... and of the staged rows (the same for the relation)
+  const float* rc_s;
   const float* grad_loss;
   const float* rope_cos;  // student RoPE tables [N][d/2] (fused entry points) or null:
   const float* rope_sin;  // the gradient is rotated back before it is written
@@ -129,8 +142,9 @@ struct ReduceArgs {
 // f16_copies: the inputs are the reserve's fp16 copies (RoPE-fused path, bf16 inputs).
 int launch_fwd(const FwdArgs& a, bool in_bf16, int d, bool causal, float* loss,
                void* stream, bool f16_copies = false);
+// mode: 0 relation gradient, 1 cross dA pass, 2 cross dB pass (see relkl_bwd_kernel).
 int launch_bwd(const BwdArgs& a, bool in_bf16, int d, bool causal, bool out_f32,
-               void* stream);
+               void* stream, int mode = 0);
 int launch_splitk_reduce(const ReduceArgs& a, bool out_f32, void* stream);
 int launch_rope_prep(const PrepArgs& a, bool in_bf16, int d, void* stream);
 

@@ -431,8 +431,12 @@ void relkl_fwd_kernel(const FwdArgs a) {
   const int hin = a.map.head_map[h];
   const elem_t* xt = reinterpret_cast<const elem_t*>(a.x_t) + b * a.t_sb + hin * a.t_sh;
   const elem_t* xs = reinterpret_cast<const elem_t*>(a.x_s) + b * a.s_sb + hin * a.s_sh;
-  const char* xt_c = reinterpret_cast<const char*>(xt);
-  const char* xs_c = reinterpret_cast<const char*>(xs);
+  // key-side rows: the same matrix for the relation, B for the cross relation (same layout)
+  const int64_t yo_t = b * a.t_sb + hin * a.t_sh, yo_s = b * a.s_sb + hin * a.s_sh;
+  const char* xt_c = reinterpret_cast<const char*>(
+      a.y_t ? reinterpret_cast<const elem_t*>(a.y_t) + yo_t : xt);
+  const char* xs_c = reinterpret_cast<const char*>(
+      a.y_s ? reinterpret_cast<const elem_t*>(a.y_s) + yo_s : xs);
   const int64_t tsn_b = a.t_sn * In::kES, ssn_b = a.s_sn * In::kES;
 
   const int i0 = I * kBR;
@@ -565,10 +569,12 @@ __global__ __launch_bounds__(256) void loss_reduce_kernel(const double* partial,
 // statistics r (R * 2^14 = exp2(S c2 - r)).
 //   row term  (entry (i, j) of dZ, normalised by the statistic of row i):  kept if j <= i
 //   col term  (entry (j, i) of dZ, normalised by the statistic of row j):  kept if i <= j
-// CLS 0: non-causal (both terms everywhere); 1: block strictly below the diagonal (row
-// term only); 2: strictly above (column term only); 3: diagonal block (both, masked).
-// TAIL zeroes columns j >= N (their staged rows and statistics are copies of row N-1).
-template <int CLS, bool TAIL>
+// ROW / COL: which terms the block takes (the symmetric relation: both where the mask keeps
+// them -- the row term below the diagonal, the column term above, both on the diagonal
+// block; the cross relation's dA pass only row terms, its dB pass only column terms);
+// DIAG: the diagonal block, masked per element; TAIL zeroes columns j >= N (their staged
+// rows and statistics are copies of row N-1).
+template <bool ROW, bool COL, bool DIAG, bool TAIL>
 __device__ __forceinline__ void make_w(const f32x16& st, const f32x16& ss, float rt, float rs,
                                        const float* clt, const float* cls, int hh, int di,
                                        int n_left, float c2, f32x8 (&w32)[2]) {
@@ -576,7 +582,7 @@ __device__ __forceinline__ void make_w(const f32x16& st, const f32x16& ss, float
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     f32x4 ct4 = f32x4{0.f, 0.f, 0.f, 0.f}, cs4 = ct4;
-    if constexpr (CLS != 1) {
+    if constexpr (COL) {
       ct4 = *reinterpret_cast<const f32x4*>(clt + 8 * q + 4 * hh);
       cs4 = *reinterpret_cast<const f32x4*>(cls + 8 * q + 4 * hh);
     }
@@ -585,13 +591,13 @@ __device__ __forceinline__ void make_w(const f32x16& st, const f32x16& ss, float
       const int r = 4 * q + t;
       const int dj = 8 * q + 4 * hh + t;  // j - jb0
       float v = 0.f;
-      if constexpr (CLS != 2) {
+      if constexpr (ROW) {
         const float rt_ = fast_exp2(fmaf(ss[r], c2, -rs)) - fast_exp2(fmaf(st[r], c2, -rt));
-        v = (CLS == 3) ? (dj <= di ? rt_ : 0.f) : rt_;
+        v = DIAG ? (dj <= di ? rt_ : 0.f) : rt_;
       }
-      if constexpr (CLS != 1) {
+      if constexpr (COL) {
         const float ct_ = fast_exp2(fmaf(ss[r], c2, -cs4[t])) - fast_exp2(fmaf(st[r], c2, -ct4[t]));
-        v += (CLS == 3) ? (dj >= di ? ct_ : 0.f) : ct_;
+        v += DIAG ? (dj >= di ? ct_ : 0.f) : ct_;
       }
       if constexpr (TAIL) v = dj < n_left ? v : 0.f;
       wv[r] = v;
@@ -718,12 +724,17 @@ __device__ __forceinline__ void m_pipeline(const char* gtile, int jbg, const cha
 
 // Backward work decomposition: a workgroup of 8 waves (two per SIMD) owns kBRB = 256 rows,
 // 32 per wave, and sweeps the whole key range in key tiles of 64 rows (two 32-key blocks).
+// MODE 0 is the relation gradient (own rows and staged rows are the same matrix: row and
+// column terms).  The cross relation softmax(A B^T) takes two passes: MODE 1 owns rows of
+// A and stages rows of B (row terms only: dA = scale dZ B_s, keys j <= i when causal);
+// MODE 2 owns rows of B and stages rows of A with their statistics (column terms only:
+// dB = scale dZ^T A_s, queries i >= j when causal).
 // For each block n a wave runs
 //    M(n): gradient MFMAs of block n-1 (W(n-1) X_s) and score MFMAs of block n
 //    V(n): W(n) from the scores of block n (exp / VALU work)
 // The waves drift freely between the barriers that separate key tiles, so one wave's
 // vector work overlaps its SIMD partner's matrix work.
-template <class Op, int D, bool CAUSAL, bool OUT_F32>
+template <class Op, int D, bool CAUSAL, bool OUT_F32, int MODE>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void relkl_bwd_kernel(const BwdArgs a) {
   using elem_t = typename Op::elem_t;
@@ -749,36 +760,50 @@ void relkl_bwd_kernel(const BwdArgs a) {
   const int split = w % a.splits;
   const int wt = w / a.splits;
   const int unit = wt / a.row_tiles;
-  const int I = wt - unit * a.row_tiles;
+  // the cross dA pass does more work for later row tiles under the causal mask: run those
+  // first, as the forward does (the dB pass already starts with its longest row tiles)
+  const int I = (CAUSAL && MODE == 1) ? a.row_tiles - 1 - (wt - unit * a.row_tiles)
+                                      : wt - unit * a.row_tiles;
   const int b = unit / a.H, h = unit - (unit / a.H) * a.H;
   const int hin = a.map.head_map[h];
 
-  // Operands: the fp16 reserve copies (dense [unit][N][D]) or the fp32 inputs.
+  // Operands: the fp16 reserve copies (dense [unit][N][D]) or the fp32 inputs; own rows
+  // from x, staged key rows from y (the same matrix for the relation).
   const elem_t* xt;
   const elem_t* xs;
+  const elem_t* yt;
+  const elem_t* ys;
   int64_t tsn, ssn;
   if constexpr (Op::kES == 2) {
     xt = a.x16_t + (int64_t)unit * N * D;
     xs = a.x16_s + (int64_t)unit * N * D;
+    yt = a.y16_t + (int64_t)unit * N * D;
+    ys = a.y16_s + (int64_t)unit * N * D;
     tsn = D;
     ssn = D;
   } else if (a.x_unit_dense) {
-    // fp32 copies in the reserve (rotated inputs), dense [unit][N][D]
+    // fp32 copies in the reserve (rotated or cross inputs), dense [unit][N][D]
     xt = reinterpret_cast<const elem_t*>(a.x_t) + (int64_t)unit * N * D;
     xs = reinterpret_cast<const elem_t*>(a.x_s) + (int64_t)unit * N * D;
+    yt = reinterpret_cast<const elem_t*>(a.y_t) + (int64_t)unit * N * D;
+    ys = reinterpret_cast<const elem_t*>(a.y_s) + (int64_t)unit * N * D;
     tsn = D;
     ssn = D;
   } else {
     xt = reinterpret_cast<const elem_t*>(a.x_t) + b * a.t_sb + hin * a.t_sh;
     xs = reinterpret_cast<const elem_t*>(a.x_s) + b * a.s_sb + hin * a.s_sh;
+    yt = xt;
+    ys = xs;
     tsn = a.t_sn;
     ssn = a.s_sn;
   }
-  const char* xt_c = reinterpret_cast<const char*>(xt);
-  const char* xs_c = reinterpret_cast<const char*>(xs);
+  const char* yt_c = reinterpret_cast<const char*>(yt);
+  const char* ys_c = reinterpret_cast<const char*>(ys);
   const int64_t tsn_b = tsn * Op::kES, ssn_b = ssn * Op::kES;
-  const float* rst_t = a.r_t + (int64_t)unit * a.npad;
+  const float* rst_t = a.r_t + (int64_t)unit * a.npad;   // statistics of the own rows
   const float* rst_s = a.r_s + (int64_t)unit * a.npad;
+  const float* cst_t = a.rc_t + (int64_t)unit * a.npad;  // statistics of the staged rows
+  const float* cst_s = a.rc_s + (int64_t)unit * a.npad;
 
   const int i0 = I * kBRB;
   const int ib0 = i0 + 32 * wave;
@@ -788,8 +813,14 @@ void relkl_bwd_kernel(const BwdArgs a) {
   const int tb0 = Op::kES == 2 ? trb_base<D>(lane, 0) : 0;
   const int tb1 = Op::kES == 2 ? trb_base<D>(lane, 1) : 0;
 
-  const int kt_begin = (int)(((int64_t)a.key_tiles * split) / a.splits);
-  const int kt_end = (int)(((int64_t)a.key_tiles * (split + 1)) / a.splits);
+  // Key tiles this workgroup sweeps: all of them for the relation; for the cross passes
+  // under the causal mask only those holding kept entries (up to the last own row for
+  // dA, from the first own row on for dB).  The split divides that range.
+  int kt_lo = 0, kt_hi = a.key_tiles;
+  if constexpr (CAUSAL && MODE == 1) kt_hi = min(a.key_tiles, (i0 + kBRB + kBC - 1) / kBC);
+  if constexpr (CAUSAL && MODE == 2) kt_lo = i0 / kBC;
+  const int kt_begin = kt_lo + (int)(((int64_t)(kt_hi - kt_lo) * split) / a.splits);
+  const int kt_end = kt_lo + (int)(((int64_t)(kt_hi - kt_lo) * (split + 1)) / a.splits);
   const int NB = 2 * (kt_end - kt_begin);
 
   // Stage: [teacher tile][student tile][teacher stats][student stats]; all 8 waves copy
@@ -804,11 +835,11 @@ void relkl_bwd_kernel(const BwdArgs a) {
       const int r = t / G::kCPR;
       const int c = (t % G::kCPR) ^ G::swz(r);
       const int j = min(j0 + r, N - 1);
-      lds_copy16(xt_c + (int64_t)j * tsn_b + c * 16, lds_addr(st_base + slot0 * 16));
-      lds_copy16(xs_c + (int64_t)j * ssn_b + c * 16, lds_addr(st_base + G::kTileBytes + slot0 * 16));
+      lds_copy16(yt_c + (int64_t)j * tsn_b + c * 16, lds_addr(st_base + slot0 * 16));
+      lds_copy16(ys_c + (int64_t)j * ssn_b + c * 16, lds_addr(st_base + G::kTileBytes + slot0 * 16));
     }
     if (wave == 0 && lane < 32) {
-      const float* src = (lane < 16 ? rst_t : rst_s) + j0 + 4 * (lane & 15);
+      const float* src = (lane < 16 ? cst_t : cst_s) + j0 + 4 * (lane & 15);
       lds_copy16(src, lds_addr(st_base + 2 * G::kTileBytes));
     }
   };
@@ -883,22 +914,34 @@ void relkl_bwd_kernel(const BwdArgs a) {
       const int di = row - jb0;
       const int nl = N - jb0;
       const bool tail = jb0 + 32 > N;
+      constexpr bool ROW = MODE != 2, COL = MODE != 1;
+      bool none = false;  // the block holds no entry this pass keeps
       if constexpr (!CAUSAL) {
-        if (tail) make_w<0, true>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, w32);
-        else make_w<0, false>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, w32);
+        if (tail) make_w<ROW, COL, false, true>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, w32);
+        else make_w<ROW, COL, false, false>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, w32);
       } else {
-        if (jb0 + 31 < ib0) {
-          make_w<1, false>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, w32);
-        } else if (jb0 > ib0 + 31) {
-          if (tail) make_w<2, true>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, w32);
-          else make_w<2, false>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, w32);
+        if (jb0 + 31 < ib0) {  // strictly below the diagonal: row terms
+          if constexpr (ROW) make_w<true, false, false, false>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, w32);
+          else none = true;
+        } else if (jb0 > ib0 + 31) {  // strictly above: column terms
+          if constexpr (COL) {
+            if (tail) make_w<false, true, false, true>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, w32);
+            else make_w<false, true, false, false>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, w32);
+          } else {
+            none = true;
+          }
         } else {
-          if (tail) make_w<3, true>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, w32);
-          else make_w<3, false>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, w32);
+          if (tail) make_w<ROW, COL, true, true>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, w32);
+          else make_w<ROW, COL, true, false>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, w32);
         }
       }
-      wf0 = w_frag<Op>(w32[0]);
-      wf1 = w_frag<Op>(w32[1]);
+      if (none) {
+        wf0 = frag_t{};
+        wf1 = frag_t{};
+      } else {
+        wf0 = w_frag<Op>(w32[0]);
+        wf1 = w_frag<Op>(w32[1]);
+      }
     } else {
       wf0 = frag_t{};
       wf1 = frag_t{};
@@ -1115,30 +1158,41 @@ int launch_fwd(const FwdArgs& a, bool in_bf16, int d, bool causal, float* loss, 
                 : launch_fwd_t<F32In, 64, false>(a, loss, s);
 }
 
-template <class Op, int D, bool CAUSAL, bool OUT_F32>
+template <class Op, int D, bool CAUSAL, bool OUT_F32, int MODE>
 static int launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   const int grid = a.B * a.H * a.row_tiles * a.splits;
-  hipLaunchKernelGGL((relkl_bwd_kernel<Op, D, CAUSAL, OUT_F32>), dim3(grid), dim3(kBWaves * kWave),
-                     0, s, a);
+  hipLaunchKernelGGL((relkl_bwd_kernel<Op, D, CAUSAL, OUT_F32, MODE>), dim3(grid),
+                     dim3(kBWaves * kWave), 0, s, a);
   return (int)hipGetLastError();
 }
 
-template <class Op, int D>
+template <class Op, int D, int MODE>
 static int launch_bwd_d(const BwdArgs& a, bool causal, bool out_f32, hipStream_t s) {
-  if (causal) return out_f32 ? launch_bwd_t<Op, D, true, true>(a, s) : launch_bwd_t<Op, D, true, false>(a, s);
-  return out_f32 ? launch_bwd_t<Op, D, false, true>(a, s) : launch_bwd_t<Op, D, false, false>(a, s);
+  if (causal) return out_f32 ? launch_bwd_t<Op, D, true, true, MODE>(a, s)
+                             : launch_bwd_t<Op, D, true, false, MODE>(a, s);
+  return out_f32 ? launch_bwd_t<Op, D, false, true, MODE>(a, s)
+                 : launch_bwd_t<Op, D, false, false, MODE>(a, s);
 }
 
-int launch_bwd(const BwdArgs& a, bool in_bf16, int d, bool causal, bool out_f32, void* stream) {
-  if (fault_injected()) return (int)hipErrorLaunchFailure;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+template <int MODE>
+static int launch_bwd_m(const BwdArgs& a, bool in_bf16, int d, bool causal, bool out_f32,
+                        hipStream_t s) {
   if (in_bf16) {
-    return d == 128 ? launch_bwd_d<F16Op, 128>(a, causal, out_f32, s)
-                    : launch_bwd_d<F16Op, 64>(a, causal, out_f32, s);
+    return d == 128 ? launch_bwd_d<F16Op, 128, MODE>(a, causal, out_f32, s)
+                    : launch_bwd_d<F16Op, 64, MODE>(a, causal, out_f32, s);
   }
   // fp32 inputs always give an fp32 gradient
-  return d == 128 ? launch_bwd_d<F32In, 128>(a, causal, true, s)
-                  : launch_bwd_d<F32In, 64>(a, causal, true, s);
+  return d == 128 ? launch_bwd_d<F32In, 128, MODE>(a, causal, true, s)
+                  : launch_bwd_d<F32In, 64, MODE>(a, causal, true, s);
+}
+
+int launch_bwd(const BwdArgs& a, bool in_bf16, int d, bool causal, bool out_f32, void* stream,
+               int mode) {
+  if (fault_injected()) return (int)hipErrorLaunchFailure;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (mode == 1) return launch_bwd_m<1>(a, in_bf16, d, causal, out_f32, s);
+  if (mode == 2) return launch_bwd_m<2>(a, in_bf16, d, causal, out_f32, s);
+  return launch_bwd_m<0>(a, in_bf16, d, causal, out_f32, s);
 }
 
 int launch_rope_prep(const PrepArgs& a, bool in_bf16, int d, void* stream) {

@@ -19,7 +19,8 @@ import torch
 
 __all__ = ["LardError", "library_path", "load_library", "relkl_fwd", "relkl_bwd",
            "relation_kl", "workspace_size", "reserve_size", "rope_reserve_size",
-           "rope_relkl_fwd", "rope_relkl_bwd", "rope_relation_kl", "LARD_MAX_HEADS"]
+           "rope_relkl_fwd", "rope_relkl_bwd", "rope_relation_kl", "cross_reserve_size",
+           "cross_relkl_fwd", "cross_relkl_bwd", "cross_relation_kl", "LARD_MAX_HEADS"]
 
 LARD_FP32 = 0
 LARD_BF16 = 1
@@ -55,6 +56,15 @@ class _RopeDesc(ctypes.Structure):
     _fields_ = [
         ("cos_teacher", ctypes.c_void_p), ("sin_teacher", ctypes.c_void_p),
         ("cos_student", ctypes.c_void_p), ("sin_student", ctypes.c_void_p),
+    ]
+
+
+class _CrossDesc(ctypes.Structure):
+    _fields_ = [
+        ("bt_stride_b", ctypes.c_int64), ("bt_stride_h", ctypes.c_int64),
+        ("bt_stride_n", ctypes.c_int64),
+        ("bs_stride_b", ctypes.c_int64), ("bs_stride_h", ctypes.c_int64),
+        ("bs_stride_n", ctypes.c_int64),
     ]
 
 
@@ -104,6 +114,17 @@ def load_library():
     lib.lard_relkl_rope_bwd.restype = ctypes.c_int
     lib.lard_relkl_rope_bwd.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(_RopeDesc), vp,
                                         sz, vp, ctypes.POINTER(_GradDesc), vp, vp, sz, vp]
+    lib.lard_relkl_cross_reserve_size.restype = sz
+    lib.lard_relkl_cross_reserve_size.argtypes = [ctypes.POINTER(_Desc),
+                                                  ctypes.POINTER(ctypes.c_int)]
+    lib.lard_relkl_cross_fwd.restype = ctypes.c_int
+    lib.lard_relkl_cross_fwd.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(_CrossDesc),
+                                         ctypes.POINTER(_RopeDesc), vp, vp, vp, vp, vp, vp, vp,
+                                         vp, vp, sz, vp, sz, vp]
+    lib.lard_relkl_cross_bwd.restype = ctypes.c_int
+    lib.lard_relkl_cross_bwd.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(_RopeDesc), vp,
+                                         sz, vp, ctypes.POINTER(_GradDesc), vp,
+                                         ctypes.POINTER(_GradDesc), vp, vp, sz, vp]
     lib.lard_status_string.restype = ctypes.c_char_p
     lib.lard_status_string.argtypes = [ctypes.c_int]
     lib.lard_version.restype = ctypes.c_int
@@ -400,3 +421,141 @@ def rope_relation_kl(x_t: torch.Tensor, x_s: torch.Tensor, cos_t=None, sin_t=Non
     token (None: that side is not rotated).  Differentiable with respect to x_s."""
     return _RopeRelationKL.apply(x_t.detach(), x_s, cos_t, sin_t, cos_s, sin_s, causal, scale,
                                  None if head_map is None else tuple(int(v) for v in head_map))
+
+
+# ------------------------------------------------------------------ cross-relation entry points
+def _cross_desc(a_t, a_s, b_t, b_s) -> _CrossDesc:
+    if b_t.shape != a_t.shape or b_s.shape != a_s.shape:
+        raise LardError(1, "A and B must have the same shape [B, H, N, d]")
+    if b_t.dtype != a_t.dtype or b_s.dtype != a_s.dtype:
+        raise LardError(1, "A and B must have the same dtype")
+    if b_t.stride(-1) != 1 or b_s.stride(-1) != 1:
+        raise LardError(1, "the last dimension (d) of B must be contiguous")
+    if b_t.device != a_t.device or b_s.device != a_t.device:
+        raise LardError(1, "all inputs must be on the same device")
+    return _CrossDesc(bt_stride_b=b_t.stride(0), bt_stride_h=b_t.stride(1),
+                      bt_stride_n=b_t.stride(2), bs_stride_b=b_s.stride(0),
+                      bs_stride_h=b_s.stride(1), bs_stride_n=b_s.stride(2))
+
+
+def _rope_ptr(x, tables):
+    if tables is None or all(t is None for t in tables):
+        return None
+    return ctypes.byref(_rope_desc(x, tables))
+
+
+def cross_reserve_size(a_t, a_s, *, causal=True, scale=None, head_map=None) -> int:
+    lib = load_library()
+    desc, _keep = _make_desc(a_t, a_s, causal, scale, head_map)
+    st = ctypes.c_int(0)
+    n = lib.lard_relkl_cross_reserve_size(ctypes.byref(desc), ctypes.byref(st))
+    _check(st.value)
+    return int(n)
+
+
+def cross_relkl_fwd(a_t: torch.Tensor, b_t: torch.Tensor, a_s: torch.Tensor, b_s: torch.Tensor,
+                    *, rope=None, causal: bool = True, scale: Optional[float] = None,
+                    head_map: Optional[Sequence[int]] = None, want_row_kl: bool = False,
+                    stream=None):
+    """Forward of the cross relation softmax(scale A B^T) per side (A: queries, B: keys);
+    rope: None or (cos_t, sin_t, cos_s, sin_s) rotating each side's A and B.  Returns the
+    same dict as relkl_fwd; its reserve is what cross_relkl_bwd needs."""
+    lib = load_library()
+    desc, keep = _make_desc(a_t, a_s, causal, scale, head_map)
+    kdesc = _cross_desc(a_t, a_s, b_t, b_s)
+    rptr = _rope_ptr(a_t, rope)
+    _require_gpu(a_t)
+    b, n = desc.B, desc.N
+    dev = a_t.device
+    lse_t = torch.empty((b, desc.H, n), dtype=torch.float32, device=dev)
+    lse_s = torch.empty((b, desc.H, n), dtype=torch.float32, device=dev)
+    row_kl = torch.empty((b, desc.H, n), dtype=torch.float32, device=dev) if want_row_kl else None
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    st = ctypes.c_int(0)
+    ws_bytes = lib.lard_relkl_workspace_size(ctypes.byref(desc), 0, ctypes.byref(st))
+    _check(st.value)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    rs_bytes = lib.lard_relkl_cross_reserve_size(ctypes.byref(desc), ctypes.byref(st))
+    _check(st.value)
+    reserve = torch.empty(max(rs_bytes, 256), dtype=torch.uint8, device=dev)
+    _check(lib.lard_relkl_cross_fwd(ctypes.byref(desc), ctypes.byref(kdesc), rptr,
+                                    a_t.data_ptr(), b_t.data_ptr(), a_s.data_ptr(),
+                                    b_s.data_ptr(), lse_t.data_ptr(), lse_s.data_ptr(),
+                                    row_kl.data_ptr() if row_kl is not None else None,
+                                    loss.data_ptr(), reserve.data_ptr(), reserve.numel(),
+                                    ws.data_ptr(), ws.numel(), _stream_handle(dev, stream)))
+    del keep
+    return {"loss": loss, "lse_t": lse_t, "lse_s": lse_s, "row_kl": row_kl, "reserve": reserve}
+
+
+def _new_grad(x, head_map, n_in, dx, dx_dtype):
+    if dx is None:
+        out_dtype = x.dtype if dx_dtype is None else dx_dtype
+        subset = head_map is not None and sorted(int(v) for v in head_map) != list(range(n_in))
+        dx = (torch.zeros if subset else torch.empty)(x.shape, dtype=out_dtype, device=x.device)
+    if dx.shape != x.shape or dx.stride(-1) != 1 or dx.device != x.device:
+        raise LardError(1, "gradients must match their input in shape, with a contiguous last "
+                           "dimension")
+    return dx, _GradDesc(dtype=_dtype_code(dx.dtype), reserved=0, stride_b=dx.stride(0),
+                         stride_h=dx.stride(1), stride_n=dx.stride(2))
+
+
+def cross_relkl_bwd(a_s: torch.Tensor, b_s: torch.Tensor, reserve: torch.Tensor,
+                    grad_loss: torch.Tensor, *, rope=None, causal: bool = True,
+                    scale: Optional[float] = None, head_map: Optional[Sequence[int]] = None,
+                    da: Optional[torch.Tensor] = None, db: Optional[torch.Tensor] = None,
+                    dx_dtype: Optional[torch.dtype] = None, stream=None):
+    """(dA_s, dB_s) of grad_loss * loss; a_s / b_s give shapes, dtypes and the device (their
+    values are not read: the operands come from the reserve)."""
+    lib = load_library()
+    desc, keep = _make_desc(a_s, a_s, causal, scale, head_map)
+    rptr = _rope_ptr(a_s, rope)
+    _require_gpu(a_s)
+    dev = a_s.device
+    if reserve.dtype != torch.uint8 or not reserve.is_contiguous() or reserve.device != dev:
+        raise LardError(1, "reserve must be the uint8 device buffer returned by cross_relkl_fwd")
+    if (grad_loss.dtype != torch.float32 or grad_loss.numel() != 1 or grad_loss.device != dev):
+        raise LardError(1, "grad_loss must be a one-element fp32 tensor on the inputs' device")
+    grad_loss = grad_loss.contiguous()
+    da, gda = _new_grad(a_s, head_map, desc.H_in, da, dx_dtype)
+    db, gdb = _new_grad(b_s, head_map, desc.H_in, db, dx_dtype)
+    st = ctypes.c_int(0)
+    ws_bytes = lib.lard_relkl_workspace_size(ctypes.byref(desc), 1, ctypes.byref(st))
+    _check(st.value)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    _check(lib.lard_relkl_cross_bwd(ctypes.byref(desc), rptr, reserve.data_ptr(),
+                                    reserve.numel(), grad_loss.data_ptr(), ctypes.byref(gda),
+                                    da.data_ptr(), ctypes.byref(gdb), db.data_ptr(),
+                                    ws.data_ptr(), ws.numel(), _stream_handle(dev, stream)))
+    del keep
+    return da, db
+
+
+class _CrossRelationKL(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, a_t, b_t, a_s, b_s, rope, causal, scale, head_map):
+        out = cross_relkl_fwd(a_t, b_t, a_s, b_s, rope=rope, causal=causal, scale=scale,
+                              head_map=head_map)
+        ctx.save_for_backward(a_s, b_s, out["reserve"])
+        ctx.rope, ctx.causal, ctx.scale, ctx.head_map = rope, causal, scale, head_map
+        return out["loss"]
+
+    @staticmethod
+    def backward(ctx, grad):
+        a_s, b_s, reserve = ctx.saved_tensors
+        g = grad if grad.dtype == torch.float32 else grad.float()
+        da, db = cross_relkl_bwd(a_s, b_s, reserve, g, rope=ctx.rope, causal=ctx.causal,
+                                 scale=ctx.scale, head_map=ctx.head_map)
+        return None, None, da, db, None, None, None, None
+
+
+def cross_relation_kl(a_t: torch.Tensor, b_t: torch.Tensor, a_s: torch.Tensor,
+                      b_s: torch.Tensor, *, rope=None, causal: bool = True,
+                      scale: Optional[float] = None, head_map: Optional[Sequence[int]] = None):
+    """Sum over rows of KL(softmax(scale A_t B_t^T) || softmax(scale A_s B_s^T)) (e.g. the
+    attention maps of queries A and keys B), differentiable with respect to a_s and b_s.
+    rope: None or (cos_t, sin_t, cos_s, sin_s) applied to each side's A and B inside the
+    call."""
+    return _CrossRelationKL.apply(a_t.detach(), b_t.detach(), a_s, b_s,
+                                  None if rope is None else tuple(rope), causal, scale,
+                                  None if head_map is None else tuple(int(v) for v in head_map))

@@ -188,6 +188,56 @@ def rope_fused_timing(relkl, workloads, wl, dev, causal, steps, tokens, plain_ms
             "rotated": [r.name for r in rels if r.cos_t is not None]}
 
 
+def cross_timing(relkl, workloads, wl, dev, causal, steps, tokens):
+    """The cross relation on the same workload: the attention maps softmax(Q K^T / sqrt(d))
+    of teacher and student from the pre-RoPE Q and K draws, rotated inside the call (teacher
+    native RoPE, student the workload's), gradients to the student's Q and K; one call per
+    step over all heads, timed like the main line after one untimed step."""
+    import torch
+    rels = {r.name: r for r in workloads.make_rope_inputs(wl, relations=("qq", "kk"))}
+    q, k = rels["qq"], rels["kk"]
+    if q.x_t.shape != k.x_t.shape:
+        return {"skipped": "query and key head counts differ"}
+    a_t, b_t = q.x_t.to(dev), k.x_t.to(dev)
+    a_s, b_s = q.x_s.to(dev), k.x_s.to(dev)
+    tabs = [t.to(dev) for t in (q.cos_t, q.sin_t, q.cos_s, q.sin_s)]
+    gl = torch.ones((), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    log = []
+
+    def step(record):
+        if record:
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            ev[0].record(stream)
+        f = relkl.cross_relkl_fwd(a_t, b_t, a_s, b_s, rope=tabs, causal=causal)
+        if record:
+            ev[1].record(stream)
+        relkl.cross_relkl_bwd(a_s, b_s, f["reserve"], gl, rope=tabs, causal=causal)
+        if record:
+            ev[2].record(stream)
+            log.append(ev)
+
+    step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(True)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    fwd = sum(e[0].elapsed_time(e[1]) for e in log) / steps
+    bwd = sum(e[1].elapsed_time(e[2]) for e in log) / steps
+    h = q.x_t.shape[1]
+    fl_f, fl_b = alg_flops(wl.B, h, wl.N, wl.d, causal)
+    ach = fl_b / (bwd / 1e3) / 1e12
+    return {"metric": "cross-relation (Q K^T attention map, RoPE inside) fwd+bwd tokens/s",
+            "value": round(tokens / (ms / 1e3), 1), "unit": "tokens/s", "steps": steps,
+            "ms_per_step": round(ms, 3), "fwd_ms": round(fwd, 3), "bwd_ms": round(bwd, 3),
+            "roofline": {"bound": "mfma", "kernel": "relkl_bwd_kernel (dA and dB passes)",
+                         "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                         "alg_flops_per_call": fl_b}}
+
+
 def stats_ms(v):
     return {"median": round(statistics.median(v), 3), "min": round(min(v), 3)}
 
@@ -204,6 +254,9 @@ def main():
     ap.add_argument("--no-mem-sweep", action="store_true")
     ap.add_argument("--rope-steps", type=int, default=5,
                     help="timed steps of the RoPE-fused path on the same workload (0: skip)")
+    ap.add_argument("--cross-steps", type=int, default=5,
+                    help="timed steps of the cross relation (attention maps Q K^T with RoPE "
+                         "inside) on the same workload (0: skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="before the steps, copy a MIB-MiB buffer three times (a plain copy "
                          "kernel of known size, for scaling HBM byte counters)")
@@ -346,6 +399,10 @@ def main():
         out["next_rows"] = {"rope_fused": rope_fused_timing(relkl, workloads, wl, dev, causal,
                                                              args.rope_steps, tokens, ms_per_step)}
         print("[bench] RoPE-fused timing done", file=sys.stderr, flush=True)
+    if args.cross_steps > 0:
+        out.setdefault("next_rows", {})["cross_attention_map"] = cross_timing(
+            relkl, workloads, wl, dev, causal, args.cross_steps, tokens)
+        print("[bench] cross-relation timing done", file=sys.stderr, flush=True)
 
     if not args.no_mem_sweep:
         del gpu

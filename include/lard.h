@@ -213,6 +213,58 @@ lard_status lard_relkl_rope_bwd(const lard_relkl_desc* desc, const lard_rope_des
                                 void* dx_student, void* workspace, size_t workspace_bytes,
                                 void* stream);
 
+/*
+ * Cross-relation entry points: the same row-wise KL for the relation between two different
+ * matrices per side, softmax(scale * A B^T + M) -- e.g. the attention map of queries A and
+ * keys B -- the general form the verdict page's own inference on the method's scope
+ * points to (the relation case is A = B).  Per side m = t, s:
+ *     Z_m = scale * A_m B_m^T + M,  R_m = row-softmax(Z_m),  loss = sum_i KL(R_t(i,:) || R_s(i,:))
+ * and, for an upstream gradient g, with dZ = g (R_s - R_t) (0 where masked):
+ *     dA_s = scale * dZ B_s,   dB_s = scale * dZ^T A_s      (teacher frozen).
+ * A and B have the same shape [B, H_in, N, d] and dtype; `desc` describes A (its t_ / s_
+ * strides) together with the mask, scale and head map, which apply to B too; `keys` gives
+ * B's strides (same rules as the descriptor's).  With `rope` non-NULL each side's tables
+ * rotate both its A and its B (as RoPE rotates queries and keys alike; see the RoPE-fused
+ * entry points for the rotation, rounding and table layout) and the gradients are returned
+ * with respect to the pre-rotation inputs.  The reserve holds copies of all four matrices
+ * (fp16 images of bf16 values, or fp32) and the row statistics; size from
+ * lard_relkl_cross_reserve_size.  Workspaces are those of lard_relkl_workspace_size.
+ * Validation, ownership, stream and error conventions are those of the plain entry points.
+ */
+typedef struct lard_cross_desc {
+  int64_t bt_stride_b, bt_stride_h, bt_stride_n;  /* teacher B strides, in elements */
+  int64_t bs_stride_b, bs_stride_h, bs_stride_n;  /* student B strides, in elements */
+} lard_cross_desc;
+
+/* Bytes of the reserve the cross forward writes: 4 * c * B * H * N * d (c = 2 for bf16, 4
+ * for fp32 inputs) plus 2 * 4 * B * H * roundup(N, 64), each part rounded up to 256 bytes.
+ * Returns 0 and sets *status on an invalid descriptor. */
+size_t lard_relkl_cross_reserve_size(const lard_relkl_desc* desc, lard_status* status);
+
+/*
+ * Cross forward.  a_*, b_*: device, A in desc's layout, B in `keys`' layout, desc's dtype.
+ * rope: NULL (no rotation) or tables as for lard_relkl_rope_fwd.  Outputs (LSE and row KL
+ * per row of A), reserve and workspace as for lard_relkl_fwd.
+ */
+lard_status lard_relkl_cross_fwd(const lard_relkl_desc* desc, const lard_cross_desc* keys,
+                                 const lard_rope_desc* rope, const void* a_teacher,
+                                 const void* b_teacher, const void* a_student,
+                                 const void* b_student, float* lse_teacher, float* lse_student,
+                                 float* row_kl, float* loss, void* reserve, size_t reserve_bytes,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Cross backward: dA_s and dB_s of g * loss, each written like lard_relkl_bwd's gradient
+ * (layout and dtype from grad_a / grad_b; heads outside head_map untouched).  Needs only the
+ * reserve the cross forward wrote and the same `rope` (NULL if the forward had none).
+ */
+lard_status lard_relkl_cross_bwd(const lard_relkl_desc* desc, const lard_rope_desc* rope,
+                                 const void* reserve, size_t reserve_bytes,
+                                 const float* grad_loss, const lard_grad_desc* grad_a,
+                                 void* da_student, const lard_grad_desc* grad_b,
+                                 void* db_student, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* lard_status_string(lard_status status);
 

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 from attention_relation_distillation_amd import relkl
-from attention_relation_distillation_amd.relkl import _Desc, _GradDesc, _RopeDesc
+from attention_relation_distillation_amd.relkl import _CrossDesc, _Desc, _GradDesc, _RopeDesc
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 OK, INVALID, UNSUPPORTED, WS_SMALL, HIP = 0, 1, 2, 3, 4
@@ -32,7 +32,8 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) >= {"lard_relkl_fwd", "lard_relkl_bwd", "lard_relkl_workspace_size",
                           "lard_relkl_reserve_size", "lard_status_string", "lard_version",
                           "lard_relkl_rope_reserve_size", "lard_relkl_rope_fwd",
-                          "lard_relkl_rope_bwd"}
+                          "lard_relkl_rope_bwd", "lard_relkl_cross_reserve_size",
+                          "lard_relkl_cross_fwd", "lard_relkl_cross_bwd"}
     for n in names:
         assert hasattr(lib, n), n
     assert lib.lard_version() >= 10000
@@ -249,3 +250,66 @@ def test_rope_python_layer_checks_tables():
         relkl.rope_relkl_fwd(x, x)
     with pytest.raises(relkl.LardError):
         relkl.rope_relkl_fwd(x, x, torch.zeros(8, 31), torch.zeros(8, 31))
+
+
+# ------------------------------------------------------------------ cross-relation entry points
+def good_keys(**kw):
+    base = dict(bt_stride_b=4 * 100 * 128, bt_stride_h=100 * 128, bt_stride_n=128,
+                bs_stride_b=4 * 100 * 128, bs_stride_h=100 * 128, bs_stride_n=128)
+    base.update(kw)
+    return _CrossDesc(**base)
+
+
+def cross_fwd(lib, desc, keys, rope=None, rs=FAKE, nrs=1 << 30):
+    return lib.lard_relkl_cross_fwd(ctypes.byref(desc), ctypes.byref(keys) if keys else None,
+                                    ctypes.byref(rope) if rope else None, FAKE, FAKE, FAKE, FAKE,
+                                    FAKE, FAKE, None, FAKE, rs, nrs, FAKE, 1 << 20, None)
+
+
+def cross_bwd(lib, desc, ga=None, gb=None, rope=None, rs=FAKE, nrs=1 << 30, da=FAKE, db=FAKE):
+    g = _GradDesc(dtype=1, reserved=0, stride_b=4 * 100 * 128, stride_h=100 * 128, stride_n=128)
+    ga = ga or g
+    gb = gb or g
+    return lib.lard_relkl_cross_bwd(ctypes.byref(desc), ctypes.byref(rope) if rope else None,
+                                    rs, nrs, FAKE, ctypes.byref(ga), da, ctypes.byref(gb), db,
+                                    FAKE, 1 << 30, None)
+
+
+def test_cross_reserve_size(lib):
+    st = ctypes.c_int(-1)
+    stats = 2 * (((4 * 128 * 4) + 255) // 256 * 256)
+    n = lib.lard_relkl_cross_reserve_size(ctypes.byref(good_desc()), ctypes.byref(st))
+    assert st.value == OK and n == 4 * (((4 * 100 * 128 * 2) + 255) // 256 * 256) + stats
+    n = lib.lard_relkl_cross_reserve_size(ctypes.byref(good_desc(dtype=0)), ctypes.byref(st))
+    assert st.value == OK and n == 4 * (((4 * 100 * 128 * 4) + 255) // 256 * 256) + stats
+
+
+def test_cross_validation(lib):
+    d = good_desc()
+    assert cross_fwd(lib, d, None) == INVALID                             # no key strides
+    assert cross_fwd(lib, d, good_keys(bt_stride_n=100)) == INVALID       # not 16-byte rows
+    assert cross_fwd(lib, d, good_keys(bs_stride_n=64)) == INVALID        # overlapping rows
+    assert cross_fwd(lib, d, good_keys(), rope=_RopeDesc(FAKE, None, None, None)) == INVALID
+    need = lib.lard_relkl_cross_reserve_size(ctypes.byref(d), None)
+    assert cross_fwd(lib, d, good_keys(), nrs=need - 1) == WS_SMALL
+    assert cross_bwd(lib, d, nrs=need - 1) == WS_SMALL
+    assert cross_bwd(lib, d, db=None) == INVALID
+    assert cross_bwd(lib, d, da=FAKE + 8) == INVALID                      # misaligned gradient
+    bad = _GradDesc(dtype=1, reserved=0, stride_b=4 * 100 * 128, stride_h=100 * 128, stride_n=130)
+    assert cross_bwd(lib, d, gb=bad) == INVALID
+    g16 = _GradDesc(dtype=1, reserved=0, stride_b=4 * 100 * 128, stride_h=100 * 128, stride_n=128)
+    assert cross_bwd(lib, good_desc(dtype=0), ga=g16) == UNSUPPORTED      # fp32 -> bf16 grad
+
+
+def test_cross_fault_injection_maps_to_hip_error(lib, monkeypatch):
+    monkeypatch.setenv("LARD_FAULT_INJECT", "1")
+    assert cross_fwd(lib, good_desc(), good_keys()) == HIP
+    assert cross_bwd(lib, good_desc()) == HIP
+
+
+def test_cross_python_layer_checks_shapes():
+    a = torch.zeros(1, 1, 8, 64)
+    with pytest.raises(relkl.LardError):
+        relkl.cross_relkl_fwd(a, torch.zeros(1, 1, 9, 64), a, a)
+    with pytest.raises(RuntimeError, match="GPU"):
+        relkl.cross_relkl_fwd(a, a, a, a)

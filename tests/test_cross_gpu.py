@@ -1,0 +1,158 @@
+"""GPU parity of the cross-relation entry points (lard_relkl_cross_fwd / _bwd through the
+C ABI) with the float64 oracle (``oracle.cross``): seeded A (queries) and B (keys) per side
+at sizes with ragged tails over several row and key tiles, edge sizes, A = B against the
+relation path, the attention map of the 4K recipe with RoPE inside the call, split-K
+invariance, head maps and the autograd function.  Gates are the relation path's, applied
+to the loss and to each of dA_s and dB_s."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import cross, rope
+from attention_relation_distillation_amd import relkl, workloads
+from tests._gpu import (GRAD_RL2, LOSS_RTOL, banner, device, fp32_floor, np64, rel_l2)
+
+pytestmark = pytest.mark.gpu
+
+
+def quad(b, h, n, d, dtype, seed, noise=0.2):
+    g = torch.Generator().manual_seed(seed)
+    a = torch.randn((b, h, n, d), generator=g)
+    k = torch.randn((b, h, n, d), generator=g)
+    a_s = a + noise * torch.randn((b, h, n, d), generator=g)
+    k_s = k + noise * torch.randn((b, h, n, d), generator=g)
+    return [t.to(dtype) for t in (a, k, a_s, k_s)]
+
+
+def gpu_cross(a_t, b_t, a_s, b_s, causal, tabs=None, head_map=None, dx_dtype=None, g=1.0,
+              da=None, db=None):
+    dev = device()
+    ts = [t.to(dev) for t in (a_t, b_t, a_s, b_s)]
+    rp = None if tabs is None else [None if t is None else t.to(dev).contiguous() for t in tabs]
+    f = relkl.cross_relkl_fwd(*ts, rope=rp, causal=causal, head_map=head_map, want_row_kl=True)
+    gl = torch.tensor(g, dtype=torch.float32, device=dev)
+    da, db = relkl.cross_relkl_bwd(ts[2], ts[3], f["reserve"], gl, rope=rp, causal=causal,
+                                   head_map=head_map, dx_dtype=dx_dtype, da=da, db=db)
+    torch.cuda.synchronize()
+    return f, da, db
+
+
+def oracle_cross(a_t, b_t, a_s, b_s, causal, tabs=None, head_map=None, g=1.0):
+    s = oracle.default_scale(a_t.shape[-1])
+    v = [np64(t) for t in (a_t, b_t, a_s, b_s)]
+    if tabs is not None:
+        dt = "bf16" if a_t.dtype == torch.bfloat16 else "fp32"
+        ct, st, cs, ss = [None if t is None else t.double().numpy() for t in tabs]
+        v = [rope.rotate_in_dtype(v[0], ct, st, dt), rope.rotate_in_dtype(v[1], ct, st, dt),
+             rope.rotate_in_dtype(v[2], cs, ss, dt), rope.rotate_in_dtype(v[3], cs, ss, dt)]
+    fo = cross.forward(*v, s, causal, head_map=head_map)
+    da, db = cross.backward(*v, s, causal, g, head_map=head_map)
+    if tabs is not None:
+        da, db = rope.rotate_back(da, cs, ss), rope.rotate_back(db, cs, ss)
+    return fo, da, db
+
+
+def check(f, da, db, fo, dao, dbo, dtype, label, floors=None):
+    loss = float(f["loss"].item())
+    lerr = abs(loss - fo["loss"])
+    ea, eb = np.linalg.norm(np64(da) - dao), np.linalg.norm(np64(db) - dbo)
+    lse = max(float(np.max(np.abs(np64(f["lse_t"]) - fo["lse_t"]))),
+              float(np.max(np.abs(np64(f["lse_s"]) - fo["lse_s"]))))
+    lf, gf = (0.0, 0.0) if floors is None else floors
+    diag = dict(loss=loss, ref=fo["loss"], loss_rel=lerr / max(abs(fo["loss"]), 1e-30),
+                da_rl2=rel_l2(np64(da), dao), db_rl2=rel_l2(np64(db), dbo), lse_abs=lse)
+    print(f"[parity] cross {label} {diag}", flush=True)
+    assert lerr <= LOSS_RTOL[dtype] * abs(fo["loss"]) + lf, diag
+    assert ea <= GRAD_RL2[dtype] * np.linalg.norm(dao) + gf, diag
+    assert eb <= GRAD_RL2[dtype] * np.linalg.norm(dbo) + gf, diag
+    assert lse <= 5e-5 * max(1.0, float(np.max(np.abs(fo["lse_t"])))), diag
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("n", [1, 2, 65, 257, 700])
+def test_cross_sizes(n, causal, d, dtype):
+    banner(f"cross N={n} d={d} causal={causal} {dtype}")
+    a_t, b_t, a_s, b_s = quad(1, 2, n, d, dtype, seed=n * 13 + d)
+    f, da, db = gpu_cross(a_t, b_t, a_s, b_s, causal, dx_dtype=torch.float32)
+    fo, dao, dbo = oracle_cross(a_t, b_t, a_s, b_s, causal)
+    floors = fp32_floor(fo, a_s, oracle.default_scale(d))
+    check(f, da, db, fo, dao, dbo, dtype, f"N={n}", floors)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_cross_equal_operands_is_the_relation(dtype):
+    """A = B: the cross loss is the relation loss, and dA + dB is the relation gradient."""
+    banner(f"cross A = B {dtype}")
+    dev = device()
+    g = torch.Generator().manual_seed(31)
+    x = torch.randn((1, 2, 333, 128), generator=g)
+    x_t, x_s = x.to(dtype), (x + 0.1 * torch.randn(x.shape, generator=g)).to(dtype)
+    f, da, db = gpu_cross(x_t, x_t, x_s, x_s, True, dx_dtype=torch.float32)
+    fp = relkl.relkl_fwd(x_t.to(dev), x_s.to(dev), causal=True)
+    dp = relkl.relkl_bwd(x_t.to(dev), x_s.to(dev), fp["reserve"], torch.ones((), device=dev),
+                         causal=True, dx_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert abs(float(f["loss"].item()) - float(fp["loss"].item())) <= 1e-6 * float(fp["loss"].item())
+    assert rel_l2(np64(da) + np64(db), np64(dp)) <= 1e-5
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_cross_attention_map_with_rope(causal):
+    """Attention maps softmax(Q K^T / sqrt(d)) of the 4K recipe (teacher native RoPE,
+    student position interpolation 8x), rotated inside the call, gradients to the student's
+    pre-RoPE Q and K."""
+    banner(f"cross attention map + RoPE causal={causal}")
+    rels = {r.name: r for r in workloads.make_rope_inputs("llama2_4k", N=900, Hq=2, Hkv=2,
+                                                           relations=("qq", "kk"))}
+    q, k = rels["qq"], rels["kk"]
+    tabs = (q.cos_t, q.sin_t, q.cos_s, q.sin_s)
+    f, da, db = gpu_cross(q.x_t, k.x_t, q.x_s, k.x_s, causal, tabs=tabs)
+    fo, dao, dbo = oracle_cross(q.x_t, k.x_t, q.x_s, k.x_s, causal, tabs=tabs)
+    check(f, da, db, fo, dao, dbo, torch.bfloat16, f"qk rope c{int(causal)}")
+
+
+def test_cross_split_invariant(monkeypatch):
+    banner("cross split-K")
+    a_t, b_t, a_s, b_s = quad(1, 1, 600, 128, torch.bfloat16, seed=41)
+    outs = []
+    for s in ("1", "3", "7"):
+        monkeypatch.setenv("LARD_SPLITK", s)
+        _, da, db = gpu_cross(a_t, b_t, a_s, b_s, True, dx_dtype=torch.float32)
+        outs.append((np64(da), np64(db)))
+    for da, db in outs[1:]:
+        assert rel_l2(da, outs[0][0]) < 1e-6 and rel_l2(db, outs[0][1]) < 1e-6
+    fo, dao, dbo = oracle_cross(a_t, b_t, a_s, b_s, True)
+    assert rel_l2(outs[1][0], dao) <= 1e-3 and rel_l2(outs[1][1], dbo) <= 1e-3
+
+
+def test_cross_head_map_and_untouched_heads():
+    banner("cross head_map")
+    dev = device()
+    a_t, b_t, a_s, b_s = quad(1, 4, 300, 64, torch.bfloat16, seed=43)
+    hm = [3, 1]
+    sa = torch.full(a_s.shape, 5.0, dtype=torch.float32, device=dev)
+    sb = torch.full(b_s.shape, 6.0, dtype=torch.float32, device=dev)
+    f, _, _ = gpu_cross(a_t, b_t, a_s, b_s, True, head_map=hm, da=sa, db=sb)
+    fo, dao, dbo = oracle_cross(a_t[:, hm], b_t[:, hm], a_s[:, hm], b_s[:, hm], True)
+    assert abs(float(f["loss"].item()) - fo["loss"]) <= 1e-4 * fo["loss"]
+    ga, gb = np64(sa), np64(sb)
+    assert rel_l2(ga[:, hm], dao) <= 1e-3 and rel_l2(gb[:, hm], dbo) <= 1e-3
+    assert np.all(ga[:, [0, 2]] == 5.0) and np.all(gb[:, [0, 2]] == 6.0)
+
+
+def test_cross_autograd_function():
+    banner("cross autograd")
+    dev = device()
+    a_t, b_t, a_s, b_s = quad(1, 2, 200, 64, torch.float32, seed=47)
+    xa = a_s.clone().to(dev).requires_grad_(True)
+    xb = b_s.clone().to(dev).requires_grad_(True)
+    loss = relkl.cross_relation_kl(a_t.to(dev), b_t.to(dev), xa, xb, causal=True)
+    (1.5 * loss).backward()
+    fo, dao, dbo = oracle_cross(a_t, b_t, a_s, b_s, True, g=1.5)
+    assert float(loss.item()) == pytest.approx(fo["loss"], rel=1e-5)
+    assert rel_l2(np64(xa.grad), dao) <= GRAD_RL2[torch.float32]
+    assert rel_l2(np64(xb.grad), dbo) <= GRAD_RL2[torch.float32]
