@@ -209,3 +209,34 @@ def test_growing_row_maximum(causal, d, dtype):
     f, dx = gpu_fwd_bwd(x_t, x_s, causal)
     fo, dxo = oracle_fwd_bwd(x_t, x_s, causal)
     assert_parity(f, dx, fo, dxo, dtype, "growing", x_s=x_s, scale=oracle.default_scale(d))
+
+
+def test_relations_in_one_call_through_a_fused_qkv_buffer():
+    """Q/Q, K/K and V/V of equal head counts in one launch: a fused projection buffer
+    [N, 3, H, d] viewed as [3, H, N, d] (the batch index selects the relation) gives, in one
+    call, the sum of the three relation losses and each relation's gradient, bitwise equal
+    to three separate calls."""
+    banner("fused QKV buffer, one call")
+    dev = device()
+    rels = workloads.make_inputs("llama2_4k", N=500, Hq=2, Hkv=2)
+    H, N, d = 2, 500, 128
+    buf_t = torch.empty((N, 3, H, d), dtype=torch.bfloat16, device=dev)
+    buf_s = torch.empty_like(buf_t)
+    for k, r in enumerate(rels):
+        buf_t[:, k] = r.x_t[0].permute(1, 0, 2).to(dev)
+        buf_s[:, k] = r.x_s[0].permute(1, 0, 2).to(dev)
+    v_t, v_s = buf_t.permute(1, 2, 0, 3), buf_s.permute(1, 2, 0, 3)  # [3, H, N, d] views
+    assert v_t.stride() == (H * d, d, 3 * H * d, 1)
+    gl = torch.ones((), device=dev)
+    f = relkl.relkl_fwd(v_t, v_s, causal=True)
+    dx = relkl.relkl_bwd(v_t, v_s, f["reserve"], gl, causal=True, dx_dtype=torch.float32)
+    torch.cuda.synchronize()
+    total, parts = 0.0, []
+    for k, r in enumerate(rels):
+        xt, xs = r.x_t.to(dev), r.x_s.to(dev)
+        fk = relkl.relkl_fwd(xt, xs, causal=True)
+        dk = relkl.relkl_bwd(xt, xs, fk["reserve"], gl, causal=True, dx_dtype=torch.float32)
+        torch.cuda.synchronize()
+        total += float(fk["loss"].item())
+        assert torch.equal(dx[k], dk[0]), k
+    assert abs(float(f["loss"].item()) - total) <= 1e-6 * total
