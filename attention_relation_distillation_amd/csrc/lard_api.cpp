@@ -1,6 +1,10 @@
 // C ABI of the relation-KL library: host-side validation, workspace sizing and launch
 // configuration.  Every check runs before the first HIP call, so an invalid request never
 // touches the device.  The operation itself is documented in include/lard.h.
+//
+// Every entry point assembles "launches" (relkl_internal.h): one kernel launch covers one
+// or, for the grouped entry points, up to LARD_MAX_GROUP relation problems ("members").
+// The single-problem entry points are groups of one.
 
 #include <math.h>
 #include <stdlib.h>
@@ -13,11 +17,14 @@ namespace {
 
 using namespace lard;
 
-constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 1 * 100 + 0;
 constexpr int kTargetWorkgroups = 512;  // two rounds of one backward workgroup per CU
 constexpr int kMaxSplits = 64;
+constexpr float kLog2e = 1.4426950408889634f;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t round256(size_t v) { return (v + 255) / 256 * 256; }
 
 int elem_size(int dtype) { return dtype == LARD_BF16 ? 2 : 4; }
 
@@ -64,20 +71,22 @@ lard_status check_desc(const lard_relkl_desc* d) {
   return LARD_OK;
 }
 
-void fill_map(UnitMap& m, const lard_relkl_desc* d) {
-  for (int h = 0; h < d->H; ++h) m.head_map[h] = d->head_map ? d->head_map[h] : h;
-  for (int h = d->H; h < LARD_MAX_HEADS; ++h) m.head_map[h] = 0;
-}
-
 int row_tiles_of(const lard_relkl_desc* d) { return (d->N + kBR - 1) / kBR; }
 int bwd_row_tiles_of(const lard_relkl_desc* d) { return (d->N + kBRB - 1) / kBRB; }
 int key_tiles_of(const lard_relkl_desc* d) { return (d->N + kBC - 1) / kBC; }
+int64_t units_of(const lard_relkl_desc* d) { return (int64_t)d->B * d->H; }
 
-// Split the key range of the backward when the (unit, row tile) grid alone cannot fill
-// the chip.  Deterministic in the shape; LARD_SPLITK overrides it (clamped).
-int choose_splits(const lard_relkl_desc* d) {
-  const int64_t base = (int64_t)d->B * d->H * bwd_row_tiles_of(d);
-  const int kt = key_tiles_of(d);
+// Split the key range of the backward when the (unit, row tile) workgroups of a launch
+// alone cannot fill the chip.  Deterministic in the shapes; LARD_SPLITK overrides it
+// (clamped to the largest member's key tiles: a split with no key tile of a smaller
+// member writes zero partials).
+int choose_splits(int n, const lard_relkl_desc* const* d) {
+  int64_t base = 0;
+  int kt = 1;
+  for (int k = 0; k < n; ++k) {
+    base += units_of(d[k]) * bwd_row_tiles_of(d[k]);
+    if (key_tiles_of(d[k]) > kt) kt = key_tiles_of(d[k]);
+  }
   int s = 1;
   if (base < kTargetWorkgroups) s = (int)((kTargetWorkgroups + base - 1) / base);
   const char* env = getenv("LARD_SPLITK");
@@ -91,18 +100,36 @@ int choose_splits(const lard_relkl_desc* d) {
   return s;
 }
 
-size_t fwd_workspace(const lard_relkl_desc* d) {
-  const size_t n = (size_t)d->B * d->H * row_tiles_of(d);
-  return ((n * sizeof(double) + 255) / 256) * 256;
+// Forward: one fp64 loss partial per workgroup.
+int64_t fwd_partials(const lard_relkl_desc* d) { return units_of(d) * row_tiles_of(d); }
+
+size_t fwd_workspace(int n, const lard_relkl_desc* const* d) {
+  int64_t p = 0;
+  for (int k = 0; k < n; ++k) p += fwd_partials(d[k]);
+  return round256((size_t)p * sizeof(double));
 }
 
-ReserveLayout reserve_of(const lard_relkl_desc* d) {
-  return reserve_layout((int64_t)d->B * d->H, d->N, d->d, d->dtype == LARD_BF16 ? 2 : 0);
+// Backward: fp32 split-K partials [splits][units][row_tiles * kBRB][d] per member.
+size_t bwd_partial_floats(const lard_relkl_desc* d) {
+  return (size_t)units_of(d) * bwd_row_tiles_of(d) * kBRB * d->d;
 }
 
-// RoPE-fused entry points: rotated copies of both sides, fp16 (bf16 inputs) or fp32.
-ReserveLayout rope_reserve_of(const lard_relkl_desc* d) {
-  return reserve_layout((int64_t)d->B * d->H, d->N, d->d, d->dtype == LARD_BF16 ? 2 : 4);
+size_t bwd_workspace(int n, const lard_relkl_desc* const* d) {
+  const int s = choose_splits(n, d);
+  if (s == 1) return 0;
+  size_t f = 0;
+  for (int k = 0; k < n; ++k) f += bwd_partial_floats(d[k]);
+  return (size_t)s * f * sizeof(float);
+}
+
+// Reserve of one problem: plain (fp16 copies of bf16 inputs only), RoPE-fused (rotated
+// copies, fp16 or fp32) or cross (copies of A and B, fp16 or fp32).
+enum class Path { kPlain, kRope, kCross };
+
+ReserveLayout reserve_of(const lard_relkl_desc* d, Path p) {
+  const bool bf16 = d->dtype == LARD_BF16;
+  const int copy = p == Path::kPlain ? (bf16 ? 2 : 0) : (bf16 ? 2 : 4);
+  return reserve_layout(units_of(d), d->N, d->d, copy, p == Path::kCross);
 }
 
 // Tables of one side: both null (not rotated) or both set, 16-byte aligned.
@@ -117,11 +144,6 @@ lard_status check_rope(const lard_rope_desc* r) {
   const lard_status s = check_tables(r->cos_teacher, r->sin_teacher);
   if (s != LARD_OK) return s;
   return check_tables(r->cos_student, r->sin_student);
-}
-
-// Cross relation: rows of A_t, A_s, B_t, B_s copied (rotated when tables are given).
-ReserveLayout cross_reserve_of(const lard_relkl_desc* d) {
-  return reserve_layout((int64_t)d->B * d->H, d->N, d->d, d->dtype == LARD_BF16 ? 2 : 4, true);
 }
 
 lard_status check_cross(const lard_relkl_desc* d, const lard_cross_desc* k) {
@@ -145,35 +167,330 @@ lard_status check_grad(const lard_relkl_desc* desc, const lard_grad_desc* grad, 
   return LARD_OK;
 }
 
-// Backward launch plus the split-K reduction, writing one gradient.
-lard_status run_bwd(const lard_relkl_desc* desc, BwdArgs& a, const lard_grad_desc* grad,
-                    void* dx, int mode, void* stream) {
-  a.g_sb = grad->stride_b; a.g_sh = grad->stride_h; a.g_sn = grad->stride_n;
+// Forward outputs of one problem.
+lard_status check_fwd_outputs(const float* lse_t, const float* lse_s, const float* row_kl) {
+  if (!lse_t || !lse_s) return LARD_ERR_INVALID_ARGUMENT;
+  if (!aligned(lse_t, 4) || !aligned(lse_s, 4) || (row_kl && !aligned(row_kl, 4)))
+    return LARD_ERR_INVALID_ARGUMENT;
+  return LARD_OK;
+}
+
+lard_status check_inputs(const void* xt, const void* xs) {
+  if (!xt || !xs) return LARD_ERR_INVALID_ARGUMENT;
+  if (!aligned(xt, 16) || !aligned(xs, 16)) return LARD_ERR_INVALID_ARGUMENT;
+  return LARD_OK;
+}
+
+// ------------------------------------------------------------------ launch assembly
+// Head maps of the members of one call, in the table every launch of the call carries.
+struct MapTable {
+  int16_t v[kMapSlots];
+  int32_t off[kMaxGroup];
+};
+
+// False when the maps do not fit the table.
+bool build_maps(MapTable& t, int n, const lard_relkl_desc* const* d) {
+  memset(&t, 0, sizeof(t));
+  int used = 0;
+  for (int k = 0; k < n; ++k) {
+    if (!d[k]->head_map) {
+      t.off[k] = -1;
+      continue;
+    }
+    if (used + d[k]->H > kMapSlots) return false;
+    t.off[k] = used;
+    for (int h = 0; h < d[k]->H; ++h) t.v[used + h] = (int16_t)d[k]->head_map[h];
+    used += d[k]->H;
+  }
+  return true;
+}
+
+template <class M>
+void launch_init(Launch<M>& L) {
+  memset(&L, 0, sizeof(L));
+}
+
+// Appends a member of `count` workgroups (blocks) to L; returns its arguments.
+template <class M>
+M& add_member(Launch<M>& L, int count) {
+  M& m = L.m[L.n];
+  L.end[L.n] = (L.n ? L.end[L.n - 1] : 0) + count;
+  ++L.n;
+  return m;
+}
+
+// Input heads of members read in place go through the call's maps.
+template <class M>
+void use_maps(Launch<M>& L, const MapTable& t) {
+  memcpy(L.head_map, t.v, sizeof(t.v));
+  for (int k = 0; k < L.n; ++k) L.m[k].map_off = t.off[k];
+}
+
+// Dense [unit][N][d] copies in the reserve are read through the identity.
+template <class M>
+void identity_maps(Launch<M>& L) {
+  for (int k = 0; k < L.n; ++k) L.m[k].map_off = -1;
+}
+
+// Forward member: shape, statistics and outputs (operands set by the caller).
+void fwd_common(FwdArgs& a, const lard_relkl_desc* d, char* rb, const ReserveLayout& R,
+                bool write_copies, float* lse_t, float* lse_s, float* row_kl, double* partial) {
+  a.B = d->B; a.H = d->H; a.N = d->N;
+  a.row_tiles = row_tiles_of(d);
+  a.scale = d->scale;
+  a.c2 = d->scale * kLog2e;
+  a.lse_t = lse_t;
+  a.lse_s = lse_s;
+  a.row_kl = row_kl;
+  a.partial = partial;
+  a.npad = (int32_t)R.npad;
+  a.x16_t = write_copies ? reinterpret_cast<uint16_t*>(rb + R.x16_t) : nullptr;
+  a.x16_s = write_copies ? reinterpret_cast<uint16_t*>(rb + R.x16_s) : nullptr;
+  a.r_t = reinterpret_cast<float*>(rb + R.r_t);
+  a.r_s = reinterpret_cast<float*>(rb + R.r_s);
+}
+
+// Forward operands read in place from the caller's tensors.
+void fwd_inputs(FwdArgs& a, const lard_relkl_desc* d, const void* xt, const void* xs) {
+  a.x_t = xt;
+  a.x_s = xs;
+  a.t_sb = d->t_stride_b; a.t_sh = d->t_stride_h; a.t_sn = d->t_stride_n;
+  a.s_sb = d->s_stride_b; a.s_sh = d->s_stride_h; a.s_sn = d->s_stride_n;
+}
+
+// Forward operands from dense [unit][N][d] reserve copies; y: key-side copies or null.
+void fwd_copies(FwdArgs& a, const lard_relkl_desc* d, const char* xt, const char* xs,
+                const char* yt, const char* ys) {
+  a.x_t = xt;
+  a.x_s = xs;
+  a.y_t = yt;
+  a.y_s = ys;
+  const int64_t sn = d->d, sh = (int64_t)d->N * d->d, sb = (int64_t)d->H * sh;
+  a.t_sb = sb; a.t_sh = sh; a.t_sn = sn;
+  a.s_sb = sb; a.s_sh = sh; a.s_sn = sn;
+}
+
+// Rotation (or plain copy, for a side without tables) of one problem's inputs with the
+// given strides into dense reserve copies.
+void prep_member(PrepLaunch& P, const lard_relkl_desc* d, const void* xt, int64_t tsb,
+                 int64_t tsh, int64_t tsn, const void* xs, int64_t ssb, int64_t ssh,
+                 int64_t ssn, const lard_rope_desc* rope, void* ct, void* cs) {
+  const int64_t total = 2 * units_of(d) * d->N * (d->d / 8);
+  PrepArgs& p = add_member(P, (int)((total + 255) / 256));
+  p.x_t = xt;
+  p.x_s = xs;
+  p.t_sb = tsb; p.t_sh = tsh; p.t_sn = tsn;
+  p.s_sb = ssb; p.s_sh = ssh; p.s_sn = ssn;
+  p.B = d->B; p.H = d->H; p.N = d->N;
+  if (rope) {
+    p.cos_t = rope->cos_teacher; p.sin_t = rope->sin_teacher;
+    p.cos_s = rope->cos_student; p.sin_s = rope->sin_student;
+  }
+  p.c_t = ct;
+  p.c_s = cs;
+}
+
+// Backward member: shape, statistics, split and output (operands set by the caller).
+void bwd_common(BwdArgs& a, const lard_relkl_desc* d, const char* rb, const ReserveLayout& R,
+                int splits, const float* grad_loss, const lard_grad_desc* g, void* dx,
+                float* partial) {
+  a.B = d->B; a.H = d->H; a.N = d->N;
+  a.row_tiles = bwd_row_tiles_of(d);
+  a.key_tiles = key_tiles_of(d);
+  a.splits = splits;
+  a.scale = d->scale;
+  a.c2 = d->scale * kLog2e;
+  a.npad = (int32_t)R.npad;
+  a.r_t = reinterpret_cast<const float*>(rb + R.r_t);
+  a.r_s = reinterpret_cast<const float*>(rb + R.r_s);
+  a.rc_t = a.r_t;
+  a.rc_s = a.r_s;
+  a.grad_loss = grad_loss;
+  a.g_sb = g->stride_b; a.g_sh = g->stride_h; a.g_sn = g->stride_n;
   a.dx = dx;
-  const bool out_f32 = grad->dtype == LARD_FP32;
-  int e = launch_bwd(a, desc->dtype == LARD_BF16, desc->d, desc->causal == 1, out_f32, stream,
-                     mode);
+  a.partial = partial;
+}
+
+// Backward operands: the plain path (fp32 rows in place, fp16 copies for bf16 inputs).
+void bwd_inputs(BwdArgs& a, const lard_relkl_desc* d, const char* rb, const ReserveLayout& R,
+                const void* xt, const void* xs) {
+  a.x_t = xt;
+  a.x_s = xs;
+  a.t_sb = d->t_stride_b; a.t_sh = d->t_stride_h; a.t_sn = d->t_stride_n;
+  a.s_sb = d->s_stride_b; a.s_sh = d->s_stride_h; a.s_sn = d->s_stride_n;
+  const bool bf16 = d->dtype == LARD_BF16;
+  a.x16_t = bf16 ? reinterpret_cast<const uint16_t*>(rb + R.x16_t) : nullptr;
+  a.x16_s = bf16 ? reinterpret_cast<const uint16_t*>(rb + R.x16_s) : nullptr;
+  a.y16_t = a.x16_t;
+  a.y16_s = a.x16_s;
+}
+
+// Backward operands from dense reserve copies (own rows at own_*, staged rows at stg_*:
+// fp16 through x16_* / y16_*, fp32 through x_* / y_*).
+void bwd_copies(BwdArgs& a, const lard_relkl_desc* d, const char* rb, size_t own_t,
+                size_t own_s, size_t stg_t, size_t stg_s) {
+  const bool bf16 = d->dtype == LARD_BF16;
+  a.x_unit_dense = 1;
+  a.x_t = rb + own_t;
+  a.x_s = rb + own_s;
+  a.y_t = rb + stg_t;
+  a.y_s = rb + stg_s;
+  a.x16_t = bf16 ? reinterpret_cast<const uint16_t*>(rb + own_t) : nullptr;
+  a.x16_s = bf16 ? reinterpret_cast<const uint16_t*>(rb + own_s) : nullptr;
+  a.y16_t = bf16 ? reinterpret_cast<const uint16_t*>(rb + stg_t) : nullptr;
+  a.y16_s = bf16 ? reinterpret_cast<const uint16_t*>(rb + stg_s) : nullptr;
+}
+
+int bwd_workgroups(const lard_relkl_desc* d, int splits) {
+  return (int)(units_of(d) * bwd_row_tiles_of(d) * splits);
+}
+
+// Backward launch plus the split-K reduction of every member.
+lard_status run_bwd(const BwdLaunch& L, const lard_relkl_desc* const* d, bool out_f32,
+                    int mode, void* stream) {
+  const lard_relkl_desc* d0 = d[0];
+  int e = launch_bwd(L, d0->dtype == LARD_BF16, d0->d, d0->causal == 1, out_f32, stream, mode);
   if (e != 0) return LARD_ERR_HIP;
-  if (a.splits > 1) {
-    ReduceArgs r;
-    memset(&r, 0, sizeof(r));
-    r.partial = a.partial;
-    r.dx = dx;
-    r.g_sb = a.g_sb; r.g_sh = a.g_sh; r.g_sn = a.g_sn;
-    r.B = a.B; r.H = a.H; r.N = a.N; r.d = desc->d;
-    r.rows_pad = a.row_tiles * kBRB;
-    r.splits = a.splits;
-    r.map = a.map;
-    e = launch_splitk_reduce(r, out_f32, stream);
+  if (L.m[0].splits > 1) {
+    ReduceLaunch R;
+    launch_init(R);
+    for (int k = 0; k < L.n; ++k) {
+      const BwdArgs& a = L.m[k];
+      const int64_t total = units_of(d[k]) * d[k]->N * (d[k]->d / 4);
+      ReduceArgs& r = add_member(R, (int)((total + 255) / 256));
+      r.partial = a.partial;
+      r.dx = a.dx;
+      r.g_sb = a.g_sb; r.g_sh = a.g_sh; r.g_sn = a.g_sn;
+      r.B = a.B; r.H = a.H; r.N = a.N; r.d = d[k]->d;
+      r.rows_pad = a.row_tiles * kBRB;
+      r.splits = a.splits;
+      r.map_off = a.map_off;
+    }
+    memcpy(R.head_map, L.head_map, sizeof(R.head_map));
+    e = launch_splitk_reduce(R, out_f32, stream);
     if (e != 0) return LARD_ERR_HIP;
   }
   return LARD_OK;
 }
 
-size_t bwd_workspace(const lard_relkl_desc* d) {
-  const int s = choose_splits(d);
-  if (s == 1) return 0;
-  return (size_t)s * d->B * d->H * (size_t)bwd_row_tiles_of(d) * kBRB * d->d * sizeof(float);
+// Loss outputs of a forward launch whose members' partials start at `partial`.
+LossOut loss_out(const FwdLaunch& L, double* partial, float* total, float* const* member) {
+  LossOut o;
+  memset(&o, 0, sizeof(o));
+  o.partial = partial;
+  o.total = total;
+  o.n = L.n;
+  for (int k = 0; k < L.n; ++k) {
+    o.member[k] = member ? member[k] : nullptr;
+    o.begin[k + 1] = L.end[k];
+  }
+  return o;
+}
+
+// ------------------------------------------------------------------ grouped problems
+// Common requirements of a group: valid members that share dtype, d and mask, head maps
+// that fit one table, 32-bit work indices.
+lard_status check_group(int n, const lard_relkl_member* m, const lard_relkl_desc** d) {
+  if (n < 1 || !m) return LARD_ERR_INVALID_ARGUMENT;
+  if (n > LARD_MAX_GROUP) return LARD_ERR_UNSUPPORTED;
+  int64_t work = 0;
+  for (int k = 0; k < n; ++k) {
+    d[k] = &m[k].desc;
+    const lard_status s = check_desc(d[k]);
+    if (s != LARD_OK) return s;
+    if (d[k]->dtype != d[0]->dtype || d[k]->d != d[0]->d || d[k]->causal != d[0]->causal)
+      return LARD_ERR_INVALID_ARGUMENT;
+    work += units_of(d[k]) * row_tiles_of(d[k]);
+  }
+  if (work * kMaxSplits > 0x7fffffffLL) return LARD_ERR_UNSUPPORTED;
+  MapTable t;
+  if (!build_maps(t, n, d)) return LARD_ERR_UNSUPPORTED;
+  return LARD_OK;
+}
+
+size_t group_reserve(int n, const lard_relkl_desc* const* d, Path p, size_t* off) {
+  size_t total = 0;
+  for (int k = 0; k < n; ++k) {
+    if (off) off[k] = total;
+    total += reserve_of(d[k], p).total;
+  }
+  return total;
+}
+
+// Forward of n problems (plain or RoPE-fused) with reserve regions at rb + off[k].
+lard_status run_group_fwd(int n, const lard_relkl_desc* const* d, const void* const* xt,
+                          const void* const* xs, float* const* lse_t, float* const* lse_s,
+                          float* const* row_kl, float* const* member_loss,
+                          const lard_rope_desc* const* rope, bool with_rope, float* loss,
+                          char* rb, const size_t* off, double* partial, void* stream) {
+  const bool bf16 = d[0]->dtype == LARD_BF16;
+  const Path path = with_rope ? Path::kRope : Path::kPlain;
+  MapTable maps;
+  build_maps(maps, n, d);
+  if (with_rope) {
+    // 1. rotated copies of every member into its reserve region
+    PrepLaunch P;
+    launch_init(P);
+    for (int k = 0; k < n; ++k) {
+      const ReserveLayout R = reserve_of(d[k], path);
+      char* r = rb + off[k];
+      prep_member(P, d[k], xt[k], d[k]->t_stride_b, d[k]->t_stride_h, d[k]->t_stride_n, xs[k],
+                  d[k]->s_stride_b, d[k]->s_stride_h, d[k]->s_stride_n, rope[k], r + R.x16_t,
+                  r + R.x16_s);
+    }
+    use_maps(P, maps);
+    if (launch_rope_prep(P, bf16, d[0]->d, stream) != 0) return LARD_ERR_HIP;
+  }
+  // 2. the forward: in place (plain) or on the copies
+  FwdLaunch F;
+  launch_init(F);
+  double* part = partial;
+  for (int k = 0; k < n; ++k) {
+    const ReserveLayout R = reserve_of(d[k], path);
+    char* r = rb + off[k];
+    FwdArgs& a = add_member(F, (int)fwd_partials(d[k]));
+    if (with_rope) fwd_copies(a, d[k], r + R.x16_t, r + R.x16_s, nullptr, nullptr);
+    else fwd_inputs(a, d[k], xt[k], xs[k]);
+    fwd_common(a, d[k], r, R, !with_rope && bf16, lse_t[k], lse_s[k], row_kl[k], part);
+    part += fwd_partials(d[k]);
+  }
+  if (with_rope) identity_maps(F);
+  else use_maps(F, maps);
+  const LossOut lo = loss_out(F, partial, loss, member_loss);
+  const int e = launch_fwd(F, bf16, d[0]->d, d[0]->causal == 1, lo, stream,
+                           /*f16_copies=*/with_rope && bf16);
+  return e == 0 ? LARD_OK : LARD_ERR_HIP;
+}
+
+// Backward of n problems (plain or RoPE-fused), one gradient dtype.
+lard_status run_group_bwd(int n, const lard_relkl_desc* const* d, const void* const* xt,
+                          const void* const* xs, const lard_rope_desc* const* rope,
+                          bool with_rope, const char* rb, const size_t* off,
+                          const float* grad_loss, const lard_grad_desc* const* grad,
+                          void* const* dx, float* partial, void* stream) {
+  const Path path = with_rope ? Path::kRope : Path::kPlain;
+  const int splits = choose_splits(n, d);
+  MapTable maps;
+  build_maps(maps, n, d);
+  BwdLaunch L;
+  launch_init(L);
+  float* part = partial;
+  for (int k = 0; k < n; ++k) {
+    const ReserveLayout R = reserve_of(d[k], path);
+    const char* r = rb + off[k];
+    BwdArgs& a = add_member(L, bwd_workgroups(d[k], splits));
+    if (with_rope) {
+      bwd_copies(a, d[k], r, R.x16_t, R.x16_s, R.x16_t, R.x16_s);
+      a.rope_cos = rope[k] ? rope[k]->cos_student : nullptr;
+      a.rope_sin = rope[k] ? rope[k]->sin_student : nullptr;
+    } else {
+      bwd_inputs(a, d[k], r, R, xt[k], xs[k]);
+    }
+    bwd_common(a, d[k], r, R, splits, grad_loss, grad[k], dx[k], part);
+    if (splits > 1) part += (size_t)splits * bwd_partial_floats(d[k]);
+  }
+  use_maps(L, maps);  // output placement (and in-place operands of the plain path)
+  return run_bwd(L, d, grad[0]->dtype == LARD_FP32, 0, stream);
 }
 
 }  // namespace
@@ -198,14 +515,14 @@ size_t lard_relkl_workspace_size(const lard_relkl_desc* desc, int pass, lard_sta
   if (s == LARD_OK && pass != 0 && pass != 1) s = LARD_ERR_INVALID_ARGUMENT;
   if (status) *status = s;
   if (s != LARD_OK) return 0;
-  return pass == 0 ? fwd_workspace(desc) : bwd_workspace(desc);
+  return pass == 0 ? fwd_workspace(1, &desc) : bwd_workspace(1, &desc);
 }
 
 size_t lard_relkl_reserve_size(const lard_relkl_desc* desc, lard_status* status) {
   const lard_status s = check_desc(desc);
   if (status) *status = s;
   if (s != LARD_OK) return 0;
-  return reserve_of(desc).total;
+  return reserve_of(desc, Path::kPlain).total;
 }
 
 lard_status lard_relkl_fwd(const lard_relkl_desc* desc, const void* x_teacher,
@@ -214,40 +531,17 @@ lard_status lard_relkl_fwd(const lard_relkl_desc* desc, const void* x_teacher,
                            void* workspace, size_t workspace_bytes, void* stream) {
   lard_status s = check_desc(desc);
   if (s != LARD_OK) return s;
-  if (!x_teacher || !x_student || !lse_teacher || !lse_student || !loss || !workspace ||
-      !reserve)
+  if ((s = check_inputs(x_teacher, x_student)) != LARD_OK) return s;
+  if ((s = check_fwd_outputs(lse_teacher, lse_student, row_kl)) != LARD_OK) return s;
+  if (!loss || !workspace || !reserve) return LARD_ERR_INVALID_ARGUMENT;
+  if (!aligned(workspace, 8) || !aligned(reserve, 256) || !aligned(loss, 4))
     return LARD_ERR_INVALID_ARGUMENT;
-  if (!aligned(x_teacher, 16) || !aligned(x_student, 16) || !aligned(workspace, 8) ||
-      !aligned(reserve, 256) || !aligned(lse_teacher, 4) || !aligned(lse_student, 4) ||
-      !aligned(loss, 4) || (row_kl && !aligned(row_kl, 4)))
-    return LARD_ERR_INVALID_ARGUMENT;
-  if (workspace_bytes < fwd_workspace(desc)) return LARD_ERR_WORKSPACE_TOO_SMALL;
-  const ReserveLayout R = reserve_of(desc);
-  if (reserve_bytes < R.total) return LARD_ERR_WORKSPACE_TOO_SMALL;
-
-  FwdArgs a;
-  memset(&a, 0, sizeof(a));
-  a.x_t = x_teacher;
-  a.x_s = x_student;
-  a.t_sb = desc->t_stride_b; a.t_sh = desc->t_stride_h; a.t_sn = desc->t_stride_n;
-  a.s_sb = desc->s_stride_b; a.s_sh = desc->s_stride_h; a.s_sn = desc->s_stride_n;
-  a.B = desc->B; a.H = desc->H; a.N = desc->N;
-  a.row_tiles = row_tiles_of(desc);
-  a.scale = desc->scale;
-  a.c2 = desc->scale * 1.4426950408889634f;
-  a.lse_t = lse_teacher;
-  a.lse_s = lse_student;
-  a.row_kl = row_kl;
-  a.partial = static_cast<double*>(workspace);
-  char* rb = static_cast<char*>(reserve);
-  a.npad = (int32_t)R.npad;
-  a.x16_t = desc->dtype == LARD_BF16 ? reinterpret_cast<uint16_t*>(rb + R.x16_t) : nullptr;
-  a.x16_s = desc->dtype == LARD_BF16 ? reinterpret_cast<uint16_t*>(rb + R.x16_s) : nullptr;
-  a.r_t = reinterpret_cast<float*>(rb + R.r_t);
-  a.r_s = reinterpret_cast<float*>(rb + R.r_s);
-  fill_map(a.map, desc);
-  const int e = launch_fwd(a, desc->dtype == LARD_BF16, desc->d, desc->causal == 1, loss, stream);
-  return e == 0 ? LARD_OK : LARD_ERR_HIP;
+  if (workspace_bytes < fwd_workspace(1, &desc)) return LARD_ERR_WORKSPACE_TOO_SMALL;
+  if (reserve_bytes < reserve_of(desc, Path::kPlain).total) return LARD_ERR_WORKSPACE_TOO_SMALL;
+  const size_t off = 0;
+  return run_group_fwd(1, &desc, &x_teacher, &x_student, &lse_teacher, &lse_student, &row_kl,
+                       nullptr, nullptr, false, loss, static_cast<char*>(reserve), &off,
+                       static_cast<double*>(workspace), stream);
 }
 
 lard_status lard_relkl_bwd(const lard_relkl_desc* desc, const void* x_teacher,
@@ -257,73 +551,25 @@ lard_status lard_relkl_bwd(const lard_relkl_desc* desc, const void* x_teacher,
                            void* stream) {
   lard_status s = check_desc(desc);
   if (s != LARD_OK) return s;
-  if (!grad || !x_teacher || !x_student || !reserve || !grad_loss || !dx_student)
-    return LARD_ERR_INVALID_ARGUMENT;
-  if (grad->dtype != LARD_FP32 && grad->dtype != LARD_BF16) return LARD_ERR_INVALID_ARGUMENT;
-  if (grad->dtype == LARD_BF16 && desc->dtype != LARD_BF16) return LARD_ERR_UNSUPPORTED;
-  s = check_strides(grad->dtype, grad->stride_b, grad->stride_h, grad->stride_n);
-  if (s != LARD_OK) return s;
-  if (desc->N > 1 && grad->stride_n < desc->d) return LARD_ERR_INVALID_ARGUMENT;
-  if (!aligned(x_teacher, 16) || !aligned(x_student, 16) || !aligned(dx_student, 16) ||
-      !aligned(reserve, 256) || !aligned(grad_loss, 4))
-    return LARD_ERR_INVALID_ARGUMENT;
-  const ReserveLayout R = reserve_of(desc);
-  if (reserve_bytes < R.total) return LARD_ERR_WORKSPACE_TOO_SMALL;
-  const size_t need = bwd_workspace(desc);
+  if ((s = check_inputs(x_teacher, x_student)) != LARD_OK) return s;
+  if (!reserve || !grad_loss) return LARD_ERR_INVALID_ARGUMENT;
+  if ((s = check_grad(desc, grad, dx_student)) != LARD_OK) return s;
+  if (!aligned(reserve, 256) || !aligned(grad_loss, 4)) return LARD_ERR_INVALID_ARGUMENT;
+  if (reserve_bytes < reserve_of(desc, Path::kPlain).total) return LARD_ERR_WORKSPACE_TOO_SMALL;
+  const size_t need = bwd_workspace(1, &desc);
   if (need > 0 && (!workspace || !aligned(workspace, 16))) return LARD_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < need) return LARD_ERR_WORKSPACE_TOO_SMALL;
-
-  BwdArgs a;
-  memset(&a, 0, sizeof(a));
-  a.x_t = x_teacher;
-  a.x_s = x_student;
-  a.t_sb = desc->t_stride_b; a.t_sh = desc->t_stride_h; a.t_sn = desc->t_stride_n;
-  a.s_sb = desc->s_stride_b; a.s_sh = desc->s_stride_h; a.s_sn = desc->s_stride_n;
-  a.g_sb = grad->stride_b; a.g_sh = grad->stride_h; a.g_sn = grad->stride_n;
-  a.B = desc->B; a.H = desc->H; a.N = desc->N;
-  a.row_tiles = bwd_row_tiles_of(desc);
-  a.key_tiles = key_tiles_of(desc);
-  a.splits = choose_splits(desc);
-  a.scale = desc->scale;
-  a.c2 = desc->scale * 1.4426950408889634f;
-  const char* rb = static_cast<const char*>(reserve);
-  a.npad = (int32_t)R.npad;
-  a.x16_t = desc->dtype == LARD_BF16 ? reinterpret_cast<const uint16_t*>(rb + R.x16_t) : nullptr;
-  a.x16_s = desc->dtype == LARD_BF16 ? reinterpret_cast<const uint16_t*>(rb + R.x16_s) : nullptr;
-  a.y16_t = a.x16_t;
-  a.y16_s = a.x16_s;
-  a.r_t = reinterpret_cast<const float*>(rb + R.r_t);
-  a.r_s = reinterpret_cast<const float*>(rb + R.r_s);
-  a.rc_t = a.r_t;
-  a.rc_s = a.r_s;
-  a.grad_loss = grad_loss;
-  a.dx = dx_student;
-  a.partial = static_cast<float*>(workspace);
-  fill_map(a.map, desc);
-  const bool out_f32 = grad->dtype == LARD_FP32;
-  int e = launch_bwd(a, desc->dtype == LARD_BF16, desc->d, desc->causal == 1, out_f32, stream);
-  if (e != 0) return LARD_ERR_HIP;
-  if (a.splits > 1) {
-    ReduceArgs r;
-    memset(&r, 0, sizeof(r));
-    r.partial = a.partial;
-    r.dx = dx_student;
-    r.g_sb = a.g_sb; r.g_sh = a.g_sh; r.g_sn = a.g_sn;
-    r.B = a.B; r.H = a.H; r.N = a.N; r.d = desc->d;
-    r.rows_pad = a.row_tiles * kBRB;
-    r.splits = a.splits;
-    r.map = a.map;
-    e = launch_splitk_reduce(r, out_f32, stream);
-    if (e != 0) return LARD_ERR_HIP;
-  }
-  return LARD_OK;
+  const size_t off = 0;
+  return run_group_bwd(1, &desc, &x_teacher, &x_student, nullptr, false,
+                       static_cast<const char*>(reserve), &off, grad_loss, &grad, &dx_student,
+                       static_cast<float*>(workspace), stream);
 }
 
 size_t lard_relkl_rope_reserve_size(const lard_relkl_desc* desc, lard_status* status) {
   const lard_status s = check_desc(desc);
   if (status) *status = s;
   if (s != LARD_OK) return 0;
-  return rope_reserve_of(desc).total;
+  return reserve_of(desc, Path::kRope).total;
 }
 
 lard_status lard_relkl_rope_fwd(const lard_relkl_desc* desc, const lard_rope_desc* rope,
@@ -333,59 +579,18 @@ lard_status lard_relkl_rope_fwd(const lard_relkl_desc* desc, const lard_rope_des
                                 void* workspace, size_t workspace_bytes, void* stream) {
   lard_status s = check_desc(desc);
   if (s != LARD_OK) return s;
-  s = check_rope(rope);
-  if (s != LARD_OK) return s;
-  if (!x_teacher || !x_student || !lse_teacher || !lse_student || !loss || !workspace ||
-      !reserve)
+  if ((s = check_rope(rope)) != LARD_OK) return s;
+  if ((s = check_inputs(x_teacher, x_student)) != LARD_OK) return s;
+  if ((s = check_fwd_outputs(lse_teacher, lse_student, row_kl)) != LARD_OK) return s;
+  if (!loss || !workspace || !reserve) return LARD_ERR_INVALID_ARGUMENT;
+  if (!aligned(workspace, 8) || !aligned(reserve, 256) || !aligned(loss, 4))
     return LARD_ERR_INVALID_ARGUMENT;
-  if (!aligned(x_teacher, 16) || !aligned(x_student, 16) || !aligned(workspace, 8) ||
-      !aligned(reserve, 256) || !aligned(lse_teacher, 4) || !aligned(lse_student, 4) ||
-      !aligned(loss, 4) || (row_kl && !aligned(row_kl, 4)))
-    return LARD_ERR_INVALID_ARGUMENT;
-  if (workspace_bytes < fwd_workspace(desc)) return LARD_ERR_WORKSPACE_TOO_SMALL;
-  const ReserveLayout R = rope_reserve_of(desc);
-  if (reserve_bytes < R.total) return LARD_ERR_WORKSPACE_TOO_SMALL;
-  const bool bf16 = desc->dtype == LARD_BF16;
-  char* rb = static_cast<char*>(reserve);
-
-  // 1. rotated copies of both sides into the reserve
-  PrepArgs p;
-  memset(&p, 0, sizeof(p));
-  p.x_t = x_teacher;
-  p.x_s = x_student;
-  p.t_sb = desc->t_stride_b; p.t_sh = desc->t_stride_h; p.t_sn = desc->t_stride_n;
-  p.s_sb = desc->s_stride_b; p.s_sh = desc->s_stride_h; p.s_sn = desc->s_stride_n;
-  p.B = desc->B; p.H = desc->H; p.N = desc->N;
-  p.cos_t = rope->cos_teacher; p.sin_t = rope->sin_teacher;
-  p.cos_s = rope->cos_student; p.sin_s = rope->sin_student;
-  p.c_t = rb + R.x16_t;
-  p.c_s = rb + R.x16_s;
-  fill_map(p.map, desc);
-  int e = launch_rope_prep(p, bf16, desc->d, stream);
-  if (e != 0) return LARD_ERR_HIP;
-
-  // 2. the forward on the copies: dense [unit][N][d], read through the identity map
-  FwdArgs a;
-  memset(&a, 0, sizeof(a));
-  a.x_t = rb + R.x16_t;
-  a.x_s = rb + R.x16_s;
-  const int64_t sn = desc->d, sh = (int64_t)desc->N * desc->d, sb = (int64_t)desc->H * sh;
-  a.t_sb = sb; a.t_sh = sh; a.t_sn = sn;
-  a.s_sb = sb; a.s_sh = sh; a.s_sn = sn;
-  a.B = desc->B; a.H = desc->H; a.N = desc->N;
-  a.row_tiles = row_tiles_of(desc);
-  a.scale = desc->scale;
-  a.c2 = desc->scale * 1.4426950408889634f;
-  a.lse_t = lse_teacher;
-  a.lse_s = lse_student;
-  a.row_kl = row_kl;
-  a.partial = static_cast<double*>(workspace);
-  a.npad = (int32_t)R.npad;
-  a.r_t = reinterpret_cast<float*>(rb + R.r_t);
-  a.r_s = reinterpret_cast<float*>(rb + R.r_s);
-  for (int h = 0; h < LARD_MAX_HEADS; ++h) a.map.head_map[h] = h < desc->H ? h : 0;
-  e = launch_fwd(a, bf16, desc->d, desc->causal == 1, loss, stream, /*f16_copies=*/bf16);
-  return e == 0 ? LARD_OK : LARD_ERR_HIP;
+  if (workspace_bytes < fwd_workspace(1, &desc)) return LARD_ERR_WORKSPACE_TOO_SMALL;
+  if (reserve_bytes < reserve_of(desc, Path::kRope).total) return LARD_ERR_WORKSPACE_TOO_SMALL;
+  const size_t off = 0;
+  return run_group_fwd(1, &desc, &x_teacher, &x_student, &lse_teacher, &lse_student, &row_kl,
+                       nullptr, &rope, true, loss, static_cast<char*>(reserve), &off,
+                       static_cast<double*>(workspace), stream);
 }
 
 lard_status lard_relkl_rope_bwd(const lard_relkl_desc* desc, const lard_rope_desc* rope,
@@ -395,78 +600,26 @@ lard_status lard_relkl_rope_bwd(const lard_relkl_desc* desc, const lard_rope_des
                                 void* stream) {
   lard_status s = check_desc(desc);
   if (s != LARD_OK) return s;
-  s = check_rope(rope);
-  if (s != LARD_OK) return s;
-  if (!grad || !reserve || !grad_loss || !dx_student) return LARD_ERR_INVALID_ARGUMENT;
-  if (grad->dtype != LARD_FP32 && grad->dtype != LARD_BF16) return LARD_ERR_INVALID_ARGUMENT;
-  if (grad->dtype == LARD_BF16 && desc->dtype != LARD_BF16) return LARD_ERR_UNSUPPORTED;
-  s = check_strides(grad->dtype, grad->stride_b, grad->stride_h, grad->stride_n);
-  if (s != LARD_OK) return s;
-  if (desc->N > 1 && grad->stride_n < desc->d) return LARD_ERR_INVALID_ARGUMENT;
-  if (!aligned(dx_student, 16) || !aligned(reserve, 256) || !aligned(grad_loss, 4))
-    return LARD_ERR_INVALID_ARGUMENT;
-  const ReserveLayout R = rope_reserve_of(desc);
-  if (reserve_bytes < R.total) return LARD_ERR_WORKSPACE_TOO_SMALL;
-  const size_t need = bwd_workspace(desc);
+  if ((s = check_rope(rope)) != LARD_OK) return s;
+  if (!reserve || !grad_loss) return LARD_ERR_INVALID_ARGUMENT;
+  if ((s = check_grad(desc, grad, dx_student)) != LARD_OK) return s;
+  if (!aligned(reserve, 256) || !aligned(grad_loss, 4)) return LARD_ERR_INVALID_ARGUMENT;
+  if (reserve_bytes < reserve_of(desc, Path::kRope).total) return LARD_ERR_WORKSPACE_TOO_SMALL;
+  const size_t need = bwd_workspace(1, &desc);
   if (need > 0 && (!workspace || !aligned(workspace, 16))) return LARD_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < need) return LARD_ERR_WORKSPACE_TOO_SMALL;
-  const bool bf16 = desc->dtype == LARD_BF16;
-  const char* rb = static_cast<const char*>(reserve);
-
-  BwdArgs a;
-  memset(&a, 0, sizeof(a));
-  // operands: the rotated copies (fp16 through x16_*, fp32 through x_* read densely)
-  a.x_t = rb + R.x16_t;
-  a.x_s = rb + R.x16_s;
-  a.y_t = a.x_t;
-  a.y_s = a.x_s;
-  a.x_unit_dense = 1;
-  a.g_sb = grad->stride_b; a.g_sh = grad->stride_h; a.g_sn = grad->stride_n;
-  a.B = desc->B; a.H = desc->H; a.N = desc->N;
-  a.row_tiles = bwd_row_tiles_of(desc);
-  a.key_tiles = key_tiles_of(desc);
-  a.splits = choose_splits(desc);
-  a.scale = desc->scale;
-  a.c2 = desc->scale * 1.4426950408889634f;
-  a.npad = (int32_t)R.npad;
-  a.x16_t = bf16 ? reinterpret_cast<const uint16_t*>(rb + R.x16_t) : nullptr;
-  a.x16_s = bf16 ? reinterpret_cast<const uint16_t*>(rb + R.x16_s) : nullptr;
-  a.y16_t = a.x16_t;
-  a.y16_s = a.x16_s;
-  a.r_t = reinterpret_cast<const float*>(rb + R.r_t);
-  a.r_s = reinterpret_cast<const float*>(rb + R.r_s);
-  a.rc_t = a.r_t;
-  a.rc_s = a.r_s;
-  a.grad_loss = grad_loss;
-  a.rope_cos = rope->cos_student;
-  a.rope_sin = rope->sin_student;
-  a.dx = dx_student;
-  a.partial = static_cast<float*>(workspace);
-  fill_map(a.map, desc);  // output placement only: operands are read per unit
-  const bool out_f32 = grad->dtype == LARD_FP32;
-  int e = launch_bwd(a, bf16, desc->d, desc->causal == 1, out_f32, stream);
-  if (e != 0) return LARD_ERR_HIP;
-  if (a.splits > 1) {
-    ReduceArgs r;
-    memset(&r, 0, sizeof(r));
-    r.partial = a.partial;
-    r.dx = dx_student;
-    r.g_sb = a.g_sb; r.g_sh = a.g_sh; r.g_sn = a.g_sn;
-    r.B = a.B; r.H = a.H; r.N = a.N; r.d = desc->d;
-    r.rows_pad = a.row_tiles * kBRB;
-    r.splits = a.splits;
-    r.map = a.map;
-    e = launch_splitk_reduce(r, out_f32, stream);
-    if (e != 0) return LARD_ERR_HIP;
-  }
-  return LARD_OK;
+  const size_t off = 0;
+  const void* none = nullptr;
+  return run_group_bwd(1, &desc, &none, &none, &rope, true, static_cast<const char*>(reserve),
+                       &off, grad_loss, &grad, &dx_student, static_cast<float*>(workspace),
+                       stream);
 }
 
 size_t lard_relkl_cross_reserve_size(const lard_relkl_desc* desc, lard_status* status) {
   const lard_status s = check_desc(desc);
   if (status) *status = s;
   if (s != LARD_OK) return 0;
-  return cross_reserve_of(desc).total;
+  return reserve_of(desc, Path::kCross).total;
 }
 
 lard_status lard_relkl_cross_fwd(const lard_relkl_desc* desc, const lard_cross_desc* keys,
@@ -477,77 +630,46 @@ lard_status lard_relkl_cross_fwd(const lard_relkl_desc* desc, const lard_cross_d
                                  void* workspace, size_t workspace_bytes, void* stream) {
   lard_status s = check_desc(desc);
   if (s != LARD_OK) return s;
-  s = check_cross(desc, keys);
-  if (s != LARD_OK) return s;
-  if (rope) {
-    s = check_rope(rope);
-    if (s != LARD_OK) return s;
-  }
-  if (!a_teacher || !b_teacher || !a_student || !b_student || !lse_teacher || !lse_student ||
-      !loss || !workspace || !reserve)
+  if ((s = check_cross(desc, keys)) != LARD_OK) return s;
+  if (rope && (s = check_rope(rope)) != LARD_OK) return s;
+  if ((s = check_inputs(a_teacher, a_student)) != LARD_OK) return s;
+  if ((s = check_inputs(b_teacher, b_student)) != LARD_OK) return s;
+  if ((s = check_fwd_outputs(lse_teacher, lse_student, row_kl)) != LARD_OK) return s;
+  if (!loss || !workspace || !reserve) return LARD_ERR_INVALID_ARGUMENT;
+  if (!aligned(workspace, 8) || !aligned(reserve, 256) || !aligned(loss, 4))
     return LARD_ERR_INVALID_ARGUMENT;
-  if (!aligned(a_teacher, 16) || !aligned(b_teacher, 16) || !aligned(a_student, 16) ||
-      !aligned(b_student, 16) || !aligned(workspace, 8) || !aligned(reserve, 256) ||
-      !aligned(lse_teacher, 4) || !aligned(lse_student, 4) || !aligned(loss, 4) ||
-      (row_kl && !aligned(row_kl, 4)))
-    return LARD_ERR_INVALID_ARGUMENT;
-  if (workspace_bytes < fwd_workspace(desc)) return LARD_ERR_WORKSPACE_TOO_SMALL;
-  const ReserveLayout R = cross_reserve_of(desc);
+  if (workspace_bytes < fwd_workspace(1, &desc)) return LARD_ERR_WORKSPACE_TOO_SMALL;
+  const ReserveLayout R = reserve_of(desc, Path::kCross);
   if (reserve_bytes < R.total) return LARD_ERR_WORKSPACE_TOO_SMALL;
   const bool bf16 = desc->dtype == LARD_BF16;
   char* rb = static_cast<char*>(reserve);
+  MapTable maps;
+  build_maps(maps, 1, &desc);
 
-  // 1. copies (rotated when tables are given) of A and B of both sides
-  for (int side = 0; side < 2; ++side) {
-    PrepArgs p;
-    memset(&p, 0, sizeof(p));
-    p.B = desc->B; p.H = desc->H; p.N = desc->N;
-    if (rope) {
-      p.cos_t = rope->cos_teacher; p.sin_t = rope->sin_teacher;
-      p.cos_s = rope->cos_student; p.sin_s = rope->sin_student;
-    }
-    fill_map(p.map, desc);
-    if (side == 0) {
-      p.x_t = a_teacher;
-      p.x_s = a_student;
-      p.t_sb = desc->t_stride_b; p.t_sh = desc->t_stride_h; p.t_sn = desc->t_stride_n;
-      p.s_sb = desc->s_stride_b; p.s_sh = desc->s_stride_h; p.s_sn = desc->s_stride_n;
-      p.c_t = rb + R.x16_t;
-      p.c_s = rb + R.x16_s;
-    } else {
-      p.x_t = b_teacher;
-      p.x_s = b_student;
-      p.t_sb = keys->bt_stride_b; p.t_sh = keys->bt_stride_h; p.t_sn = keys->bt_stride_n;
-      p.s_sb = keys->bs_stride_b; p.s_sh = keys->bs_stride_h; p.s_sn = keys->bs_stride_n;
-      p.c_t = rb + R.y16_t;
-      p.c_s = rb + R.y16_s;
-    }
-    if (launch_rope_prep(p, bf16, desc->d, stream) != 0) return LARD_ERR_HIP;
-  }
+  // 1. copies (rotated when tables are given) of A and B of both sides: one launch with
+  //    A and B as two members of the same problem
+  PrepLaunch P;
+  launch_init(P);
+  prep_member(P, desc, a_teacher, desc->t_stride_b, desc->t_stride_h, desc->t_stride_n,
+              a_student, desc->s_stride_b, desc->s_stride_h, desc->s_stride_n, rope,
+              rb + R.x16_t, rb + R.x16_s);
+  prep_member(P, desc, b_teacher, keys->bt_stride_b, keys->bt_stride_h, keys->bt_stride_n,
+              b_student, keys->bs_stride_b, keys->bs_stride_h, keys->bs_stride_n, rope,
+              rb + R.y16_t, rb + R.y16_s);
+  memcpy(P.head_map, maps.v, sizeof(maps.v));
+  P.m[0].map_off = P.m[1].map_off = maps.off[0];
+  if (launch_rope_prep(P, bf16, desc->d, stream) != 0) return LARD_ERR_HIP;
 
   // 2. the forward: own rows from the A copies, key tiles from the B copies
-  FwdArgs a;
-  memset(&a, 0, sizeof(a));
-  a.x_t = rb + R.x16_t;
-  a.x_s = rb + R.x16_s;
-  a.y_t = rb + R.y16_t;
-  a.y_s = rb + R.y16_s;
-  const int64_t sn = desc->d, sh = (int64_t)desc->N * desc->d, sb = (int64_t)desc->H * sh;
-  a.t_sb = sb; a.t_sh = sh; a.t_sn = sn;
-  a.s_sb = sb; a.s_sh = sh; a.s_sn = sn;
-  a.B = desc->B; a.H = desc->H; a.N = desc->N;
-  a.row_tiles = row_tiles_of(desc);
-  a.scale = desc->scale;
-  a.c2 = desc->scale * 1.4426950408889634f;
-  a.lse_t = lse_teacher;
-  a.lse_s = lse_student;
-  a.row_kl = row_kl;
-  a.partial = static_cast<double*>(workspace);
-  a.npad = (int32_t)R.npad;
-  a.r_t = reinterpret_cast<float*>(rb + R.r_t);
-  a.r_s = reinterpret_cast<float*>(rb + R.r_s);
-  for (int h = 0; h < LARD_MAX_HEADS; ++h) a.map.head_map[h] = h < desc->H ? h : 0;
-  const int e = launch_fwd(a, bf16, desc->d, desc->causal == 1, loss, stream, /*f16_copies=*/bf16);
+  FwdLaunch F;
+  launch_init(F);
+  FwdArgs& a = add_member(F, (int)fwd_partials(desc));
+  fwd_copies(a, desc, rb + R.x16_t, rb + R.x16_s, rb + R.y16_t, rb + R.y16_s);
+  fwd_common(a, desc, rb, R, false, lse_teacher, lse_student, row_kl,
+             static_cast<double*>(workspace));
+  identity_maps(F);
+  const LossOut lo = loss_out(F, static_cast<double*>(workspace), loss, nullptr);
+  const int e = launch_fwd(F, bf16, desc->d, desc->causal == 1, lo, stream, /*f16_copies=*/bf16);
   return e == 0 ? LARD_OK : LARD_ERR_HIP;
 }
 
@@ -559,62 +681,140 @@ lard_status lard_relkl_cross_bwd(const lard_relkl_desc* desc, const lard_rope_de
                                  void* stream) {
   lard_status s = check_desc(desc);
   if (s != LARD_OK) return s;
-  if (rope) {
-    s = check_rope(rope);
-    if (s != LARD_OK) return s;
-  }
+  if (rope && (s = check_rope(rope)) != LARD_OK) return s;
   if (!reserve || !grad_loss) return LARD_ERR_INVALID_ARGUMENT;
-  s = check_grad(desc, grad_a, da_student);
-  if (s != LARD_OK) return s;
-  s = check_grad(desc, grad_b, db_student);
-  if (s != LARD_OK) return s;
+  if ((s = check_grad(desc, grad_a, da_student)) != LARD_OK) return s;
+  if ((s = check_grad(desc, grad_b, db_student)) != LARD_OK) return s;
   if (!aligned(reserve, 256) || !aligned(grad_loss, 4)) return LARD_ERR_INVALID_ARGUMENT;
-  const ReserveLayout R = cross_reserve_of(desc);
+  const ReserveLayout R = reserve_of(desc, Path::kCross);
   if (reserve_bytes < R.total) return LARD_ERR_WORKSPACE_TOO_SMALL;
-  const size_t need = bwd_workspace(desc);
+  const size_t need = bwd_workspace(1, &desc);
   if (need > 0 && (!workspace || !aligned(workspace, 16))) return LARD_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < need) return LARD_ERR_WORKSPACE_TOO_SMALL;
-  const bool bf16 = desc->dtype == LARD_BF16;
   const char* rb = static_cast<const char*>(reserve);
+  const int splits = choose_splits(1, &desc);
+  MapTable maps;
+  build_maps(maps, 1, &desc);
 
-  BwdArgs a;
-  memset(&a, 0, sizeof(a));
-  a.x_unit_dense = 1;
-  a.B = desc->B; a.H = desc->H; a.N = desc->N;
-  a.row_tiles = bwd_row_tiles_of(desc);
-  a.key_tiles = key_tiles_of(desc);
-  a.splits = choose_splits(desc);
-  a.scale = desc->scale;
-  a.c2 = desc->scale * 1.4426950408889634f;
-  a.npad = (int32_t)R.npad;
-  a.grad_loss = grad_loss;
-  a.partial = static_cast<float*>(workspace);
-  if (rope) {
-    a.rope_cos = rope->cos_student;
-    a.rope_sin = rope->sin_student;
-  }
-  fill_map(a.map, desc);  // output placement only: operands are read per unit
-  const float* qs_t = reinterpret_cast<const float*>(rb + R.r_t);  // query-row statistics
-  const float* qs_s = reinterpret_cast<const float*>(rb + R.r_s);
-  auto set_operands = [&](size_t own_t, size_t own_s, size_t stg_t, size_t stg_s) {
-    a.x_t = rb + own_t;
-    a.x_s = rb + own_s;
-    a.y_t = rb + stg_t;
-    a.y_s = rb + stg_s;
-    a.x16_t = bf16 ? reinterpret_cast<const uint16_t*>(rb + own_t) : nullptr;
-    a.x16_s = bf16 ? reinterpret_cast<const uint16_t*>(rb + own_s) : nullptr;
-    a.y16_t = bf16 ? reinterpret_cast<const uint16_t*>(rb + stg_t) : nullptr;
-    a.y16_s = bf16 ? reinterpret_cast<const uint16_t*>(rb + stg_s) : nullptr;
-    a.r_t = qs_t; a.r_s = qs_s;
-    a.rc_t = qs_t; a.rc_s = qs_s;
+  // Both passes use the statistics of the query rows (rows of A).
+  auto pass = [&](size_t own_t, size_t own_s, size_t stg_t, size_t stg_s,
+                  const lard_grad_desc* g, void* dx, int mode) {
+    BwdLaunch L;
+    launch_init(L);
+    BwdArgs& a = add_member(L, bwd_workgroups(desc, splits));
+    bwd_copies(a, desc, rb, own_t, own_s, stg_t, stg_s);
+    bwd_common(a, desc, rb, R, splits, grad_loss, g, dx, static_cast<float*>(workspace));
+    if (rope) {
+      a.rope_cos = rope->cos_student;
+      a.rope_sin = rope->sin_student;
+    }
+    use_maps(L, maps);  // output placement only: operands are read per unit
+    return run_bwd(L, &desc, g->dtype == LARD_FP32, mode, stream);
   };
   // dA: own rows of A, staged rows of B, row terms
-  set_operands(R.x16_t, R.x16_s, R.y16_t, R.y16_s);
-  s = run_bwd(desc, a, grad_a, da_student, 1, stream);
+  s = pass(R.x16_t, R.x16_s, R.y16_t, R.y16_s, grad_a, da_student, 1);
   if (s != LARD_OK) return s;
   // dB: own rows of B, staged rows of A with their statistics, column terms
-  set_operands(R.y16_t, R.y16_s, R.x16_t, R.x16_s);
-  return run_bwd(desc, a, grad_b, db_student, 2, stream);
+  return pass(R.y16_t, R.y16_s, R.x16_t, R.x16_s, grad_b, db_student, 2);
+}
+
+// ------------------------------------------------------------------ grouped entry points
+size_t lard_relkl_group_reserve_size(int n, const lard_relkl_member* members, int with_rope,
+                                     lard_status* status) {
+  const lard_relkl_desc* d[LARD_MAX_GROUP];
+  lard_status s = check_group(n, members, d);
+  if (s == LARD_OK && with_rope != 0 && with_rope != 1) s = LARD_ERR_INVALID_ARGUMENT;
+  if (status) *status = s;
+  if (s != LARD_OK) return 0;
+  return group_reserve(n, d, with_rope ? Path::kRope : Path::kPlain, nullptr);
+}
+
+size_t lard_relkl_group_workspace_size(int n, const lard_relkl_member* members, int pass,
+                                       lard_status* status) {
+  const lard_relkl_desc* d[LARD_MAX_GROUP];
+  lard_status s = check_group(n, members, d);
+  if (s == LARD_OK && pass != 0 && pass != 1) s = LARD_ERR_INVALID_ARGUMENT;
+  if (status) *status = s;
+  if (s != LARD_OK) return 0;
+  return pass == 0 ? fwd_workspace(n, d) : bwd_workspace(n, d);
+}
+
+lard_status lard_relkl_group_fwd(int n, const lard_relkl_member* members, int with_rope,
+                                 float* loss, void* reserve, size_t reserve_bytes,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  const lard_relkl_desc* d[LARD_MAX_GROUP];
+  lard_status s = check_group(n, members, d);
+  if (s != LARD_OK) return s;
+  if (with_rope != 0 && with_rope != 1) return LARD_ERR_INVALID_ARGUMENT;
+  const void* xt[LARD_MAX_GROUP];
+  const void* xs[LARD_MAX_GROUP];
+  float* lt[LARD_MAX_GROUP];
+  float* ls[LARD_MAX_GROUP];
+  float* kl[LARD_MAX_GROUP];
+  float* ml[LARD_MAX_GROUP];
+  const lard_rope_desc* rp[LARD_MAX_GROUP];
+  for (int k = 0; k < n; ++k) {
+    const lard_relkl_member& m = members[k];
+    if ((s = check_inputs(m.x_teacher, m.x_student)) != LARD_OK) return s;
+    if ((s = check_fwd_outputs(m.lse_teacher, m.lse_student, m.row_kl)) != LARD_OK) return s;
+    if (m.loss && !aligned(m.loss, 4)) return LARD_ERR_INVALID_ARGUMENT;
+    if (with_rope && (s = check_rope(&m.rope)) != LARD_OK) return s;
+    xt[k] = m.x_teacher;
+    xs[k] = m.x_student;
+    lt[k] = m.lse_teacher;
+    ls[k] = m.lse_student;
+    kl[k] = m.row_kl;
+    ml[k] = m.loss;
+    rp[k] = &m.rope;
+  }
+  if (!loss || !workspace || !reserve) return LARD_ERR_INVALID_ARGUMENT;
+  if (!aligned(workspace, 8) || !aligned(reserve, 256) || !aligned(loss, 4))
+    return LARD_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < fwd_workspace(n, d)) return LARD_ERR_WORKSPACE_TOO_SMALL;
+  size_t off[LARD_MAX_GROUP];
+  const Path path = with_rope ? Path::kRope : Path::kPlain;
+  if (reserve_bytes < group_reserve(n, d, path, off)) return LARD_ERR_WORKSPACE_TOO_SMALL;
+  return run_group_fwd(n, d, xt, xs, lt, ls, kl, ml, rp, with_rope == 1, loss,
+                       static_cast<char*>(reserve), off, static_cast<double*>(workspace),
+                       stream);
+}
+
+lard_status lard_relkl_group_bwd(int n, const lard_relkl_member* members, int with_rope,
+                                 const void* reserve, size_t reserve_bytes,
+                                 const float* grad_loss, const lard_grad_desc* grads,
+                                 void* const* dx_student, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  const lard_relkl_desc* d[LARD_MAX_GROUP];
+  lard_status s = check_group(n, members, d);
+  if (s != LARD_OK) return s;
+  if (with_rope != 0 && with_rope != 1) return LARD_ERR_INVALID_ARGUMENT;
+  if (!reserve || !grad_loss || !grads || !dx_student) return LARD_ERR_INVALID_ARGUMENT;
+  const void* xt[LARD_MAX_GROUP];
+  const void* xs[LARD_MAX_GROUP];
+  const lard_rope_desc* rp[LARD_MAX_GROUP];
+  const lard_grad_desc* g[LARD_MAX_GROUP];
+  void* dx[LARD_MAX_GROUP];
+  for (int k = 0; k < n; ++k) {
+    const lard_relkl_member& m = members[k];
+    if (!with_rope && (s = check_inputs(m.x_teacher, m.x_student)) != LARD_OK) return s;
+    if (with_rope && (s = check_rope(&m.rope)) != LARD_OK) return s;
+    if ((s = check_grad(d[k], &grads[k], dx_student[k])) != LARD_OK) return s;
+    if (grads[k].dtype != grads[0].dtype) return LARD_ERR_INVALID_ARGUMENT;
+    xt[k] = m.x_teacher;
+    xs[k] = m.x_student;
+    rp[k] = &m.rope;
+    g[k] = &grads[k];
+    dx[k] = dx_student[k];
+  }
+  if (!aligned(reserve, 256) || !aligned(grad_loss, 4)) return LARD_ERR_INVALID_ARGUMENT;
+  size_t off[LARD_MAX_GROUP];
+  const Path path = with_rope ? Path::kRope : Path::kPlain;
+  if (reserve_bytes < group_reserve(n, d, path, off)) return LARD_ERR_WORKSPACE_TOO_SMALL;
+  const size_t need = bwd_workspace(n, d);
+  if (need > 0 && (!workspace || !aligned(workspace, 16))) return LARD_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < need) return LARD_ERR_WORKSPACE_TOO_SMALL;
+  return run_group_bwd(n, d, xt, xs, rp, with_rope == 1, static_cast<const char*>(reserve),
+                       off, grad_loss, g, dx, static_cast<float*>(workspace), stream);
 }
 
 }  // extern "C"

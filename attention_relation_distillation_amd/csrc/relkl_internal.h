@@ -52,10 +52,6 @@ inline ReserveLayout reserve_layout(int64_t units, int64_t N, int64_t d, int cop
   return L;
 }
 
-struct UnitMap {
-  int32_t head_map[LARD_MAX_HEADS];
-};
-
 struct FwdArgs {
   const void* x_t;    // own (query-side) rows
   const void* x_s;
@@ -76,7 +72,7 @@ struct FwdArgs {
   uint16_t* x16_s;
   float* r_t;         // reserve log2 statistics
   float* r_s;
-  UnitMap map;
+  int32_t map_off;    // head map: offset in the launch's table, or -1 (identity)
 };
 
 struct BwdArgs {
@@ -108,7 +104,7 @@ struct BwdArgs {
   int32_t x_unit_dense;   // fp32 path: x_t / x_s are dense [unit][N][d] copies
   void* dx;            // final gradient (splits == 1)
   float* partial;      // [splits][B*H][row_tiles*kBR][d] (splits > 1)
-  UnitMap map;
+  int32_t map_off;
 };
 
 // Rotation of the inputs into the reserve for the RoPE-fused entry points.
@@ -124,7 +120,7 @@ struct PrepArgs {
   const float* sin_s;
   void* c_t;           // reserve copies, dense [units][N][d]
   void* c_s;
-  UnitMap map;
+  int32_t map_off;
 };
 
 struct ReduceArgs {
@@ -134,18 +130,50 @@ struct ReduceArgs {
   int32_t B, H, N, d;
   int32_t rows_pad;    // row_tiles * kBRB
   int32_t splits;
-  UnitMap map;
+  int32_t map_off;
+};
+
+// One launch covers up to kMaxGroup members (relation problems that share the dtype, d and
+// mask, e.g. Q/Q on the query heads and K/K, V/V on the KV heads of one layer).  The grid
+// is the members' workgroups (or blocks) back to back: member k takes [end[k-1], end[k]).
+// Head maps of all members sit in one table; member k's entries start at m[k].map_off.
+constexpr int kMaxGroup = LARD_MAX_GROUP;
+constexpr int kMapSlots = 512;
+
+template <class M>
+struct Launch {
+  M m[kMaxGroup];
+  int32_t n;
+  int32_t end[kMaxGroup];
+  int16_t head_map[kMapSlots];
+};
+using FwdLaunch = Launch<FwdArgs>;
+using BwdLaunch = Launch<BwdArgs>;
+using PrepLaunch = Launch<PrepArgs>;
+using ReduceLaunch = Launch<ReduceArgs>;
+static_assert(sizeof(BwdLaunch) <= 4096 && sizeof(FwdLaunch) <= 4096,
+              "a launch's arguments must fit the 4 KiB kernel-argument segment");
+
+// Where the forward's per-workgroup loss partials go: `total` receives the sum over every
+// member, member[k] (when non-null) the sum over member k's workgroups [begin[k],
+// begin[k+1]).  The partials of all members are contiguous.
+struct LossOut {
+  const double* partial;
+  float* total;
+  float* member[kMaxGroup];
+  int32_t begin[kMaxGroup + 1];
+  int32_t n;
 };
 
 // Each returns a hipError_t value (0 on success).  `in_bf16`: input dtype; `out_f32`:
 // gradient dtype (fp32 or the input dtype).
 // f16_copies: the inputs are the reserve's fp16 copies (RoPE-fused path, bf16 inputs).
-int launch_fwd(const FwdArgs& a, bool in_bf16, int d, bool causal, float* loss,
+int launch_fwd(const FwdLaunch& a, bool in_bf16, int d, bool causal, const LossOut& loss,
                void* stream, bool f16_copies = false);
 // mode: 0 relation gradient, 1 cross dA pass, 2 cross dB pass (see relkl_bwd_kernel).
-int launch_bwd(const BwdArgs& a, bool in_bf16, int d, bool causal, bool out_f32,
+int launch_bwd(const BwdLaunch& a, bool in_bf16, int d, bool causal, bool out_f32,
                void* stream, int mode = 0);
-int launch_splitk_reduce(const ReduceArgs& a, bool out_f32, void* stream);
-int launch_rope_prep(const PrepArgs& a, bool in_bf16, int d, void* stream);
+int launch_splitk_reduce(const ReduceLaunch& a, bool out_f32, void* stream);
+int launch_rope_prep(const PrepLaunch& a, bool in_bf16, int d, void* stream);
 
 }  // namespace lard

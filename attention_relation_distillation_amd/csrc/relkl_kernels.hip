@@ -117,6 +117,27 @@ __device__ __forceinline__ int xcd_remap(int g, int G) {
   return (g & 7) * (full >> 3) + (g >> 3);
 }
 
+// Member of a grouped launch that workgroup (or block) g belongs to, and g's index
+// inside it.  Wave-uniform: a few scalar compares.
+template <class M>
+__device__ __forceinline__ int member_of(const Launch<M>& L, int g) {
+  int k = 0;
+#pragma unroll
+  for (int q = 0; q < kMaxGroup - 1; ++q) k += (q + 1 < L.n && g >= L.end[q]) ? 1 : 0;
+  return k;
+}
+
+template <class M>
+__device__ __forceinline__ int member_begin(const Launch<M>& L, int k) {
+  return k == 0 ? 0 : L.end[k - 1];
+}
+
+// Input head of relation head h of a member.
+template <class M>
+__device__ __forceinline__ int head_of(const Launch<M>& L, int map_off, int h) {
+  return map_off < 0 ? h : (int)L.head_map[map_off + h];
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
@@ -406,7 +427,7 @@ __device__ __forceinline__ void score_pipeline(const char* tile_t, const char* t
 
 template <class In, int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
-void relkl_fwd_kernel(const FwdArgs a) {
+void relkl_fwd_kernel(const FwdLaunch L) {
   using elem_t = typename In::elem_t;
   using frag_t = typename In::frag_t;
   using G = Geo<D, In::kES>;
@@ -421,14 +442,17 @@ void relkl_fwd_kernel(const FwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31, hh = lane >> 5;
-  const int N = a.N;
 
-  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int g = xcd_remap(blockIdx.x, gridDim.x);
+  const int mi = member_of(L, g);
+  const FwdArgs& a = L.m[mi];
+  const int N = a.N;
+  const int w = g - member_begin(L, mi);
   const int unit = w / a.row_tiles;
   const int it = w - unit * a.row_tiles;
   const int I = CAUSAL ? (a.row_tiles - 1 - it) : it;  // longest causal rows first
   const int b = unit / a.H, h = unit - (unit / a.H) * a.H;
-  const int hin = a.map.head_map[h];
+  const int hin = head_of(L, a.map_off, h);
   const elem_t* xt = reinterpret_cast<const elem_t*>(a.x_t) + b * a.t_sb + hin * a.t_sh;
   const elem_t* xs = reinterpret_cast<const elem_t*>(a.x_s) + b * a.s_sb + hin * a.s_sh;
   // key-side rows: the same matrix for the relation, B for the cross relation (same layout)
@@ -548,19 +572,25 @@ void relkl_fwd_kernel(const FwdArgs a) {
   }
 }
 
-// Fixed-order fp64 reduction of the per-workgroup partial sums into the fp32 loss.
-__global__ __launch_bounds__(256) void loss_reduce_kernel(const double* partial, int count,
-                                                          float* loss) {
+// Fixed-order fp64 reduction of the per-workgroup partial sums into the fp32 loss: block 0
+// sums every member's partials into the total, block k >= 1 member k-1's into its own
+// loss (when requested).
+__global__ __launch_bounds__(256) void loss_reduce_kernel(const LossOut o) {
   __shared__ double red[256];
+  const int blk = blockIdx.x;
+  float* out = blk == 0 ? o.total : o.member[blk - 1];
+  if (out == nullptr) return;
+  const int lo = blk == 0 ? 0 : o.begin[blk - 1];
+  const int hi = blk == 0 ? o.begin[o.n] : o.begin[blk];
   double s = 0.0;
-  for (int k = threadIdx.x; k < count; k += 256) s += partial[k];
+  for (int k = lo + (int)threadIdx.x; k < hi; k += 256) s += o.partial[k];
   red[threadIdx.x] = s;
   __syncthreads();
   for (int off = 128; off >= 1; off >>= 1) {
     if ((int)threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
     __syncthreads();
   }
-  if (threadIdx.x == 0) loss[0] = (float)red[0];
+  if (threadIdx.x == 0) out[0] = (float)red[0];
 }
 
 // ------------------------------------------------------------------ backward
@@ -736,7 +766,7 @@ __device__ __forceinline__ void m_pipeline(const char* gtile, int jbg, const cha
 // vector work overlaps its SIMD partner's matrix work.
 template <class Op, int D, bool CAUSAL, bool OUT_F32, int MODE>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
-void relkl_bwd_kernel(const BwdArgs a) {
+void relkl_bwd_kernel(const BwdLaunch L) {
   using elem_t = typename Op::elem_t;
   using frag_t = typename Op::frag_t;
   using G = Geo<D, Op::kES>;
@@ -754,9 +784,12 @@ void relkl_bwd_kernel(const BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31, hh = lane >> 5;
-  const int N = a.N;
 
-  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int g = xcd_remap(blockIdx.x, gridDim.x);
+  const int mi = member_of(L, g);
+  const BwdArgs& a = L.m[mi];
+  const int N = a.N;
+  const int w = g - member_begin(L, mi);
   const int split = w % a.splits;
   const int wt = w / a.splits;
   const int unit = wt / a.row_tiles;
@@ -765,7 +798,7 @@ void relkl_bwd_kernel(const BwdArgs a) {
   const int I = (CAUSAL && MODE == 1) ? a.row_tiles - 1 - (wt - unit * a.row_tiles)
                                       : wt - unit * a.row_tiles;
   const int b = unit / a.H, h = unit - (unit / a.H) * a.H;
-  const int hin = a.map.head_map[h];
+  const int hin = head_of(L, a.map_off, h);
 
   // Operands: the fp16 reserve copies (dense [unit][N][D]) or the fp32 inputs; own rows
   // from x, staged key rows from y (the same matrix for the relation).
@@ -1018,8 +1051,10 @@ void relkl_bwd_kernel(const BwdArgs a) {
 
 // Fixed-order sum of the split-K partials into the gradient (one thread per 4 d-values).
 template <bool OUT_F32>
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(const ReduceArgs a) {
-  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const ReduceLaunch L) {
+  const int mi = member_of(L, (int)blockIdx.x);
+  const ReduceArgs& a = L.m[mi];
+  const int64_t q = (int64_t)((int)blockIdx.x - member_begin(L, mi)) * 256 + threadIdx.x;
   const int dq = a.d / 4;
   const int64_t total = (int64_t)a.B * a.H * a.N * dq;
   if (q >= total) return;
@@ -1028,7 +1063,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const ReduceArgs a) 
   const int i = (int)(rowlin % a.N);
   const int unit = (int)(rowlin / a.N);
   const int b = unit / a.H, h = unit % a.H;
-  const int hin = a.map.head_map[h];
+  const int hin = head_of(L, a.map_off, h);
   f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int c = 0; c < a.splits; ++c) {
     const float* p = a.partial + (((int64_t)c * a.B * a.H + unit) * a.rows_pad + i) * a.d + 4 * c4;
@@ -1056,9 +1091,11 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const ReduceArgs a) 
 // thread per (side, unit, row, group of 4 frequencies): consecutive threads cover
 // consecutive frequencies of one row, so each half-row is read and written in one run.
 template <bool IN_BF16, int D>
-__global__ __launch_bounds__(256) void rope_prep_kernel(const PrepArgs a) {
+__global__ __launch_bounds__(256) void rope_prep_kernel(const PrepLaunch L) {
   constexpr int G4 = D / 8;  // groups of 4 frequencies per row
-  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int mi = member_of(L, (int)blockIdx.x);
+  const PrepArgs& a = L.m[mi];
+  const int64_t q = (int64_t)((int)blockIdx.x - member_begin(L, mi)) * 256 + threadIdx.x;
   const int64_t per_side = (int64_t)a.B * a.H * a.N * G4;
   if (q >= 2 * per_side) return;
   const int side = (int)(q / per_side);
@@ -1068,7 +1105,7 @@ __global__ __launch_bounds__(256) void rope_prep_kernel(const PrepArgs a) {
   const int p = (int)(rowlin % a.N);
   const int unit = (int)(rowlin / a.N);
   const int b = unit / a.H, h = unit % a.H;
-  const int hin = a.map.head_map[h];
+  const int hin = head_of(L, a.map_off, h);
   const void* x = side ? a.x_s : a.x_t;
   const int64_t sb = side ? a.s_sb : a.t_sb, sh = side ? a.s_sh : a.t_sh;
   const int64_t sn = side ? a.s_sn : a.t_sn;
@@ -1126,18 +1163,23 @@ static bool fault_injected() {
   return v && v[0] == '1';
 }
 
+template <class M>
+static int grid_of(const Launch<M>& L) {
+  return L.n >= 1 ? L.end[L.n - 1] : 0;
+}
+
 template <class In, int D, bool CAUSAL>
-static int launch_fwd_t(const FwdArgs& a, float* loss, hipStream_t s) {
-  const int grid = a.B * a.H * a.row_tiles;
-  hipLaunchKernelGGL((relkl_fwd_kernel<In, D, CAUSAL>), dim3(grid), dim3(kThreads), 0, s, a);
+static int launch_fwd_t(const FwdLaunch& a, const LossOut& loss, hipStream_t s) {
+  hipLaunchKernelGGL((relkl_fwd_kernel<In, D, CAUSAL>), dim3(grid_of(a)), dim3(kThreads), 0, s,
+                     a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return (int)e;
-  hipLaunchKernelGGL(loss_reduce_kernel, dim3(1), dim3(256), 0, s, a.partial, grid, loss);
+  hipLaunchKernelGGL(loss_reduce_kernel, dim3(1 + loss.n), dim3(256), 0, s, loss);
   return (int)hipGetLastError();
 }
 
-int launch_fwd(const FwdArgs& a, bool in_bf16, int d, bool causal, float* loss, void* stream,
-               bool f16_copies) {
+int launch_fwd(const FwdLaunch& a, bool in_bf16, int d, bool causal, const LossOut& loss,
+               void* stream, bool f16_copies) {
   if (fault_injected()) return (int)hipErrorLaunchFailure;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (in_bf16 && f16_copies) {
@@ -1159,15 +1201,14 @@ int launch_fwd(const FwdArgs& a, bool in_bf16, int d, bool causal, float* loss, 
 }
 
 template <class Op, int D, bool CAUSAL, bool OUT_F32, int MODE>
-static int launch_bwd_t(const BwdArgs& a, hipStream_t s) {
-  const int grid = a.B * a.H * a.row_tiles * a.splits;
-  hipLaunchKernelGGL((relkl_bwd_kernel<Op, D, CAUSAL, OUT_F32, MODE>), dim3(grid),
+static int launch_bwd_t(const BwdLaunch& a, hipStream_t s) {
+  hipLaunchKernelGGL((relkl_bwd_kernel<Op, D, CAUSAL, OUT_F32, MODE>), dim3(grid_of(a)),
                      dim3(kBWaves * kWave), 0, s, a);
   return (int)hipGetLastError();
 }
 
 template <class Op, int D, int MODE>
-static int launch_bwd_d(const BwdArgs& a, bool causal, bool out_f32, hipStream_t s) {
+static int launch_bwd_d(const BwdLaunch& a, bool causal, bool out_f32, hipStream_t s) {
   if (causal) return out_f32 ? launch_bwd_t<Op, D, true, true, MODE>(a, s)
                              : launch_bwd_t<Op, D, true, false, MODE>(a, s);
   return out_f32 ? launch_bwd_t<Op, D, false, true, MODE>(a, s)
@@ -1175,7 +1216,7 @@ static int launch_bwd_d(const BwdArgs& a, bool causal, bool out_f32, hipStream_t
 }
 
 template <int MODE>
-static int launch_bwd_m(const BwdArgs& a, bool in_bf16, int d, bool causal, bool out_f32,
+static int launch_bwd_m(const BwdLaunch& a, bool in_bf16, int d, bool causal, bool out_f32,
                         hipStream_t s) {
   if (in_bf16) {
     return d == 128 ? launch_bwd_d<F16Op, 128, MODE>(a, causal, out_f32, s)
@@ -1186,7 +1227,7 @@ static int launch_bwd_m(const BwdArgs& a, bool in_bf16, int d, bool causal, bool
                   : launch_bwd_d<F32In, 64, MODE>(a, causal, true, s);
 }
 
-int launch_bwd(const BwdArgs& a, bool in_bf16, int d, bool causal, bool out_f32, void* stream,
+int launch_bwd(const BwdLaunch& a, bool in_bf16, int d, bool causal, bool out_f32, void* stream,
                int mode) {
   if (fault_injected()) return (int)hipErrorLaunchFailure;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -1195,30 +1236,27 @@ int launch_bwd(const BwdArgs& a, bool in_bf16, int d, bool causal, bool out_f32,
   return launch_bwd_m<0>(a, in_bf16, d, causal, out_f32, s);
 }
 
-int launch_rope_prep(const PrepArgs& a, bool in_bf16, int d, void* stream) {
+int launch_rope_prep(const PrepLaunch& a, bool in_bf16, int d, void* stream) {
   if (fault_injected()) return (int)hipErrorLaunchFailure;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const int64_t total = 2LL * a.B * a.H * a.N * (d / 8);
-  const int grid = (int)((total + 255) / 256);
+  const dim3 grid(grid_of(a));
   if (in_bf16) {
-    if (d == 128) hipLaunchKernelGGL((rope_prep_kernel<true, 128>), dim3(grid), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((rope_prep_kernel<true, 64>), dim3(grid), dim3(256), 0, s, a);
+    if (d == 128) hipLaunchKernelGGL((rope_prep_kernel<true, 128>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((rope_prep_kernel<true, 64>), grid, dim3(256), 0, s, a);
   } else {
-    if (d == 128) hipLaunchKernelGGL((rope_prep_kernel<false, 128>), dim3(grid), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((rope_prep_kernel<false, 64>), dim3(grid), dim3(256), 0, s, a);
+    if (d == 128) hipLaunchKernelGGL((rope_prep_kernel<false, 128>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((rope_prep_kernel<false, 64>), grid, dim3(256), 0, s, a);
   }
   return (int)hipGetLastError();
 }
 
-int launch_splitk_reduce(const ReduceArgs& a, bool out_f32, void* stream) {
+int launch_splitk_reduce(const ReduceLaunch& a, bool out_f32, void* stream) {
   if (fault_injected()) return (int)hipErrorLaunchFailure;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const int64_t total = (int64_t)a.B * a.H * a.N * (a.d / 4);
-  const int grid = (int)((total + 255) / 256);
   if (out_f32)
-    hipLaunchKernelGGL(splitk_reduce_kernel<true>, dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(splitk_reduce_kernel<true>, dim3(grid_of(a)), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3(grid_of(a)), dim3(256), 0, s, a);
   return (int)hipGetLastError();
 }
 

@@ -20,11 +20,14 @@ import torch
 __all__ = ["LardError", "library_path", "load_library", "relkl_fwd", "relkl_bwd",
            "relation_kl", "workspace_size", "reserve_size", "rope_reserve_size",
            "rope_relkl_fwd", "rope_relkl_bwd", "rope_relation_kl", "cross_reserve_size",
-           "cross_relkl_fwd", "cross_relkl_bwd", "cross_relation_kl", "LARD_MAX_HEADS"]
+           "cross_relkl_fwd", "cross_relkl_bwd", "cross_relation_kl", "group_reserve_size",
+           "group_workspace_size", "group_relkl_fwd", "group_relkl_bwd", "group_relation_kl",
+           "LARD_MAX_HEADS", "LARD_MAX_GROUP"]
 
 LARD_FP32 = 0
 LARD_BF16 = 1
 LARD_MAX_HEADS = 256
+LARD_MAX_GROUP = 4
 _STATUS_NAMES = {0: "LARD_OK", 1: "LARD_ERR_INVALID_ARGUMENT", 2: "LARD_ERR_UNSUPPORTED",
                  3: "LARD_ERR_WORKSPACE_TOO_SMALL", 4: "LARD_ERR_HIP"}
 
@@ -65,6 +68,16 @@ class _CrossDesc(ctypes.Structure):
         ("bt_stride_n", ctypes.c_int64),
         ("bs_stride_b", ctypes.c_int64), ("bs_stride_h", ctypes.c_int64),
         ("bs_stride_n", ctypes.c_int64),
+    ]
+
+
+class _Member(ctypes.Structure):
+    _fields_ = [
+        ("desc", _Desc),
+        ("x_teacher", ctypes.c_void_p), ("x_student", ctypes.c_void_p),
+        ("lse_teacher", ctypes.c_void_p), ("lse_student", ctypes.c_void_p),
+        ("row_kl", ctypes.c_void_p), ("loss", ctypes.c_void_p),
+        ("rope", _RopeDesc),
     ]
 
 
@@ -125,6 +138,16 @@ def load_library():
     lib.lard_relkl_cross_bwd.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(_RopeDesc), vp,
                                          sz, vp, ctypes.POINTER(_GradDesc), vp,
                                          ctypes.POINTER(_GradDesc), vp, vp, sz, vp]
+    mp, ci = ctypes.POINTER(_Member), ctypes.c_int
+    lib.lard_relkl_group_reserve_size.restype = sz
+    lib.lard_relkl_group_reserve_size.argtypes = [ci, mp, ci, ctypes.POINTER(ctypes.c_int)]
+    lib.lard_relkl_group_workspace_size.restype = sz
+    lib.lard_relkl_group_workspace_size.argtypes = [ci, mp, ci, ctypes.POINTER(ctypes.c_int)]
+    lib.lard_relkl_group_fwd.restype = ctypes.c_int
+    lib.lard_relkl_group_fwd.argtypes = [ci, mp, ci, vp, vp, sz, vp, sz, vp]
+    lib.lard_relkl_group_bwd.restype = ctypes.c_int
+    lib.lard_relkl_group_bwd.argtypes = [ci, mp, ci, vp, sz, vp, ctypes.POINTER(_GradDesc),
+                                         ctypes.POINTER(ctypes.c_void_p), vp, sz, vp]
     lib.lard_status_string.restype = ctypes.c_char_p
     lib.lard_status_string.argtypes = [ctypes.c_int]
     lib.lard_version.restype = ctypes.c_int
@@ -559,3 +582,176 @@ def cross_relation_kl(a_t: torch.Tensor, b_t: torch.Tensor, a_s: torch.Tensor,
     return _CrossRelationKL.apply(a_t.detach(), b_t.detach(), a_s, b_s,
                                   None if rope is None else tuple(rope), causal, scale,
                                   None if head_map is None else tuple(int(v) for v in head_map))
+
+
+# ------------------------------------------------------------------ grouped entry points
+def _group(pairs, causal, scale, head_maps, rope):
+    """ctypes members for [(x_t, x_s), ...]; head_maps and rope: None or one entry per member
+    (rope entries: None -- not rotated -- or (cos_t, sin_t, cos_s, sin_s))."""
+    pairs = [tuple(p) for p in pairs]
+    n = len(pairs)
+    if n < 1:
+        raise LardError(1, "a group needs at least one member")
+    if n > LARD_MAX_GROUP:
+        raise LardError(2, f"a group holds at most {LARD_MAX_GROUP} members")
+    if head_maps is not None and len(head_maps) != n:
+        raise LardError(1, "head_maps needs one entry per member")
+    if rope is not None and len(rope) != n:
+        raise LardError(1, "rope needs one entry per member")
+    members = (_Member * n)()
+    keep = []
+    for k, (x_t, x_s) in enumerate(pairs):
+        desc, kk = _make_desc(x_t, x_s, causal, scale, None if head_maps is None else head_maps[k])
+        keep.extend(kk)
+        members[k].desc = desc
+        members[k].x_teacher = x_t.data_ptr()
+        members[k].x_student = x_s.data_ptr()
+        if rope is not None and rope[k] is not None:
+            members[k].rope = _rope_desc(x_t, rope[k])
+    return members, keep, (0 if rope is None else 1)
+
+
+def group_reserve_size(pairs, *, causal=True, scale=None, head_maps=None, rope=None) -> int:
+    lib = load_library()
+    members, _keep, with_rope = _group(pairs, causal, scale, head_maps, rope)
+    st = ctypes.c_int(0)
+    n = lib.lard_relkl_group_reserve_size(len(members), members, with_rope, ctypes.byref(st))
+    _check(st.value)
+    return int(n)
+
+
+def group_workspace_size(pairs, *, causal=True, scale=None, head_maps=None, pass_: int = 0) -> int:
+    lib = load_library()
+    members, _keep, _ = _group(pairs, causal, scale, head_maps, None)
+    st = ctypes.c_int(0)
+    n = lib.lard_relkl_group_workspace_size(len(members), members, pass_, ctypes.byref(st))
+    _check(st.value)
+    return int(n)
+
+
+def group_relkl_fwd(pairs, *, causal: bool = True, scale: Optional[float] = None,
+                    head_maps=None, rope=None, want_row_kl: bool = False, stream=None):
+    """Forward of up to LARD_MAX_GROUP relation problems in one launch per kernel.
+
+    pairs: [(x_t, x_s), ...] with a shared dtype and d (B, H, N may differ); head_maps:
+    None or one head map (or None) per member; rope: None (post-rotation inputs) or one
+    entry per member, None or (cos_t, sin_t, cos_s, sin_s), rotating inside the call.
+    Returns dict(loss: 0-d fp32 sum over the members, member_loss: list of 0-d fp32,
+    lse_t, lse_s, row_kl: lists per member, reserve)."""
+    lib = load_library()
+    members, keep, with_rope = _group(pairs, causal, scale, head_maps, rope)
+    _require_gpu(pairs[0][0])
+    dev = pairs[0][0].device
+    # one allocation for all members' row vectors and losses; views per member
+    n = len(members)
+    sizes = [m.desc.B * m.desc.H * m.desc.N for m in members]
+    per = 3 if want_row_kl else 2
+    flat = torch.empty(per * sum(sizes) + n, dtype=torch.float32, device=dev)
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    out = {"lse_t": [], "lse_s": [], "row_kl": [], "member_loss": []}
+    off = 0
+    for k, m in enumerate(members):
+        shape = (m.desc.B, m.desc.H, m.desc.N)
+        views = []
+        for _ in range(per):
+            views.append(flat[off:off + sizes[k]].view(shape))
+            off += sizes[k]
+        lt, ls = views[0], views[1]
+        kl = views[2] if want_row_kl else None
+        m.lse_teacher, m.lse_student = lt.data_ptr(), ls.data_ptr()
+        m.row_kl = kl.data_ptr() if kl is not None else None
+        out["lse_t"].append(lt)
+        out["lse_s"].append(ls)
+        out["row_kl"].append(kl)
+    for k, m in enumerate(members):
+        ml = flat[off + k]
+        m.loss = ml.data_ptr()
+        out["member_loss"].append(ml)
+    st = ctypes.c_int(0)
+    ws_bytes = lib.lard_relkl_group_workspace_size(n, members, 0, ctypes.byref(st))
+    _check(st.value)
+    rs_bytes = lib.lard_relkl_group_reserve_size(n, members, with_rope, ctypes.byref(st))
+    _check(st.value)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    reserve = torch.empty(max(rs_bytes, 256), dtype=torch.uint8, device=dev)
+    _check(lib.lard_relkl_group_fwd(n, members, with_rope, loss.data_ptr(), reserve.data_ptr(),
+                                    reserve.numel(), ws.data_ptr(), ws.numel(),
+                                    _stream_handle(dev, stream)))
+    del keep
+    out["loss"] = loss
+    out["reserve"] = reserve
+    return out
+
+
+def group_relkl_bwd(pairs, reserve: torch.Tensor, grad_loss: torch.Tensor, *,
+                    causal: bool = True, scale: Optional[float] = None, head_maps=None,
+                    rope=None, dx=None, dx_dtype: Optional[torch.dtype] = None, stream=None):
+    """Gradients of grad_loss * (group loss) with respect to every member's x_s (a list);
+    arguments as given to group_relkl_fwd.  dx (optional): one output tensor per member."""
+    lib = load_library()
+    members, keep, with_rope = _group(pairs, causal, scale, head_maps, rope)
+    _require_gpu(pairs[0][0])
+    dev = pairs[0][0].device
+    if reserve.dtype != torch.uint8 or not reserve.is_contiguous() or reserve.device != dev:
+        raise LardError(1, "reserve must be the uint8 device buffer returned by group_relkl_fwd")
+    if (grad_loss.dtype != torch.float32 or grad_loss.numel() != 1 or grad_loss.device != dev):
+        raise LardError(1, "grad_loss must be a one-element fp32 tensor on the inputs' device")
+    grad_loss = grad_loss.contiguous()
+    n = len(members)
+    if dx is not None and len(dx) != n:
+        raise LardError(1, "dx needs one tensor per member")
+    outs = []
+    gdescs = (_GradDesc * n)()
+    ptrs = (ctypes.c_void_p * n)()
+    for k, (_, x_s) in enumerate(pairs):
+        hm = None if head_maps is None else head_maps[k]
+        g, gd = _new_grad(x_s, hm, members[k].desc.H_in, None if dx is None else dx[k], dx_dtype)
+        outs.append(g)
+        gdescs[k] = gd
+        ptrs[k] = g.data_ptr()
+    st = ctypes.c_int(0)
+    ws_bytes = lib.lard_relkl_group_workspace_size(n, members, 1, ctypes.byref(st))
+    _check(st.value)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    _check(lib.lard_relkl_group_bwd(n, members, with_rope, reserve.data_ptr(), reserve.numel(),
+                                    grad_loss.data_ptr(), gdescs, ptrs, ws.data_ptr(),
+                                    ws.numel(), _stream_handle(dev, stream)))
+    del keep
+    return outs
+
+
+class _GroupRelationKL(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, causal, scale, head_maps, rope, *xs):
+        pairs = [(xs[2 * k], xs[2 * k + 1]) for k in range(len(xs) // 2)]
+        out = group_relkl_fwd(pairs, causal=causal, scale=scale, head_maps=head_maps, rope=rope)
+        ctx.save_for_backward(*xs, out["reserve"])
+        ctx.causal, ctx.scale, ctx.head_maps, ctx.rope = causal, scale, head_maps, rope
+        return out["loss"]
+
+    @staticmethod
+    def backward(ctx, grad):
+        *xs, reserve = ctx.saved_tensors
+        pairs = [(xs[2 * k], xs[2 * k + 1]) for k in range(len(xs) // 2)]
+        g = grad if grad.dtype == torch.float32 else grad.float()
+        dxs = group_relkl_bwd(pairs, reserve, g, causal=ctx.causal, scale=ctx.scale,
+                              head_maps=ctx.head_maps, rope=ctx.rope)
+        grads = [None, None, None, None]
+        for dx in dxs:
+            grads.extend([None, dx])
+        return tuple(grads)
+
+
+def group_relation_kl(pairs, *, causal: bool = True, scale: Optional[float] = None,
+                      head_maps=None, rope=None):
+    """Sum of relation_kl over up to LARD_MAX_GROUP members [(x_t, x_s), ...] -- e.g. the
+    Q/Q, K/K and V/V relations of one layer, with GQA head counts -- computed by one launch
+    per kernel.  head_maps / rope: None or one entry per member (see group_relkl_fwd).
+    Differentiable with respect to every x_s."""
+    hm = None if head_maps is None else tuple(None if h is None else tuple(int(v) for v in h)
+                                              for h in head_maps)
+    rp = None if rope is None else tuple(None if r is None else tuple(r) for r in rope)
+    flat = []
+    for x_t, x_s in pairs:
+        flat.extend([x_t.detach(), x_s])
+    return _GroupRelationKL.apply(causal, scale, hm, rp, *flat)

@@ -238,6 +238,50 @@ def cross_timing(relkl, workloads, wl, dev, causal, steps, tokens):
                          "alg_flops_per_call": fl_b}}
 
 
+def group_timing(relkl, workloads, dev, steps):
+    """Every relation of a layer in one grouped call (one launch of each kernel) against one
+    call per relation, fwd + bwd per step: on the GQA shapes (Q/Q on 32 query heads, K/K and
+    V/V on 8 KV heads, N = 16384) and on the 4K LLaMA2 shapes, where each relation's grid is
+    small.  Two interleaved rounds of `steps` steps each; the faster round of each counts."""
+    import torch
+    gl = torch.ones((), dtype=torch.float32, device=dev)
+    res = {}
+    for name in ("gqa_16k", "llama2_4k"):
+        wl = workloads.WORKLOADS[name]
+        causal = wl.masks[0]
+        pairs = [(r.x_t.to(dev), r.x_s.to(dev)) for r in workloads.make_inputs(wl)]
+
+        def separate():
+            for xt, xs in pairs:
+                f = relkl.relkl_fwd(xt, xs, causal=causal)
+                relkl.relkl_bwd(xt, xs, f["reserve"], gl, causal=causal)
+
+        def grouped():
+            f = relkl.group_relkl_fwd(pairs, causal=causal)
+            relkl.group_relkl_bwd(pairs, f["reserve"], gl, causal=causal)
+
+        best = {}
+        for fn, label in ((separate, "separate"), (grouped, "group")) * 2:
+            fn()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                fn()
+            torch.cuda.synchronize()
+            ms = (time.perf_counter() - t0) * 1e3 / steps
+            best[label] = min(ms, best.get(label, float("inf")))
+        tokens = wl.B * wl.N
+        res[name] = {"heads": [p[0].shape[1] for p in pairs], "N": wl.N, "steps": steps,
+                     "separate_ms_per_step": round(best["separate"], 3),
+                     "group_ms_per_step": round(best["group"], 3),
+                     "group_tokens_per_s": round(tokens / (best["group"] / 1e3), 1),
+                     "separate_tokens_per_s": round(tokens / (best["separate"] / 1e3), 1),
+                     "speedup": round(best["separate"] / best["group"], 4)}
+        del pairs
+    return {"metric": "relation-KL fwd+bwd tokens/s, all relations of a layer in one grouped "
+                      "call vs one call per relation", **res}
+
+
 def stats_ms(v):
     return {"median": round(statistics.median(v), 3), "min": round(min(v), 3)}
 
@@ -257,6 +301,9 @@ def main():
     ap.add_argument("--cross-steps", type=int, default=5,
                     help="timed steps of the cross relation (attention maps Q K^T with RoPE "
                          "inside) on the same workload (0: skip)")
+    ap.add_argument("--group-steps", type=int, default=10,
+                    help="timed steps of the grouped call against per-relation calls on the "
+                         "GQA 16K and LLaMA2 4K shapes (0: skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="before the steps, copy a MIB-MiB buffer three times (a plain copy "
                          "kernel of known size, for scaling HBM byte counters)")
@@ -403,6 +450,11 @@ def main():
         out.setdefault("next_rows", {})["cross_attention_map"] = cross_timing(
             relkl, workloads, wl, dev, causal, args.cross_steps, tokens)
         print("[bench] cross-relation timing done", file=sys.stderr, flush=True)
+
+    if args.group_steps > 0:
+        out.setdefault("next_rows", {})["single_launch_group"] = group_timing(
+            relkl, workloads, dev, args.group_steps)
+        print("[bench] grouped-call timing done", file=sys.stderr, flush=True)
 
     if not args.no_mem_sweep:
         del gpu

@@ -9,7 +9,8 @@ import pytest
 import torch
 
 from attention_relation_distillation_amd import relkl
-from attention_relation_distillation_amd.relkl import _CrossDesc, _Desc, _GradDesc, _RopeDesc
+from attention_relation_distillation_amd.relkl import (_CrossDesc, _Desc, _GradDesc, _Member,
+                                                       _RopeDesc)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 OK, INVALID, UNSUPPORTED, WS_SMALL, HIP = 0, 1, 2, 3, 4
@@ -33,7 +34,9 @@ def test_exports_every_declared_symbol(lib):
                           "lard_relkl_reserve_size", "lard_status_string", "lard_version",
                           "lard_relkl_rope_reserve_size", "lard_relkl_rope_fwd",
                           "lard_relkl_rope_bwd", "lard_relkl_cross_reserve_size",
-                          "lard_relkl_cross_fwd", "lard_relkl_cross_bwd"}
+                          "lard_relkl_cross_fwd", "lard_relkl_cross_bwd",
+                          "lard_relkl_group_reserve_size", "lard_relkl_group_workspace_size",
+                          "lard_relkl_group_fwd", "lard_relkl_group_bwd"}
     for n in names:
         assert hasattr(lib, n), n
     assert lib.lard_version() >= 10000
@@ -313,3 +316,133 @@ def test_cross_python_layer_checks_shapes():
         relkl.cross_relkl_fwd(a, torch.zeros(1, 1, 9, 64), a, a)
     with pytest.raises(RuntimeError, match="GPU"):
         relkl.cross_relkl_fwd(a, a, a, a)
+
+
+# ------------------------------------------------------------------ grouped entry points
+def members_of(*descs, rope=None):
+    ms = (_Member * len(descs))()
+    for k, d in enumerate(descs):
+        ms[k].desc = d
+        ms[k].x_teacher = ms[k].x_student = FAKE
+        ms[k].lse_teacher = ms[k].lse_student = ms[k].loss = FAKE
+        ms[k].row_kl = None
+        if rope is not None:
+            ms[k].rope = rope
+    return ms
+
+
+def kv_desc(**kw):  # 2 KV heads of a GQA layer, N = 100
+    base = dict(H_in=2, H=2, t_stride_b=2 * 100 * 128, s_stride_b=2 * 100 * 128)
+    base.update(kw)
+    return good_desc(**base)
+
+
+def group_query(lib, fn, ms, arg):
+    st = ctypes.c_int(-1)
+    n = getattr(lib, fn)(len(ms), ms, arg, ctypes.byref(st))
+    return n, st.value
+
+
+def group_fwd(lib, ms, with_rope=0, rs=FAKE, nrs=1 << 30, n=None):
+    return lib.lard_relkl_group_fwd(len(ms) if n is None else n, ms, with_rope, FAKE, rs, nrs,
+                                    FAKE, 1 << 20, None)
+
+
+def group_bwd(lib, ms, grads=None, with_rope=0, nrs=1 << 30):
+    k = len(ms)
+    if grads is None:
+        grads = [_GradDesc(dtype=1, reserved=0, stride_b=m.desc.t_stride_b,
+                           stride_h=m.desc.t_stride_h, stride_n=128) for m in ms]
+    g = (_GradDesc * k)(*grads)
+    dx = (ctypes.c_void_p * k)(*([FAKE] * k))
+    return lib.lard_relkl_group_bwd(k, ms, with_rope, FAKE, nrs, FAKE, g, dx, FAKE, 1 << 30,
+                                    None)
+
+
+def test_group_sizes_are_the_sums_of_the_members(lib):
+    q, kv = good_desc(), kv_desc()
+    ms = members_of(q, kv, kv)
+    n, st = group_query(lib, "lard_relkl_group_reserve_size", ms, 0)
+    one = [lib.lard_relkl_reserve_size(ctypes.byref(d), None) for d in (q, kv, kv)]
+    assert st == OK and n == sum(one)
+    n, st = group_query(lib, "lard_relkl_group_reserve_size", ms, 1)
+    one = [lib.lard_relkl_rope_reserve_size(ctypes.byref(d), None) for d in (q, kv, kv)]
+    assert st == OK and n == sum(one)
+    # forward: one fp64 partial per workgroup of 128 rows, all members back to back
+    n, st = group_query(lib, "lard_relkl_group_workspace_size", ms, 0)
+    assert st == OK and n == ((8 * (4 + 2 + 2)) + 255) // 256 * 256
+    # backward: 8 (unit, row tile) workgroups in total -> the key range (2 tiles) is split
+    # in two, fp32 partials of 256 padded rows per unit
+    n, st = group_query(lib, "lard_relkl_group_workspace_size", ms, 1)
+    assert st == OK and n == 2 * (4 + 2 + 2) * 256 * 128 * 4
+    big = good_desc(N=32768, H_in=32, H=32, t_stride_h=32768 * 128, t_stride_b=32 * 32768 * 128,
+                    s_stride_h=32768 * 128, s_stride_b=32 * 32768 * 128)
+    n, st = group_query(lib, "lard_relkl_group_workspace_size", members_of(big, big), 1)
+    assert st == OK and n == 0
+    _, st = group_query(lib, "lard_relkl_group_workspace_size", ms, 2)
+    assert st == INVALID
+
+
+def test_group_validation(lib):
+    q, kv = good_desc(), kv_desc()
+    assert group_fwd(lib, members_of(q), n=0) == INVALID
+    five = members_of(q, q, q, q, q)
+    assert group_fwd(lib, five) == UNSUPPORTED                   # more than LARD_MAX_GROUP
+    assert group_fwd(lib, members_of(q, kv_desc(dtype=0))) == INVALID   # mixed dtype
+    assert group_fwd(lib, members_of(q, kv_desc(causal=0))) == INVALID  # mixed mask
+    d64 = kv_desc(d=64, t_stride_n=64, s_stride_n=64, t_stride_h=6400, s_stride_h=6400,
+                  t_stride_b=12800, s_stride_b=12800)
+    assert group_fwd(lib, members_of(q, d64)) == INVALID         # mixed d
+    assert group_fwd(lib, members_of(q, kv_desc(N=0))) == INVALID  # an invalid member
+    assert group_bwd(lib, members_of(q, kv_desc(d=96))) == UNSUPPORTED
+    assert group_fwd(lib, members_of(q, kv), with_rope=2) == INVALID
+    # with_rope = 1 checks every member's tables; with_rope = 0 does not read them
+    half = _RopeDesc(FAKE, None, None, None)
+    assert group_fwd(lib, members_of(q, kv, rope=half), with_rope=1, nrs=16) == INVALID
+    assert group_fwd(lib, members_of(q, kv, rope=half), with_rope=0, nrs=16) == WS_SMALL
+    # head maps of one group: at most 512 entries together
+    arr = (ctypes.c_int32 * 200)(*range(200))
+    hm = ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32))
+    wide = good_desc(H_in=256, H=200, head_map=hm, t_stride_b=256 * 100 * 128,
+                     s_stride_b=256 * 100 * 128)
+    n, st = group_query(lib, "lard_relkl_group_reserve_size", members_of(wide, wide), 0)
+    assert st == OK
+    n, st = group_query(lib, "lard_relkl_group_reserve_size", members_of(wide, wide, wide), 0)
+    assert st == UNSUPPORTED and n == 0
+    # reserve too small, gradients of two dtypes, missing pointers
+    need, _ = group_query(lib, "lard_relkl_group_reserve_size", members_of(q, kv), 0)
+    assert group_fwd(lib, members_of(q, kv), nrs=need - 1) == WS_SMALL
+    assert group_bwd(lib, members_of(q, kv), nrs=need - 1) == WS_SMALL
+    g16 = _GradDesc(dtype=1, reserved=0, stride_b=4 * 100 * 128, stride_h=100 * 128, stride_n=128)
+    g32 = _GradDesc(dtype=0, reserved=0, stride_b=2 * 100 * 128, stride_h=100 * 128, stride_n=128)
+    assert group_bwd(lib, members_of(q, kv), grads=[g16, g32]) == INVALID
+    ms = members_of(q, kv)
+    ms[1].lse_student = None
+    assert group_fwd(lib, ms) == INVALID
+    ms = members_of(q, kv)
+    ms[0].x_teacher = FAKE + 8
+    assert group_fwd(lib, ms) == INVALID
+    assert group_bwd(lib, ms) == INVALID         # the plain backward reads the inputs
+    assert group_bwd(lib, ms, with_rope=1, nrs=16) == WS_SMALL  # the fused one does not
+    del arr
+
+
+def test_group_fault_injection_maps_to_hip_error(lib, monkeypatch):
+    monkeypatch.setenv("LARD_FAULT_INJECT", "1")
+    ms = members_of(good_desc(), kv_desc(), kv_desc())
+    assert group_fwd(lib, ms) == HIP
+    assert group_bwd(lib, ms) == HIP
+    assert group_fwd(lib, members_of(good_desc(), kv_desc(), rope=_RopeDesc(None, None, None, None)),
+                     with_rope=1) == HIP
+
+
+def test_group_python_layer_checks_members():
+    x = torch.zeros(1, 1, 8, 64)
+    with pytest.raises(relkl.LardError):
+        relkl.group_relkl_fwd([(x, x)] * 5)
+    with pytest.raises(relkl.LardError):
+        relkl.group_relkl_fwd([])
+    with pytest.raises(relkl.LardError):
+        relkl.group_relkl_fwd([(x, x), (x, x)], head_maps=[None])
+    with pytest.raises(RuntimeError, match="GPU"):
+        relkl.group_relkl_fwd([(x, x), (x, x)])
