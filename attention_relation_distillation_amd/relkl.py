@@ -598,10 +598,14 @@ def _group(pairs, causal, scale, head_maps, rope):
         raise LardError(1, "head_maps needs one entry per member")
     if rope is not None and len(rope) != n:
         raise LardError(1, "rope needs one entry per member")
+    scales = list(scale) if isinstance(scale, (list, tuple)) else [scale] * n
+    if len(scales) != n:
+        raise LardError(1, "scale needs one value, or one per member")
     members = (_Member * n)()
     keep = []
     for k, (x_t, x_s) in enumerate(pairs):
-        desc, kk = _make_desc(x_t, x_s, causal, scale, None if head_maps is None else head_maps[k])
+        desc, kk = _make_desc(x_t, x_s, causal, scales[k],
+                              None if head_maps is None else head_maps[k])
         keep.extend(kk)
         members[k].desc = desc
         members[k].x_teacher = x_t.data_ptr()
@@ -637,7 +641,8 @@ def group_relkl_fwd(pairs, *, causal: bool = True, scale: Optional[float] = None
     None or one head map (or None) per member; rope: None (post-rotation inputs) or one
     entry per member, None or (cos_t, sin_t, cos_s, sin_s), rotating inside the call.
     Returns dict(loss: 0-d fp32 sum over the members, member_loss: list of 0-d fp32,
-    lse_t, lse_s, row_kl: lists per member, reserve)."""
+    lse_t, lse_s, row_kl: lists per member, reserve).  scale: None (1/sqrt(d)), one value
+    for every member, or one per member."""
     lib = load_library()
     members, keep, with_rope = _group(pairs, causal, scale, head_maps, rope)
     _require_gpu(pairs[0][0])
@@ -750,6 +755,8 @@ def group_relation_kl(pairs, *, causal: bool = True, scale: Optional[float] = No
     Differentiable with respect to every x_s."""
     hm = None if head_maps is None else tuple(None if h is None else tuple(int(v) for v in h)
                                               for h in head_maps)
+    if isinstance(scale, list):
+        scale = tuple(scale)
     rp = None if rope is None else tuple(None if r is None else tuple(r) for r in rope)
     flat = []
     for x_t, x_s in pairs:

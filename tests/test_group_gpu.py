@@ -37,6 +37,18 @@ def gpu_group(pairs, causal, head_maps=None, tabs=None, dx_dtype=None, g=1.0):
     return f, dx
 
 
+def gpu_group_scaled(pairs, causal, head_maps, scales):
+    dev = device()
+    ps, _ = to_dev(pairs)
+    f = relkl.group_relkl_fwd(ps, causal=causal, head_maps=head_maps, scale=scales,
+                              want_row_kl=True)
+    gl = torch.ones((), dtype=torch.float32, device=dev)
+    dx = relkl.group_relkl_bwd(ps, f["reserve"], gl, causal=causal, head_maps=head_maps,
+                               scale=scales)
+    torch.cuda.synchronize()
+    return f, dx
+
+
 def gpu_single(x_t, x_s, causal, head_map=None, tabs=None, dx_dtype=None):
     dev = device()
     xt, xs = x_t.to(dev), x_s.to(dev)
@@ -196,3 +208,36 @@ def test_group_fullsize_gqa_16k():
     print(f"[parity] gqa_16k group loss {float(f['loss'].item())} sum of singles {total}",
           flush=True)
     assert abs(float(f["loss"].item()) - total) <= 1e-6 * total
+
+
+def test_group_of_four_members_mixed_scale_and_length():
+    """LARD_MAX_GROUP members with their own scale, length, batch and head map, non-causal,
+    fp32 (d = 64): each against the oracle at its own scale."""
+    banner("group of four, fp32, non-causal")
+    g = torch.Generator().manual_seed(13)
+    shapes = [(1, 2, 129), (2, 1, 300), (1, 3, 64), (1, 2, 517)]
+    pairs = []
+    for b, h, n in shapes:
+        x = torch.randn((b, h, n, 64), generator=g)
+        pairs.append((x, x + 0.3 * torch.randn(x.shape, generator=g)))
+    scales = [0.125, 0.09375, 0.1875, 0.125]  # fp32-exact, one per member
+    maps = [None, None, [2, 0], [1]]
+    f, dx = gpu_group_scaled(pairs, False, maps, scales)
+    for k, ((x_t, x_s), hm, sc) in enumerate(zip(pairs, maps, scales)):
+        fo, dxo = oracle_fwd_bwd(x_t, x_s, False, head_map=hm, scale=sc)
+        assert_parity(member(f, k), dx[k], fo, dxo, torch.float32, f"four/{k}", x_s=x_s, scale=sc)
+
+
+def test_group_rope_fullsize_gqa_16k():
+    """The GQA workload at full size handed over before the rotation, Q/Q and K/K rotated
+    inside one group call, V/V not: bitwise equal to three single fused calls."""
+    banner("group RoPE gqa_16k full size")
+    rels = workloads.make_rope_inputs("gqa_16k")
+    pairs = [(r.x_t, r.x_s) for r in rels]
+    tabs = [None if r.cos_t is None else (r.cos_t, r.sin_t, r.cos_s, r.sin_s) for r in rels]
+    f, dx = gpu_group(pairs, True, tabs=tabs)
+    for k, r in enumerate(rels):
+        t = tabs[k] if tabs[k] is not None else (None, None, None, None)
+        fs, dxs = gpu_single(r.x_t, r.x_s, True, tabs=t)
+        assert_same_as_single(f, dx, k, fs, dxs, f"rope gqa_16k {r.name}")
+        del fs, dxs
