@@ -103,7 +103,7 @@ struct BwdArgs {
   const float* rope_sin;  // the gradient is rotated back before it is written
   int32_t x_unit_dense;   // fp32 path: x_t / x_s are dense [unit][N][d] copies
   void* dx;            // final gradient (splits == 1)
-  float* partial;      // [splits][B*H][row_tiles*kBR][d] (splits > 1)
+  float* partial;      // [splits][B*H][row_tiles*kBRB][d] (splits > 1)
   int32_t map_off;
 };
 
