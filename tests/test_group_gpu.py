@@ -241,3 +241,38 @@ def test_group_rope_fullsize_gqa_16k():
         fs, dxs = gpu_single(r.x_t, r.x_s, True, tabs=t)
         assert_same_as_single(f, dx, k, fs, dxs, f"rope gqa_16k {r.name}")
         del fs, dxs
+
+
+def test_group_rope_fp32_members(monkeypatch):
+    """A RoPE-fused group of fp32 members (fp32 rotated copies in the reserve, members of
+    different N and heads, one without tables): bitwise equal to single fused calls, and
+    against the RoPE oracle at the fp32 gates."""
+    banner("group RoPE fp32")
+    monkeypatch.setenv("LARD_SPLITK", "2")
+    g = torch.Generator().manual_seed(17)
+    specs = [(3, 300, True), (2, 517, True), (2, 200, False)]  # heads, N, rotated
+    pairs, tabs = [], []
+    for h, n, rot in specs:
+        x = torch.randn((1, h, n, 64), generator=g)
+        pairs.append((x, x + 0.3 * torch.randn(x.shape, generator=g)))
+        if rot:
+            ct, st = workloads.rope_tables(n, 64, 10000.0, 1.0)
+            cs, ss = workloads.rope_tables(n, 64, 10000.0, 4.0)
+            tabs.append((ct, st, cs, ss))
+        else:
+            tabs.append(None)
+    f, dx = gpu_group(pairs, True, tabs=tabs)
+    s = oracle.default_scale(64)
+    for k, ((x_t, x_s), t) in enumerate(zip(pairs, tabs)):
+        tt = t if t is not None else (None, None, None, None)
+        fs, dxs = gpu_single(x_t, x_s, True, tabs=tt)
+        assert_same_as_single(f, dx, k, fs, dxs, f"rope fp32 member {k}")
+        if t is None:
+            fo, dxo = oracle_fwd_bwd(x_t, x_s, True)
+        else:
+            ct, st, cs, ss = [v.double().numpy() for v in t]
+            xt, xs = np64(x_t), np64(x_s)
+            fo = rope.forward(xt, xs, s, True, ct, st, cs, ss, dtype="fp32")
+            dxo = rope.backward(xt, xs, s, True, 1.0, ct, st, cs, ss, dtype="fp32")
+        assert_parity(member(f, k), dx[k], fo, dxo, torch.float32, f"group rope fp32 {k}",
+                      x_s=x_s, scale=s)
