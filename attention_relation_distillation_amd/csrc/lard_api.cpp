@@ -393,7 +393,7 @@ LossOut loss_out(const FwdLaunch& L, double* partial, float* total, float* const
 lard_status check_group(int n, const lard_relkl_member* m, const lard_relkl_desc** d) {
   if (n < 1 || !m) return LARD_ERR_INVALID_ARGUMENT;
   if (n > LARD_MAX_GROUP) return LARD_ERR_UNSUPPORTED;
-  int64_t work = 0;
+  int64_t work = 0, rows = 0;
   for (int k = 0; k < n; ++k) {
     d[k] = &m[k].desc;
     const lard_status s = check_desc(d[k]);
@@ -401,8 +401,11 @@ lard_status check_group(int n, const lard_relkl_member* m, const lard_relkl_desc
     if (d[k]->dtype != d[0]->dtype || d[k]->d != d[0]->d || d[k]->causal != d[0]->causal)
       return LARD_ERR_INVALID_ARGUMENT;
     work += units_of(d[k]) * row_tiles_of(d[k]);
+    rows += units_of(d[k]) * d[k]->N;
   }
+  // 32-bit grids over all members: workgroups with splits, and the per-row passes
   if (work * kMaxSplits > 0x7fffffffLL) return LARD_ERR_UNSUPPORTED;
+  if (rows > 0x7fffffffLL * 4LL) return LARD_ERR_UNSUPPORTED;
   MapTable t;
   if (!build_maps(t, n, d)) return LARD_ERR_UNSUPPORTED;
   return LARD_OK;
