@@ -57,6 +57,29 @@ def measured_traffic(workload):
     return int(m.group(2))
 
 
+COUNTER_PROFILE = "profiles/relkl_kernels_llama2_32k_mfma_valu_counters.md"
+
+
+def measured_counters(workload):
+    """Executed MFMA utilisation and vector / transcendental pressure per kept element of both
+    kernels from the committed counter summary (rocprofv3 --pmc), or None when it is missing,
+    covers another workload, or was taken on other kernel sources."""
+    try:
+        with open(os.path.join(ROOT, COUNTER_PROFILE)) as f:
+            text = f.read()
+    except OSError:
+        return None
+    m = re.search(r"counters: workload=(\S+) (.*) source_sha256=([0-9a-f]+)", text)
+    if not m or m.group(1) != workload or m.group(3) != kernel_source_digest():
+        return None
+    out = {}
+    for kv in m.group(2).split():
+        k, v = kv.split("=")
+        out[k] = float(v)
+    out["source"] = COUNTER_PROFILE
+    return out
+
+
 def alg_flops(B, H, N, d, causal):
     """Algorithmic FLOPs of one relation call: (fwd, bwd).
 
@@ -405,6 +428,7 @@ def main():
     achieved = mean_bwd_flops / mean_bwd_s / 1e12
     total_tflops = (fl_f + fl_b) / (ms_per_step / 1e3) / 1e12
     traffic = measured_traffic(wl.name)
+    counters = measured_counters(wl.name)
 
     props = torch.cuda.get_device_properties(dev)
     out = {
@@ -429,6 +453,7 @@ def main():
                      "traffic": traffic,
                      "alg_flops_per_launch": mean_bwd_flops,
                      "mean_launch_ms": round(mean_bwd_s * 1e3, 3)},
+        "executed_counters": counters,
         "alg_tflops_total": round(total_tflops, 1),
         "frac_of_bf16_peak_total": round(total_tflops / PEAK_BF16_TFLOPS, 4),
         "fwd_ms": round(fwd_ms, 3),
