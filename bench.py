@@ -131,7 +131,29 @@ def cpu_baseline(rel, causal, target_s=12.0):
     t_probe = run(probe)
     rows = int(min(n, max(probe, round(probe * target_s / max(t_probe, 1e-3) / 512) * 512)))
     dt = run(rows)
-    return dt, rows, cores
+    return dt, rows, cores, host_info(avail)
+
+
+def host_info(avail):
+    """CPU model, cores available to this process and host RAM, from /proc."""
+    info = {"cores_available": avail}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    info["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemTotal:"):
+                    info["ram_gb"] = round(int(line.split()[1]) / 1e6, 1)
+                    break
+    except OSError:
+        pass
+    return info
 
 
 def mem_sweep(relkl, torch, dev, d=128, H=32, ns=(4096, 8192, 16384, 32768)):
@@ -404,6 +426,9 @@ def main():
     bwd_launch_ms = [e1.elapsed_time(e2) for _, _, e1, e2 in ev_log]
     fwd_ms = sum(fwd_launch_ms) / args.steps
     bwd_ms = sum(bwd_launch_ms) / args.steps
+    n_rel_launch = len(gpu)
+    step_gpu_ms = [sum(e0.elapsed_time(e2) for _, e0, _, e2 in ev_log[k:k + n_rel_launch])
+                   for k in range(0, len(ev_log), n_rel_launch)]
     per_rel = {}
     for name, e0, e1, e2 in ev_log:
         a = per_rel.setdefault(name, ([], []))
@@ -458,6 +483,7 @@ def main():
         "frac_of_bf16_peak_total": round(total_tflops / PEAK_BF16_TFLOPS, 4),
         "fwd_ms": round(fwd_ms, 3),
         "bwd_ms": round(bwd_ms, 3),
+        "step_kernel_ms": stats_ms(step_gpu_ms),
         "per_relation_ms": {k: {"fwd": stats_ms(v[0]), "bwd": stats_ms(v[1])}
                             for k, v in per_rel.items()},
         "peak_mem_gb": round(torch.cuda.max_memory_allocated(dev) / 1e9, 3),
@@ -488,7 +514,7 @@ def main():
 
     if not args.no_cpu_baseline:
         rel0 = rels[0]
-        dt, rows, cores = cpu_baseline(rel0, causal, args.cpu_seconds)
+        dt, rows, cores, host = cpu_baseline(rel0, causal, args.cpu_seconds)
         # the oracle's cost is proportional to rows x N (it evaluates full rows), so one
         # unit costs N / rows samples and the step has sum over relations of B * H units
         units = sum(wl.B * r.x_t.shape[1] for r in rels)
@@ -502,6 +528,7 @@ def main():
                        f"{platform.processor() or platform.machine()}"),
             "sample_seconds": round(dt, 3),
             "extrapolated": True,
+            "host": host,
         }
     print(json.dumps(out), flush=True)
 
