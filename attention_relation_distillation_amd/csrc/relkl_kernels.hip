@@ -167,6 +167,13 @@ __device__ __forceinline__ void lds_copy16(const void* g, uint32_t lds_base) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds_base) : "memory");
 }
 
+// The same copy from a wave-uniform base address plus a 32-bit per-lane byte offset (the
+// scalar-base form: no per-lane 64-bit address arithmetic).
+__device__ __forceinline__ void lds_copy16_s(uint32_t voff, const void* sbase, uint32_t lds_base) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+               "{m0}"(lds_base) : "memory");
+}
+
 // Workgroup barrier of the backward's tile pipeline.  It completes this wave's LDS reads
 // (lgkmcnt(0)) and keeps the compiler from moving memory accesses across it, but unlike
 // __syncthreads() it does not wait for the wave's LDS copies still in flight (the fence
@@ -211,6 +218,19 @@ template <int D, int ES>
 __device__ __forceinline__ void dma_tile(const char* base, int64_t sn_bytes, int j0, int N,
                                          char* lds, int wave, int lane) {
   using G = Geo<D, ES>;
+  if (j0 + kBC <= N && sn_bytes < (1 << 24)) {
+    // whole tile: a uniform tile base plus per-lane offsets that do not depend on the tile
+    const char* tb = base + (int64_t)j0 * sn_bytes;
+#pragma unroll
+    for (int q = 0; q < G::kDmaPerWave; ++q) {
+      const int slot0 = (wave * G::kDmaPerWave + q) * kWave;
+      const int t = slot0 + lane;
+      const int r = t / G::kCPR;
+      const int c = (t % G::kCPR) ^ G::swz(r);
+      lds_copy16_s((uint32_t)(r * (int)sn_bytes + c * 16), tb, lds_addr(lds + slot0 * 16));
+    }
+    return;
+  }
 #pragma unroll
   for (int q = 0; q < G::kDmaPerWave; ++q) {
     const int slot0 = (wave * G::kDmaPerWave + q) * kWave;
