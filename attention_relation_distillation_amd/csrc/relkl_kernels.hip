@@ -410,12 +410,14 @@ __device__ __forceinline__ u32x4 bf16x8_to_f16x8_bits(const bf16x8& v) {
 
 // Score contraction of one 32 x 32 block of the forward as a software pipeline: the LDS
 // reads of the key fragments run ahead of their MFMAs with at most kFwdLdsOps reads in
-// flight.
-template <class In, int D>
+// flight.  After MFMA I the callback extra(I) places independent vector work (the previous
+// block's exponentials) in the same scheduling region as the reads for the next MFMA, so a
+// wave keeps its vector unit busy while its own MFMAs run.
+template <class In, int D, class Extra>
 __device__ __forceinline__ void score_pipeline(const char* tile_t, const char* tile_s, int fbase,
                                                int jb, const typename In::frag_t (&qt)[D / 16],
                                                const typename In::frag_t (&qs)[D / 16],
-                                               f32x16& st, f32x16& ss) {
+                                               f32x16& st, f32x16& ss, Extra&& extra) {
   using frag_t = typename In::frag_t;
   constexpr int KS = D / 16, NF = 2 * KS;
   using S = LoadSchedule<0, NF, 1, In::kES == 2 ? 1 : 2, kFwdLdsOps>;
@@ -441,8 +443,10 @@ __device__ __forceinline__ void score_pipeline(const char* tile_t, const char* t
         __builtin_amdgcn_sched_barrier(0);
         mma(std::integral_constant<int, I>{});
         __builtin_amdgcn_sched_barrier(0);
+        extra(std::integral_constant<int, I>{});
       }()), ...);
   }(std::make_integer_sequence<int, NF>{});
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <class In, int D, bool CAUSAL>
@@ -522,6 +526,69 @@ void relkl_fwd_kernel(const FwdLaunch L) {
   const float b_init = -kNegBig * c2;  // bias of an empty row: every real bias is below it
   float b_t = b_init, l_t = 0.f, acc_a = 0.f, b_s = b_init, l_s = 0.f;
 
+  // Software pipeline over 32-key blocks, which alternate between two score buffers: the
+  // exponentials and sums of a block without masked entries run inside the MFMA sequence of
+  // the next block (one element of the 16 per MFMA at d = 128), with both at the raised
+  // issue priority.  The order of every sum is that of online_update_fast.  A block with
+  // masked entries (the diagonal or the ragged end: always a wave's last) and the exact
+  // fallback run on their own.
+  f32x16 stA = f32x16{}, ssA = f32x16{}, stB = f32x16{}, ssB = f32x16{};
+  bool have_p = false, p_mask = false;  // a pending block, whether it has masked entries
+  int p_jb0 = 0, p_par = 0;             // its first column, its buffer (A: 0, B: 1)
+  auto finish = [&](const f32x16& pt, const f32x16& ps) __attribute__((always_inline)) {
+    if (p_mask)
+      online_update<true, CAUSAL>(pt, ps, p_jb0, row, hh, N, c2, b_t, l_t, acc_a, b_s, l_s);
+    else if (!online_update_fast(pt, ps, c2, b_t, b_s, l_t, acc_a, l_s))
+      online_update<false, CAUSAL>(pt, ps, p_jb0, row, hh, N, c2, b_t, l_t, acc_a, b_s, l_s);
+  };
+  // Block jb of the tile: scores into (st, ss) while the pending block (pt, ps) is reduced.
+  auto block = [&](auto jbc, int kt, const char* tile_t, const char* tile_s, f32x16& st,
+                   f32x16& ss, const f32x16& pt, const f32x16& ps) __attribute__((always_inline)) {
+    constexpr int jb = decltype(jbc)::value;
+    const int jb0 = kt * kBC + 32 * jb;
+    if (jb0 >= N) return false;
+    if (CAUSAL && jb0 > ib0 + 31) return false;  // above every row of the wave
+    const bool need_mask = (CAUSAL && jb0 + 31 > ib0) || (jb0 + 32 > N);
+    if (have_p && !p_mask) {
+      constexpr int NF = 2 * KS, E = (16 + NF - 1) / NF;  // elements per MFMA slot
+      float lt[2] = {0.f, 0.f}, ls[2] = {0.f, 0.f}, aa[2] = {0.f, 0.f};
+      const float bt = b_t, bs = b_s;
+      __builtin_amdgcn_s_setprio(1);
+      score_pipeline<In, D>(tile_t, tile_s, fbase, jb, qt, qs, st, ss,
+                            [&](auto ic) __attribute__((always_inline)) {
+        constexpr int I = decltype(ic)::value;
+#pragma unroll
+        for (int r = I * E; r < (I + 1) * E && r < 16; ++r) {
+          const float et = fast_exp2(fmaf(pt[r], c2, bt));
+          const float es = fast_exp2(fmaf(ps[r], c2, bs));
+          lt[r & 1] += et;
+          ls[r & 1] += es;
+          aa[r & 1] = fmaf(et, pt[r] - ps[r], aa[r & 1]);
+        }
+      });
+      __builtin_amdgcn_s_setprio(0);
+      const float sum_t = lt[0] + lt[1], sum_s = ls[0] + ls[1], sum_a = aa[0] + aa[1];
+      const bool ok = sum_t <= 0x1p64f && sum_s <= 0x1p64f;
+      // selects, not a branch, so that the KL products stay inside the MFMA sequence
+      l_t = ok ? l_t + sum_t : l_t;
+      l_s = ok ? l_s + sum_s : l_s;
+      acc_a = ok ? acc_a + sum_a : acc_a;
+      if (!ok)
+        online_update<false, CAUSAL>(pt, ps, p_jb0, row, hh, N, c2, b_t, l_t, acc_a, b_s, l_s);
+    } else {
+      if (have_p) finish(pt, ps);
+      // the LDS-bound matrix part issues ahead of the partner wave's vector work
+      __builtin_amdgcn_s_setprio(1);
+      score_pipeline<In, D>(tile_t, tile_s, fbase, jb, qt, qs, st, ss, [](auto) {});
+      __builtin_amdgcn_s_setprio(0);
+    }
+    have_p = true;
+    p_mask = need_mask;
+    p_jb0 = jb0;
+    p_par = jb;
+    return true;
+  };
+  static_assert(kBC == 64, "two 32-key blocks per tile, one per score buffer");
   auto step = [&](int kt, const char* cur, char* nxt) __attribute__((always_inline)) {
     wait_vmem();
     __syncthreads();
@@ -531,26 +598,17 @@ void relkl_fwd_kernel(const FwdLaunch L) {
     }
     const char* tile_t = cur;
     const char* tile_s = cur + G::kTileBytes;
-#pragma unroll 1
-    for (int jb = 0; jb < kBC / 32; ++jb) {
-      const int jb0 = kt * kBC + 32 * jb;
-      if (jb0 >= N) break;
-      if (CAUSAL && jb0 > ib0 + 31) break;  // above every row of the wave
-      f32x16 st, ss;
-      // the LDS-bound matrix part issues ahead of the partner wave's vector work
-      __builtin_amdgcn_s_setprio(1);
-      score_pipeline<In, D>(tile_t, tile_s, fbase, jb, qt, qs, st, ss);
-      __builtin_amdgcn_s_setprio(0);
-      const bool need_mask = (CAUSAL && jb0 + 31 > ib0) || (jb0 + 32 > N);
-      if (need_mask)
-        online_update<true, CAUSAL>(st, ss, jb0, row, hh, N, c2, b_t, l_t, acc_a, b_s, l_s);
-      else if (!online_update_fast(st, ss, c2, b_t, b_s, l_t, acc_a, l_s))
-        online_update<false, CAUSAL>(st, ss, jb0, row, hh, N, c2, b_t, l_t, acc_a, b_s, l_s);
-    }
+    // blocks are consecutive, so the pending block of block 0 is in B and that of block 1 in A
+    if (block(std::integral_constant<int, 0>{}, kt, tile_t, tile_s, stA, ssA, stB, ssB))
+      block(std::integral_constant<int, 1>{}, kt, tile_t, tile_s, stB, ssB, stA, ssA);
   };
   for (int kt = 0; kt < n_tiles; kt += 2) {
     step(kt, lds0, lds1);
     if (kt + 1 < n_tiles) step(kt + 1, lds1, lds0);
+  }
+  if (have_p) {
+    if (p_par == 0) finish(stA, ssA);
+    else finish(stB, ssB);
   }
 
   // Merge the two half-waves (lanes l and l ^ 32 hold the same row) and finish, in log2
