@@ -561,8 +561,13 @@ void relkl_fwd_kernel(const FwdLaunch L) {
         for (int r = I * E; r < (I + 1) * E && r < 16; ++r) {
           const float et = fast_exp2(fmaf(pt[r], c2, bt));
           const float es = fast_exp2(fmaf(ps[r], c2, bs));
-          lt[r & 1] += et;
-          ls[r & 1] += es;
+          if (r < 2) {  // exponentials are never -0, so these equal 0 + et and 0 + es bitwise
+            lt[r] = et;
+            ls[r] = es;
+          } else {
+            lt[r & 1] += et;
+            ls[r & 1] += es;
+          }
           aa[r & 1] = fmaf(et, pt[r] - ps[r], aa[r & 1]);
         }
       });
@@ -705,7 +710,10 @@ __device__ __forceinline__ void make_w(const f32x16& st, const f32x16& ss, float
       }
       if constexpr (COL) {
         const float ct_ = fast_exp2(fmaf(ss[r], c2, -cs4[t])) - fast_exp2(fmaf(st[r], c2, -ct4[t]));
-        v += DIAG ? (dj >= di ? ct_ : 0.f) : ct_;
+        const float cm = DIAG ? (dj >= di ? ct_ : 0.f) : ct_;
+        // a difference of two exponentials is never -0, so v = cm equals 0 + cm bitwise
+        if constexpr (ROW) v += cm;
+        else v = cm;
       }
       if constexpr (TAIL) v = dj < n_left ? v : 0.f;
       wv[r] = v;
