@@ -1005,7 +1005,8 @@ void relkl_bwd_kernel(const BwdLaunch L) {
   //    step t-1) at its start and awaits it at its end;
   //  * two buffers (fp32, d = 128): tile t+1 goes into the buffer of tile t-1, whose last
   //    reads are the gradient MFMAs of M(2t); a barrier after M(2t) precedes the copy.
-  // The barrier ending step t publishes tile t+1 to every wave.
+  // The barrier ending step t publishes tile t+1 to every wave.  A V(2t-1) that a wave runs
+  // at the start of step t (below) reads tile t-1's statistics before either copy reaches them.
 
   // M(n): gradient of block n-1, scores of block n.  Every M runs the full pipeline: M(0)
   // contracts the initial zero W with the zero-filled student tile of the last buffer;
@@ -1067,10 +1068,16 @@ void relkl_bwd_kernel(const BwdLaunch L) {
     }
   };
 
+  // Waves w and w + 4 share a SIMD.  The barrier that ends each step would start both in their
+  // matrix phases; waves 4-7 instead run V of a tile's last block after the barrier, at the
+  // start of the next step, so their matrix phases fall beside the vector phases of waves 0-3
+  // (each wave's own order of operations is unchanged; its stage buffer is still resident).
+  const bool lag = wave >= kBWaves / 2;
   wait_vmem();
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     if (kStages == 3 && t + 1 < ntiles) stage_tile(t + 1, buf(t + 1));
+    if (lag && t > 0) v_phase(2 * t - 1);
     m_phase(2 * t);
     if (kStages == 2) {
       lds_barrier();
@@ -1078,10 +1085,11 @@ void relkl_bwd_kernel(const BwdLaunch L) {
     }
     v_phase(2 * t);
     m_phase(2 * t + 1);
-    v_phase(2 * t + 1);
+    if (!lag) v_phase(2 * t + 1);
     wait_vmem();
     lds_barrier();
   }
+  if (lag && ntiles > 0) v_phase(NB - 1);
   m_phase(NB);
 
   // Scale and write: acc[mb][r] = dX[i][d] * 2^14 / (scale g) for
