@@ -356,7 +356,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the relation-KL "
-              "path is single-GPU in this build", file=sys.stderr)
+              "library runs on a single GPU and has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
 
     import torch
