@@ -17,7 +17,7 @@ namespace {
 
 using namespace lard;
 
-constexpr int kVersion = 1 * 10000 + 1 * 100 + 0;
+constexpr int kVersion = 2 * 10000 + 0 * 100 + 0;
 constexpr int kTargetWorkgroups = 512;  // two rounds of one backward workgroup per CU
 constexpr int kMaxSplits = 64;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -109,7 +109,8 @@ size_t fwd_workspace(int n, const lard_relkl_desc* const* d) {
   return round256((size_t)p * sizeof(double));
 }
 
-// Backward: fp32 split-K partials [splits][units][row_tiles * kBRB][d] per member.
+// Backward workspace: fp32 split-K partials [splits][units][row_tiles * kBRB][d] per member
+// when the key range is split, else nothing.
 size_t bwd_partial_floats(const lard_relkl_desc* d) {
   return (size_t)units_of(d) * bwd_row_tiles_of(d) * kBRB * d->d;
 }
@@ -122,14 +123,17 @@ size_t bwd_workspace(int n, const lard_relkl_desc* const* d) {
   return (size_t)s * f * sizeof(float);
 }
 
-// Reserve of one problem: plain (fp16 copies of bf16 inputs only), RoPE-fused (rotated
-// copies, fp16 or fp32) or cross (copies of A and B, fp16 or fp32).
+// Reserve of one problem: none (plain), rotated copies in the input dtype (RoPE-fused), or
+// copies of A and B as fp16 images of bf16 values or fp32 (cross).
 enum class Path { kPlain, kRope, kCross };
 
+size_t reserve_total(const lard_relkl_desc* d, Path p) {
+  if (p == Path::kPlain) return 0;
+  return reserve_layout(units_of(d), d->N, d->d, elem_size(d->dtype), p == Path::kCross).total;
+}
+
 ReserveLayout reserve_of(const lard_relkl_desc* d, Path p) {
-  const bool bf16 = d->dtype == LARD_BF16;
-  const int copy = p == Path::kPlain ? (bf16 ? 2 : 0) : (bf16 ? 2 : 4);
-  return reserve_layout(units_of(d), d->N, d->d, copy, p == Path::kCross);
+  return reserve_layout(units_of(d), d->N, d->d, elem_size(d->dtype), p == Path::kCross);
 }
 
 // Tables of one side: both null (not rotated) or both set, 16-byte aligned.
@@ -167,10 +171,21 @@ lard_status check_grad(const lard_relkl_desc* desc, const lard_grad_desc* grad, 
   return LARD_OK;
 }
 
-// Forward outputs of one problem.
-lard_status check_fwd_outputs(const float* lse_t, const float* lse_s, const float* row_kl) {
+// Forward outputs of one problem (diag_delta and row_kl are optional).
+lard_status check_fwd_outputs(const float* lse_t, const float* lse_s, const float* diag_delta,
+                              const float* row_kl) {
   if (!lse_t || !lse_s) return LARD_ERR_INVALID_ARGUMENT;
-  if (!aligned(lse_t, 4) || !aligned(lse_s, 4) || (row_kl && !aligned(row_kl, 4)))
+  if (!aligned(lse_t, 4) || !aligned(lse_s, 4) || (row_kl && !aligned(row_kl, 4)) ||
+      (diag_delta && !aligned(diag_delta, 4)))
+    return LARD_ERR_INVALID_ARGUMENT;
+  return LARD_OK;
+}
+
+// Forward state the backward reads (diag_delta: the relation only).
+lard_status check_bwd_state(const float* lse_t, const float* lse_s, const float* diag_delta,
+                            bool relation) {
+  if (!lse_t || !lse_s || (relation && !diag_delta)) return LARD_ERR_INVALID_ARGUMENT;
+  if (!aligned(lse_t, 4) || !aligned(lse_s, 4) || (diag_delta && !aligned(diag_delta, 4)))
     return LARD_ERR_INVALID_ARGUMENT;
   return LARD_OK;
 }
@@ -232,9 +247,9 @@ void identity_maps(Launch<M>& L) {
   for (int k = 0; k < L.n; ++k) L.m[k].map_off = -1;
 }
 
-// Forward member: shape, statistics and outputs (operands set by the caller).
-void fwd_common(FwdArgs& a, const lard_relkl_desc* d, char* rb, const ReserveLayout& R,
-                bool write_copies, float* lse_t, float* lse_s, float* row_kl, double* partial) {
+// Forward member: shape and outputs (operands set by the caller).
+void fwd_common(FwdArgs& a, const lard_relkl_desc* d, float* lse_t, float* lse_s,
+                float* diag_delta, float* row_kl, double* partial) {
   a.B = d->B; a.H = d->H; a.N = d->N;
   a.row_tiles = row_tiles_of(d);
   a.scale = d->scale;
@@ -242,12 +257,8 @@ void fwd_common(FwdArgs& a, const lard_relkl_desc* d, char* rb, const ReserveLay
   a.lse_t = lse_t;
   a.lse_s = lse_s;
   a.row_kl = row_kl;
+  a.diag_delta = diag_delta;
   a.partial = partial;
-  a.npad = (int32_t)R.npad;
-  a.x16_t = write_copies ? reinterpret_cast<uint16_t*>(rb + R.x16_t) : nullptr;
-  a.x16_s = write_copies ? reinterpret_cast<uint16_t*>(rb + R.x16_s) : nullptr;
-  a.r_t = reinterpret_cast<float*>(rb + R.r_t);
-  a.r_s = reinterpret_cast<float*>(rb + R.r_s);
 }
 
 // Forward operands read in place from the caller's tensors.
@@ -290,55 +301,44 @@ void prep_member(PrepLaunch& P, const lard_relkl_desc* d, const void* xt, int64_
   p.c_s = cs;
 }
 
-// Backward member: shape, statistics, split and output (operands set by the caller).
-void bwd_common(BwdArgs& a, const lard_relkl_desc* d, const char* rb, const ReserveLayout& R,
-                int splits, const float* grad_loss, const lard_grad_desc* g, void* dx,
-                float* partial) {
+// Backward member: shape, the forward's state, split and output (operands set by the
+// caller).
+void bwd_common(BwdArgs& a, const lard_relkl_desc* d, const float* lse_t, const float* lse_s,
+                int splits, const float* diag_delta, const float* grad_loss,
+                const lard_grad_desc* g, void* dx, float* partial) {
   a.B = d->B; a.H = d->H; a.N = d->N;
   a.row_tiles = bwd_row_tiles_of(d);
   a.key_tiles = key_tiles_of(d);
   a.splits = splits;
   a.scale = d->scale;
   a.c2 = d->scale * kLog2e;
-  a.npad = (int32_t)R.npad;
-  a.r_t = reinterpret_cast<const float*>(rb + R.r_t);
-  a.r_s = reinterpret_cast<const float*>(rb + R.r_s);
-  a.rc_t = a.r_t;
-  a.rc_s = a.r_s;
+  a.lse_t = lse_t;
+  a.lse_s = lse_s;
+  a.lc_t = lse_t;
+  a.lc_s = lse_s;
+  a.diag_delta = diag_delta;
   a.grad_loss = grad_loss;
   a.g_sb = g->stride_b; a.g_sh = g->stride_h; a.g_sn = g->stride_n;
   a.dx = dx;
   a.partial = partial;
 }
 
-// Backward operands: the plain path (fp32 rows in place, fp16 copies for bf16 inputs).
-void bwd_inputs(BwdArgs& a, const lard_relkl_desc* d, const char* rb, const ReserveLayout& R,
-                const void* xt, const void* xs) {
+// Backward operands read in place from the caller's tensors.
+void bwd_inputs(BwdArgs& a, const lard_relkl_desc* d, const void* xt, const void* xs) {
   a.x_t = xt;
   a.x_s = xs;
   a.t_sb = d->t_stride_b; a.t_sh = d->t_stride_h; a.t_sn = d->t_stride_n;
   a.s_sb = d->s_stride_b; a.s_sh = d->s_stride_h; a.s_sn = d->s_stride_n;
-  const bool bf16 = d->dtype == LARD_BF16;
-  a.x16_t = bf16 ? reinterpret_cast<const uint16_t*>(rb + R.x16_t) : nullptr;
-  a.x16_s = bf16 ? reinterpret_cast<const uint16_t*>(rb + R.x16_s) : nullptr;
-  a.y16_t = a.x16_t;
-  a.y16_s = a.x16_s;
 }
 
-// Backward operands from dense reserve copies (own rows at own_*, staged rows at stg_*:
-// fp16 through x16_* / y16_*, fp32 through x_* / y_*).
-void bwd_copies(BwdArgs& a, const lard_relkl_desc* d, const char* rb, size_t own_t,
-                size_t own_s, size_t stg_t, size_t stg_s) {
-  const bool bf16 = d->dtype == LARD_BF16;
-  a.x_unit_dense = 1;
+// Backward operands from dense reserve copies (own rows at own_*, staged rows at stg_*).
+void bwd_copies(BwdArgs& a, const char* rb, size_t own_t, size_t own_s, size_t stg_t,
+                size_t stg_s) {
+  a.x_dense = 1;
   a.x_t = rb + own_t;
   a.x_s = rb + own_s;
   a.y_t = rb + stg_t;
   a.y_s = rb + stg_s;
-  a.x16_t = bf16 ? reinterpret_cast<const uint16_t*>(rb + own_t) : nullptr;
-  a.x16_s = bf16 ? reinterpret_cast<const uint16_t*>(rb + own_s) : nullptr;
-  a.y16_t = bf16 ? reinterpret_cast<const uint16_t*>(rb + stg_t) : nullptr;
-  a.y16_s = bf16 ? reinterpret_cast<const uint16_t*>(rb + stg_s) : nullptr;
 }
 
 int bwd_workgroups(const lard_relkl_desc* d, int splits) {
@@ -346,8 +346,8 @@ int bwd_workgroups(const lard_relkl_desc* d, int splits) {
 }
 
 // Backward launch plus the split-K reduction of every member.
-lard_status run_bwd(const BwdLaunch& L, const lard_relkl_desc* const* d, bool out_f32,
-                    int mode, void* stream) {
+lard_status run_bwd(const BwdLaunch& L, const lard_relkl_desc* const* d, bool out_f32, int mode,
+                    void* stream) {
   const lard_relkl_desc* d0 = d[0];
   int e = launch_bwd(L, d0->dtype == LARD_BF16, d0->d, d0->causal == 1, out_f32, stream, mode);
   if (e != 0) return LARD_ERR_HIP;
@@ -415,7 +415,7 @@ size_t group_reserve(int n, const lard_relkl_desc* const* d, Path p, size_t* off
   size_t total = 0;
   for (int k = 0; k < n; ++k) {
     if (off) off[k] = total;
-    total += reserve_of(d[k], p).total;
+    total += reserve_total(d[k], p);
   }
   return total;
 }
@@ -423,55 +423,58 @@ size_t group_reserve(int n, const lard_relkl_desc* const* d, Path p, size_t* off
 // Forward of n problems (plain or RoPE-fused) with reserve regions at rb + off[k].
 lard_status run_group_fwd(int n, const lard_relkl_desc* const* d, const void* const* xt,
                           const void* const* xs, float* const* lse_t, float* const* lse_s,
-                          float* const* row_kl, float* const* member_loss,
-                          const lard_rope_desc* const* rope, bool with_rope, float* loss,
-                          char* rb, const size_t* off, double* partial, void* stream) {
+                          float* const* diag_delta, float* const* row_kl,
+                          float* const* member_loss, const lard_rope_desc* const* rope,
+                          bool with_rope, float* loss, char* rb, const size_t* off,
+                          double* partial, void* stream) {
   const bool bf16 = d[0]->dtype == LARD_BF16;
-  const Path path = with_rope ? Path::kRope : Path::kPlain;
   MapTable maps;
   build_maps(maps, n, d);
   if (with_rope) {
-    // 1. rotated copies of every member into its reserve region
+    // 1. rotated copies of every member into its reserve region, in the input dtype
     PrepLaunch P;
     launch_init(P);
     for (int k = 0; k < n; ++k) {
-      const ReserveLayout R = reserve_of(d[k], path);
+      const ReserveLayout R = reserve_of(d[k], Path::kRope);
       char* r = rb + off[k];
       prep_member(P, d[k], xt[k], d[k]->t_stride_b, d[k]->t_stride_h, d[k]->t_stride_n, xs[k],
-                  d[k]->s_stride_b, d[k]->s_stride_h, d[k]->s_stride_n, rope[k], r + R.x16_t,
-                  r + R.x16_s);
+                  d[k]->s_stride_b, d[k]->s_stride_h, d[k]->s_stride_n, rope[k], r + R.x_t,
+                  r + R.x_s);
     }
     use_maps(P, maps);
-    if (launch_rope_prep(P, bf16, d[0]->d, stream) != 0) return LARD_ERR_HIP;
+    if (launch_rope_prep(P, bf16, d[0]->d, stream, /*f16_images=*/false) != 0)
+      return LARD_ERR_HIP;
   }
   // 2. the forward: in place (plain) or on the copies
   FwdLaunch F;
   launch_init(F);
   double* part = partial;
   for (int k = 0; k < n; ++k) {
-    const ReserveLayout R = reserve_of(d[k], path);
-    char* r = rb + off[k];
     FwdArgs& a = add_member(F, (int)fwd_partials(d[k]));
-    if (with_rope) fwd_copies(a, d[k], r + R.x16_t, r + R.x16_s, nullptr, nullptr);
-    else fwd_inputs(a, d[k], xt[k], xs[k]);
-    fwd_common(a, d[k], r, R, !with_rope && bf16, lse_t[k], lse_s[k], row_kl[k], part);
+    if (with_rope) {
+      const ReserveLayout R = reserve_of(d[k], Path::kRope);
+      fwd_copies(a, d[k], rb + off[k] + R.x_t, rb + off[k] + R.x_s, nullptr, nullptr);
+    } else {
+      fwd_inputs(a, d[k], xt[k], xs[k]);
+    }
+    fwd_common(a, d[k], lse_t[k], lse_s[k], diag_delta[k], row_kl[k], part);
     part += fwd_partials(d[k]);
   }
   if (with_rope) identity_maps(F);
   else use_maps(F, maps);
   const LossOut lo = loss_out(F, partial, loss, member_loss);
-  const int e = launch_fwd(F, bf16, d[0]->d, d[0]->causal == 1, lo, stream,
-                           /*f16_copies=*/with_rope && bf16);
+  const int e = launch_fwd(F, bf16, d[0]->d, d[0]->causal == 1, lo, stream, /*cross=*/false);
   return e == 0 ? LARD_OK : LARD_ERR_HIP;
 }
 
 // Backward of n problems (plain or RoPE-fused), one gradient dtype.
 lard_status run_group_bwd(int n, const lard_relkl_desc* const* d, const void* const* xt,
-                          const void* const* xs, const lard_rope_desc* const* rope,
-                          bool with_rope, const char* rb, const size_t* off,
-                          const float* grad_loss, const lard_grad_desc* const* grad,
-                          void* const* dx, float* partial, void* stream) {
-  const Path path = with_rope ? Path::kRope : Path::kPlain;
+                          const void* const* xs, const float* const* lse_t,
+                          const float* const* lse_s, const float* const* diag_delta,
+                          const lard_rope_desc* const* rope, bool with_rope, const char* rb,
+                          const size_t* off, const float* grad_loss,
+                          const lard_grad_desc* const* grad, void* const* dx, float* partial,
+                          void* stream) {
   const int splits = choose_splits(n, d);
   MapTable maps;
   build_maps(maps, n, d);
@@ -479,21 +482,28 @@ lard_status run_group_bwd(int n, const lard_relkl_desc* const* d, const void* co
   launch_init(L);
   float* part = partial;
   for (int k = 0; k < n; ++k) {
-    const ReserveLayout R = reserve_of(d[k], path);
-    const char* r = rb + off[k];
     BwdArgs& a = add_member(L, bwd_workgroups(d[k], splits));
     if (with_rope) {
-      bwd_copies(a, d[k], r, R.x16_t, R.x16_s, R.x16_t, R.x16_s);
+      const ReserveLayout R = reserve_of(d[k], Path::kRope);
+      bwd_copies(a, rb + off[k], R.x_t, R.x_s, R.x_t, R.x_s);
       a.rope_cos = rope[k] ? rope[k]->cos_student : nullptr;
       a.rope_sin = rope[k] ? rope[k]->sin_student : nullptr;
     } else {
-      bwd_inputs(a, d[k], r, R, xt[k], xs[k]);
+      bwd_inputs(a, d[k], xt[k], xs[k]);
     }
-    bwd_common(a, d[k], r, R, splits, grad_loss, grad[k], dx[k], part);
+    bwd_common(a, d[k], lse_t[k], lse_s[k], splits, diag_delta[k], grad_loss, grad[k], dx[k],
+               part);
     if (splits > 1) part += (size_t)splits * bwd_partial_floats(d[k]);
   }
   use_maps(L, maps);  // output placement (and in-place operands of the plain path)
   return run_bwd(L, d, grad[0]->dtype == LARD_FP32, 0, stream);
+}
+
+// Workspace argument check of a backward needing `need` bytes.
+lard_status check_bwd_workspace(const void* ws, size_t bytes, size_t need) {
+  if (need > 0 && (!ws || !aligned(ws, 16))) return LARD_ERR_INVALID_ARGUMENT;
+  if (bytes < need) return LARD_ERR_WORKSPACE_TOO_SMALL;
+  return LARD_OK;
 }
 
 }  // namespace
@@ -521,108 +531,98 @@ size_t lard_relkl_workspace_size(const lard_relkl_desc* desc, int pass, lard_sta
   return pass == 0 ? fwd_workspace(1, &desc) : bwd_workspace(1, &desc);
 }
 
-size_t lard_relkl_reserve_size(const lard_relkl_desc* desc, lard_status* status) {
-  const lard_status s = check_desc(desc);
-  if (status) *status = s;
-  if (s != LARD_OK) return 0;
-  return reserve_of(desc, Path::kPlain).total;
-}
-
 lard_status lard_relkl_fwd(const lard_relkl_desc* desc, const void* x_teacher,
                            const void* x_student, float* lse_teacher, float* lse_student,
-                           float* row_kl, float* loss, void* reserve, size_t reserve_bytes,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+                           float* diag_delta, float* row_kl, float* loss, void* workspace,
+                           size_t workspace_bytes, void* stream) {
   lard_status s = check_desc(desc);
   if (s != LARD_OK) return s;
   if ((s = check_inputs(x_teacher, x_student)) != LARD_OK) return s;
-  if ((s = check_fwd_outputs(lse_teacher, lse_student, row_kl)) != LARD_OK) return s;
-  if (!loss || !workspace || !reserve) return LARD_ERR_INVALID_ARGUMENT;
-  if (!aligned(workspace, 8) || !aligned(reserve, 256) || !aligned(loss, 4))
-    return LARD_ERR_INVALID_ARGUMENT;
+  if ((s = check_fwd_outputs(lse_teacher, lse_student, diag_delta, row_kl)) != LARD_OK) return s;
+  if (!loss || !workspace) return LARD_ERR_INVALID_ARGUMENT;
+  if (!aligned(workspace, 8) || !aligned(loss, 4)) return LARD_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < fwd_workspace(1, &desc)) return LARD_ERR_WORKSPACE_TOO_SMALL;
-  if (reserve_bytes < reserve_of(desc, Path::kPlain).total) return LARD_ERR_WORKSPACE_TOO_SMALL;
-  const size_t off = 0;
-  return run_group_fwd(1, &desc, &x_teacher, &x_student, &lse_teacher, &lse_student, &row_kl,
-                       nullptr, nullptr, false, loss, static_cast<char*>(reserve), &off,
+  return run_group_fwd(1, &desc, &x_teacher, &x_student, &lse_teacher, &lse_student,
+                       &diag_delta, &row_kl, nullptr, nullptr, false, loss, nullptr, nullptr,
                        static_cast<double*>(workspace), stream);
 }
 
 lard_status lard_relkl_bwd(const lard_relkl_desc* desc, const void* x_teacher,
-                           const void* x_student, const void* reserve, size_t reserve_bytes,
+                           const void* x_student, const float* lse_teacher,
+                           const float* lse_student, const float* diag_delta,
                            const float* grad_loss, const lard_grad_desc* grad,
                            void* dx_student, void* workspace, size_t workspace_bytes,
                            void* stream) {
   lard_status s = check_desc(desc);
   if (s != LARD_OK) return s;
   if ((s = check_inputs(x_teacher, x_student)) != LARD_OK) return s;
-  if (!reserve || !grad_loss) return LARD_ERR_INVALID_ARGUMENT;
+  if ((s = check_bwd_state(lse_teacher, lse_student, diag_delta, true)) != LARD_OK) return s;
+  if (!grad_loss || !aligned(grad_loss, 4)) return LARD_ERR_INVALID_ARGUMENT;
   if ((s = check_grad(desc, grad, dx_student)) != LARD_OK) return s;
-  if (!aligned(reserve, 256) || !aligned(grad_loss, 4)) return LARD_ERR_INVALID_ARGUMENT;
-  if (reserve_bytes < reserve_of(desc, Path::kPlain).total) return LARD_ERR_WORKSPACE_TOO_SMALL;
-  const size_t need = bwd_workspace(1, &desc);
-  if (need > 0 && (!workspace || !aligned(workspace, 16))) return LARD_ERR_INVALID_ARGUMENT;
-  if (workspace_bytes < need) return LARD_ERR_WORKSPACE_TOO_SMALL;
-  const size_t off = 0;
-  return run_group_bwd(1, &desc, &x_teacher, &x_student, nullptr, false,
-                       static_cast<const char*>(reserve), &off, grad_loss, &grad, &dx_student,
-                       static_cast<float*>(workspace), stream);
+  s = check_bwd_workspace(workspace, workspace_bytes, bwd_workspace(1, &desc));
+  if (s != LARD_OK) return s;
+  return run_group_bwd(1, &desc, &x_teacher, &x_student, &lse_teacher, &lse_student,
+                       &diag_delta, nullptr, false, nullptr, nullptr, grad_loss, &grad,
+                       &dx_student, static_cast<float*>(workspace), stream);
 }
 
 size_t lard_relkl_rope_reserve_size(const lard_relkl_desc* desc, lard_status* status) {
   const lard_status s = check_desc(desc);
   if (status) *status = s;
   if (s != LARD_OK) return 0;
-  return reserve_of(desc, Path::kRope).total;
+  return reserve_total(desc, Path::kRope);
 }
 
 lard_status lard_relkl_rope_fwd(const lard_relkl_desc* desc, const lard_rope_desc* rope,
                                 const void* x_teacher, const void* x_student,
-                                float* lse_teacher, float* lse_student, float* row_kl,
-                                float* loss, void* reserve, size_t reserve_bytes,
+                                float* lse_teacher, float* lse_student, float* diag_delta,
+                                float* row_kl, float* loss, void* reserve, size_t reserve_bytes,
                                 void* workspace, size_t workspace_bytes, void* stream) {
   lard_status s = check_desc(desc);
   if (s != LARD_OK) return s;
   if ((s = check_rope(rope)) != LARD_OK) return s;
   if ((s = check_inputs(x_teacher, x_student)) != LARD_OK) return s;
-  if ((s = check_fwd_outputs(lse_teacher, lse_student, row_kl)) != LARD_OK) return s;
+  if ((s = check_fwd_outputs(lse_teacher, lse_student, diag_delta, row_kl)) != LARD_OK) return s;
   if (!loss || !workspace || !reserve) return LARD_ERR_INVALID_ARGUMENT;
   if (!aligned(workspace, 8) || !aligned(reserve, 256) || !aligned(loss, 4))
     return LARD_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < fwd_workspace(1, &desc)) return LARD_ERR_WORKSPACE_TOO_SMALL;
-  if (reserve_bytes < reserve_of(desc, Path::kRope).total) return LARD_ERR_WORKSPACE_TOO_SMALL;
+  if (reserve_bytes < reserve_total(desc, Path::kRope)) return LARD_ERR_WORKSPACE_TOO_SMALL;
   const size_t off = 0;
-  return run_group_fwd(1, &desc, &x_teacher, &x_student, &lse_teacher, &lse_student, &row_kl,
-                       nullptr, &rope, true, loss, static_cast<char*>(reserve), &off,
-                       static_cast<double*>(workspace), stream);
+  return run_group_fwd(1, &desc, &x_teacher, &x_student, &lse_teacher, &lse_student,
+                       &diag_delta, &row_kl, nullptr, &rope, true, loss,
+                       static_cast<char*>(reserve), &off, static_cast<double*>(workspace),
+                       stream);
 }
 
 lard_status lard_relkl_rope_bwd(const lard_relkl_desc* desc, const lard_rope_desc* rope,
                                 const void* reserve, size_t reserve_bytes,
-                                const float* grad_loss, const lard_grad_desc* grad,
-                                void* dx_student, void* workspace, size_t workspace_bytes,
-                                void* stream) {
+                                const float* lse_teacher, const float* lse_student,
+                                const float* diag_delta, const float* grad_loss,
+                                const lard_grad_desc* grad, void* dx_student, void* workspace,
+                                size_t workspace_bytes, void* stream) {
   lard_status s = check_desc(desc);
   if (s != LARD_OK) return s;
   if ((s = check_rope(rope)) != LARD_OK) return s;
-  if (!reserve || !grad_loss) return LARD_ERR_INVALID_ARGUMENT;
+  if (!reserve || !aligned(reserve, 256)) return LARD_ERR_INVALID_ARGUMENT;
+  if ((s = check_bwd_state(lse_teacher, lse_student, diag_delta, true)) != LARD_OK) return s;
+  if (!grad_loss || !aligned(grad_loss, 4)) return LARD_ERR_INVALID_ARGUMENT;
   if ((s = check_grad(desc, grad, dx_student)) != LARD_OK) return s;
-  if (!aligned(reserve, 256) || !aligned(grad_loss, 4)) return LARD_ERR_INVALID_ARGUMENT;
-  if (reserve_bytes < reserve_of(desc, Path::kRope).total) return LARD_ERR_WORKSPACE_TOO_SMALL;
-  const size_t need = bwd_workspace(1, &desc);
-  if (need > 0 && (!workspace || !aligned(workspace, 16))) return LARD_ERR_INVALID_ARGUMENT;
-  if (workspace_bytes < need) return LARD_ERR_WORKSPACE_TOO_SMALL;
+  if (reserve_bytes < reserve_total(desc, Path::kRope)) return LARD_ERR_WORKSPACE_TOO_SMALL;
+  s = check_bwd_workspace(workspace, workspace_bytes, bwd_workspace(1, &desc));
+  if (s != LARD_OK) return s;
   const size_t off = 0;
   const void* none = nullptr;
-  return run_group_bwd(1, &desc, &none, &none, &rope, true, static_cast<const char*>(reserve),
-                       &off, grad_loss, &grad, &dx_student, static_cast<float*>(workspace),
-                       stream);
+  return run_group_bwd(1, &desc, &none, &none, &lse_teacher, &lse_student, &diag_delta, &rope,
+                       true, static_cast<const char*>(reserve), &off, grad_loss, &grad,
+                       &dx_student, static_cast<float*>(workspace), stream);
 }
 
 size_t lard_relkl_cross_reserve_size(const lard_relkl_desc* desc, lard_status* status) {
   const lard_status s = check_desc(desc);
   if (status) *status = s;
   if (s != LARD_OK) return 0;
-  return reserve_of(desc, Path::kCross).total;
+  return reserve_total(desc, Path::kCross);
 }
 
 lard_status lard_relkl_cross_fwd(const lard_relkl_desc* desc, const lard_cross_desc* keys,
@@ -637,7 +637,7 @@ lard_status lard_relkl_cross_fwd(const lard_relkl_desc* desc, const lard_cross_d
   if (rope && (s = check_rope(rope)) != LARD_OK) return s;
   if ((s = check_inputs(a_teacher, a_student)) != LARD_OK) return s;
   if ((s = check_inputs(b_teacher, b_student)) != LARD_OK) return s;
-  if ((s = check_fwd_outputs(lse_teacher, lse_student, row_kl)) != LARD_OK) return s;
+  if ((s = check_fwd_outputs(lse_teacher, lse_student, nullptr, row_kl)) != LARD_OK) return s;
   if (!loss || !workspace || !reserve) return LARD_ERR_INVALID_ARGUMENT;
   if (!aligned(workspace, 8) || !aligned(reserve, 256) || !aligned(loss, 4))
     return LARD_ERR_INVALID_ARGUMENT;
@@ -655,29 +655,30 @@ lard_status lard_relkl_cross_fwd(const lard_relkl_desc* desc, const lard_cross_d
   launch_init(P);
   prep_member(P, desc, a_teacher, desc->t_stride_b, desc->t_stride_h, desc->t_stride_n,
               a_student, desc->s_stride_b, desc->s_stride_h, desc->s_stride_n, rope,
-              rb + R.x16_t, rb + R.x16_s);
+              rb + R.x_t, rb + R.x_s);
   prep_member(P, desc, b_teacher, keys->bt_stride_b, keys->bt_stride_h, keys->bt_stride_n,
               b_student, keys->bs_stride_b, keys->bs_stride_h, keys->bs_stride_n, rope,
-              rb + R.y16_t, rb + R.y16_s);
+              rb + R.y_t, rb + R.y_s);
   memcpy(P.head_map, maps.v, sizeof(maps.v));
   P.m[0].map_off = P.m[1].map_off = maps.off[0];
-  if (launch_rope_prep(P, bf16, desc->d, stream) != 0) return LARD_ERR_HIP;
+  if (launch_rope_prep(P, bf16, desc->d, stream, /*f16_images=*/true) != 0) return LARD_ERR_HIP;
 
   // 2. the forward: own rows from the A copies, key tiles from the B copies
   FwdLaunch F;
   launch_init(F);
   FwdArgs& a = add_member(F, (int)fwd_partials(desc));
-  fwd_copies(a, desc, rb + R.x16_t, rb + R.x16_s, rb + R.y16_t, rb + R.y16_s);
-  fwd_common(a, desc, rb, R, false, lse_teacher, lse_student, row_kl,
+  fwd_copies(a, desc, rb + R.x_t, rb + R.x_s, rb + R.y_t, rb + R.y_s);
+  fwd_common(a, desc, lse_teacher, lse_student, nullptr, row_kl,
              static_cast<double*>(workspace));
   identity_maps(F);
   const LossOut lo = loss_out(F, static_cast<double*>(workspace), loss, nullptr);
-  const int e = launch_fwd(F, bf16, desc->d, desc->causal == 1, lo, stream, /*f16_copies=*/bf16);
+  const int e = launch_fwd(F, bf16, desc->d, desc->causal == 1, lo, stream, /*cross=*/true);
   return e == 0 ? LARD_OK : LARD_ERR_HIP;
 }
 
 lard_status lard_relkl_cross_bwd(const lard_relkl_desc* desc, const lard_rope_desc* rope,
                                  const void* reserve, size_t reserve_bytes,
+                                 const float* lse_teacher, const float* lse_student,
                                  const float* grad_loss, const lard_grad_desc* grad_a,
                                  void* da_student, const lard_grad_desc* grad_b,
                                  void* db_student, void* workspace, size_t workspace_bytes,
@@ -685,19 +686,20 @@ lard_status lard_relkl_cross_bwd(const lard_relkl_desc* desc, const lard_rope_de
   lard_status s = check_desc(desc);
   if (s != LARD_OK) return s;
   if (rope && (s = check_rope(rope)) != LARD_OK) return s;
-  if (!reserve || !grad_loss) return LARD_ERR_INVALID_ARGUMENT;
+  if (!reserve || !aligned(reserve, 256)) return LARD_ERR_INVALID_ARGUMENT;
+  if ((s = check_bwd_state(lse_teacher, lse_student, nullptr, false)) != LARD_OK) return s;
+  if (!grad_loss || !aligned(grad_loss, 4)) return LARD_ERR_INVALID_ARGUMENT;
   if ((s = check_grad(desc, grad_a, da_student)) != LARD_OK) return s;
   if ((s = check_grad(desc, grad_b, db_student)) != LARD_OK) return s;
-  if (!aligned(reserve, 256) || !aligned(grad_loss, 4)) return LARD_ERR_INVALID_ARGUMENT;
   const ReserveLayout R = reserve_of(desc, Path::kCross);
   if (reserve_bytes < R.total) return LARD_ERR_WORKSPACE_TOO_SMALL;
-  const size_t need = bwd_workspace(1, &desc);
-  if (need > 0 && (!workspace || !aligned(workspace, 16))) return LARD_ERR_INVALID_ARGUMENT;
-  if (workspace_bytes < need) return LARD_ERR_WORKSPACE_TOO_SMALL;
+  s = check_bwd_workspace(workspace, workspace_bytes, bwd_workspace(1, &desc));
+  if (s != LARD_OK) return s;
   const char* rb = static_cast<const char*>(reserve);
   const int splits = choose_splits(1, &desc);
   MapTable maps;
   build_maps(maps, 1, &desc);
+  float* part = static_cast<float*>(workspace);
 
   // Both passes use the statistics of the query rows (rows of A).
   auto pass = [&](size_t own_t, size_t own_s, size_t stg_t, size_t stg_s,
@@ -705,8 +707,8 @@ lard_status lard_relkl_cross_bwd(const lard_relkl_desc* desc, const lard_rope_de
     BwdLaunch L;
     launch_init(L);
     BwdArgs& a = add_member(L, bwd_workgroups(desc, splits));
-    bwd_copies(a, desc, rb, own_t, own_s, stg_t, stg_s);
-    bwd_common(a, desc, rb, R, splits, grad_loss, g, dx, static_cast<float*>(workspace));
+    bwd_copies(a, rb, own_t, own_s, stg_t, stg_s);
+    bwd_common(a, desc, lse_teacher, lse_student, splits, nullptr, grad_loss, g, dx, part);
     if (rope) {
       a.rope_cos = rope->cos_student;
       a.rope_sin = rope->sin_student;
@@ -715,10 +717,10 @@ lard_status lard_relkl_cross_bwd(const lard_relkl_desc* desc, const lard_rope_de
     return run_bwd(L, &desc, g->dtype == LARD_FP32, mode, stream);
   };
   // dA: own rows of A, staged rows of B, row terms
-  s = pass(R.x16_t, R.x16_s, R.y16_t, R.y16_s, grad_a, da_student, 1);
+  s = pass(R.x_t, R.x_s, R.y_t, R.y_s, grad_a, da_student, 1);
   if (s != LARD_OK) return s;
   // dB: own rows of B, staged rows of A with their statistics, column terms
-  return pass(R.y16_t, R.y16_s, R.x16_t, R.x16_s, grad_b, db_student, 2);
+  return pass(R.y_t, R.y_s, R.x_t, R.x_s, grad_b, db_student, 2);
 }
 
 // ------------------------------------------------------------------ grouped entry points
@@ -753,31 +755,35 @@ lard_status lard_relkl_group_fwd(int n, const lard_relkl_member* members, int wi
   const void* xs[LARD_MAX_GROUP];
   float* lt[LARD_MAX_GROUP];
   float* ls[LARD_MAX_GROUP];
+  float* dg[LARD_MAX_GROUP];
   float* kl[LARD_MAX_GROUP];
   float* ml[LARD_MAX_GROUP];
   const lard_rope_desc* rp[LARD_MAX_GROUP];
   for (int k = 0; k < n; ++k) {
     const lard_relkl_member& m = members[k];
     if ((s = check_inputs(m.x_teacher, m.x_student)) != LARD_OK) return s;
-    if ((s = check_fwd_outputs(m.lse_teacher, m.lse_student, m.row_kl)) != LARD_OK) return s;
+    if ((s = check_fwd_outputs(m.lse_teacher, m.lse_student, m.diag_delta, m.row_kl)) != LARD_OK)
+      return s;
     if (m.loss && !aligned(m.loss, 4)) return LARD_ERR_INVALID_ARGUMENT;
     if (with_rope && (s = check_rope(&m.rope)) != LARD_OK) return s;
     xt[k] = m.x_teacher;
     xs[k] = m.x_student;
     lt[k] = m.lse_teacher;
     ls[k] = m.lse_student;
+    dg[k] = m.diag_delta;
     kl[k] = m.row_kl;
     ml[k] = m.loss;
     rp[k] = &m.rope;
   }
-  if (!loss || !workspace || !reserve) return LARD_ERR_INVALID_ARGUMENT;
-  if (!aligned(workspace, 8) || !aligned(reserve, 256) || !aligned(loss, 4))
-    return LARD_ERR_INVALID_ARGUMENT;
+  if (!loss || !workspace) return LARD_ERR_INVALID_ARGUMENT;
+  if (!aligned(workspace, 8) || !aligned(loss, 4)) return LARD_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < fwd_workspace(n, d)) return LARD_ERR_WORKSPACE_TOO_SMALL;
   size_t off[LARD_MAX_GROUP];
   const Path path = with_rope ? Path::kRope : Path::kPlain;
-  if (reserve_bytes < group_reserve(n, d, path, off)) return LARD_ERR_WORKSPACE_TOO_SMALL;
-  return run_group_fwd(n, d, xt, xs, lt, ls, kl, ml, rp, with_rope == 1, loss,
+  const size_t need = group_reserve(n, d, path, off);
+  if (need > 0 && (!reserve || !aligned(reserve, 256))) return LARD_ERR_INVALID_ARGUMENT;
+  if (reserve_bytes < need) return LARD_ERR_WORKSPACE_TOO_SMALL;
+  return run_group_fwd(n, d, xt, xs, lt, ls, dg, kl, ml, rp, with_rope == 1, loss,
                        static_cast<char*>(reserve), off, static_cast<double*>(workspace),
                        stream);
 }
@@ -791,9 +797,13 @@ lard_status lard_relkl_group_bwd(int n, const lard_relkl_member* members, int wi
   lard_status s = check_group(n, members, d);
   if (s != LARD_OK) return s;
   if (with_rope != 0 && with_rope != 1) return LARD_ERR_INVALID_ARGUMENT;
-  if (!reserve || !grad_loss || !grads || !dx_student) return LARD_ERR_INVALID_ARGUMENT;
+  if (!grad_loss || !grads || !dx_student) return LARD_ERR_INVALID_ARGUMENT;
+  if (!aligned(grad_loss, 4)) return LARD_ERR_INVALID_ARGUMENT;
   const void* xt[LARD_MAX_GROUP];
   const void* xs[LARD_MAX_GROUP];
+  const float* lt[LARD_MAX_GROUP];
+  const float* ls[LARD_MAX_GROUP];
+  const float* dg[LARD_MAX_GROUP];
   const lard_rope_desc* rp[LARD_MAX_GROUP];
   const lard_grad_desc* g[LARD_MAX_GROUP];
   void* dx[LARD_MAX_GROUP];
@@ -801,23 +811,29 @@ lard_status lard_relkl_group_bwd(int n, const lard_relkl_member* members, int wi
     const lard_relkl_member& m = members[k];
     if (!with_rope && (s = check_inputs(m.x_teacher, m.x_student)) != LARD_OK) return s;
     if (with_rope && (s = check_rope(&m.rope)) != LARD_OK) return s;
+    if ((s = check_bwd_state(m.lse_teacher, m.lse_student, m.diag_delta, true)) != LARD_OK)
+      return s;
     if ((s = check_grad(d[k], &grads[k], dx_student[k])) != LARD_OK) return s;
     if (grads[k].dtype != grads[0].dtype) return LARD_ERR_INVALID_ARGUMENT;
     xt[k] = m.x_teacher;
     xs[k] = m.x_student;
+    lt[k] = m.lse_teacher;
+    ls[k] = m.lse_student;
+    dg[k] = m.diag_delta;
     rp[k] = &m.rope;
     g[k] = &grads[k];
     dx[k] = dx_student[k];
   }
-  if (!aligned(reserve, 256) || !aligned(grad_loss, 4)) return LARD_ERR_INVALID_ARGUMENT;
   size_t off[LARD_MAX_GROUP];
   const Path path = with_rope ? Path::kRope : Path::kPlain;
-  if (reserve_bytes < group_reserve(n, d, path, off)) return LARD_ERR_WORKSPACE_TOO_SMALL;
-  const size_t need = bwd_workspace(n, d);
-  if (need > 0 && (!workspace || !aligned(workspace, 16))) return LARD_ERR_INVALID_ARGUMENT;
-  if (workspace_bytes < need) return LARD_ERR_WORKSPACE_TOO_SMALL;
-  return run_group_bwd(n, d, xt, xs, rp, with_rope == 1, static_cast<const char*>(reserve),
-                       off, grad_loss, g, dx, static_cast<float*>(workspace), stream);
+  const size_t need = group_reserve(n, d, path, off);
+  if (need > 0 && (!reserve || !aligned(reserve, 256))) return LARD_ERR_INVALID_ARGUMENT;
+  if (reserve_bytes < need) return LARD_ERR_WORKSPACE_TOO_SMALL;
+  s = check_bwd_workspace(workspace, workspace_bytes, bwd_workspace(n, d));
+  if (s != LARD_OK) return s;
+  return run_group_bwd(n, d, xt, xs, lt, ls, dg, rp, with_rope == 1,
+                       static_cast<const char*>(reserve), off, grad_loss, g, dx,
+                       static_cast<float*>(workspace), stream);
 }
 
 }  // extern "C"

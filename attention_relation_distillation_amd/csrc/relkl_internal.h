@@ -20,35 +20,25 @@ constexpr int kBC = 64;                   // rows of one key tile staged in LDS
 
 inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
-// Phase-1 state the forward leaves for the backward ("reserve"), per relation head unit:
-//  * copies of the teacher and student rows, dense [units][N][d] each: IEEE fp16 copies
-//    of bf16 inputs (the backward's operands; bf16 -> fp16 is exact for
-//    2^-17 <= |x| < 65504), and for the RoPE-fused entry points the rotated rows, in fp16
-//    (bf16 inputs) or fp32 (fp32 inputs); none for fp32 inputs otherwise;
-//  * row statistics in log2 units, r = log2(sum_j 2^(S_ij c2 + b_i)) - b_i - 14, dense
-//    [units][Npad] with Npad = N rounded up to kBC, for teacher and student, so that
-//    R(i, j) * 2^14 = exp2(S_ij c2 - r_i).
+// Caller-owned "reserve" of the RoPE-fused and cross entry points: the rotated (or copied)
+// rows the kernels read in place of the caller's tensors, dense [units][N][d] per matrix:
+// x_t, x_s (the relation's rows, or the cross relation's A) and, for the cross relation,
+// y_t, y_s (its B).  Elements are copy_bytes wide: the input dtype for the relation (bf16 or
+// fp32), fp16 images of the bf16 values (or fp32) for the cross relation.  The plain entry
+// points need no reserve: the forward's per-row outputs are the whole state.
 struct ReserveLayout {
-  size_t x16_t, x16_s, y16_t, y16_s, r_t, r_s, total;
-  int64_t npad;
+  size_t x_t, x_s, y_t, y_s, total;
 };
 
-// copy_bytes: bytes per element of the row copies (0: none, 2: fp16, 4: fp32); cross: the
-// key-side matrices get copies too (y16_*), otherwise y16_* equal x16_*.
 inline ReserveLayout reserve_layout(int64_t units, int64_t N, int64_t d, int copy_bytes,
                                     bool cross = false) {
   ReserveLayout L;
-  L.npad = round_up(N, kBC);
   const size_t copy = (size_t)round_up(units * N * d * copy_bytes, 256);
-  const size_t stats = (size_t)round_up(units * L.npad * 4, 256);
-  const size_t ncopy = cross ? 4 : 2;
-  L.x16_t = 0;
-  L.x16_s = copy;
-  L.y16_t = cross ? 2 * copy : L.x16_t;
-  L.y16_s = cross ? 3 * copy : L.x16_s;
-  L.r_t = ncopy * copy;
-  L.r_s = ncopy * copy + stats;
-  L.total = ncopy * copy + 2 * stats;
+  L.x_t = 0;
+  L.x_s = copy;
+  L.y_t = cross ? 2 * copy : L.x_t;
+  L.y_s = cross ? 3 * copy : L.x_s;
+  L.total = (cross ? 4 : 2) * copy;
   return L;
 }
 
@@ -61,25 +51,21 @@ struct FwdArgs {
   int64_t s_sb, s_sh, s_sn;
   int32_t B, H, N;
   int32_t row_tiles;  // ceil(N / kBR)
-  int32_t npad;       // reserve statistics stride per unit
   float scale;        // logit scale
   float c2;           // scale * log2(e)
   float* lse_t;
   float* lse_s;
   float* row_kl;      // may be null
+  float* diag_delta;  // R_s(i,i) - R_t(i,i) per row (the relation; null for the cross relation)
   double* partial;    // [B*H*row_tiles]
-  uint16_t* x16_t;    // reserve fp16 copies (bf16 inputs) or null
-  uint16_t* x16_s;
-  float* r_t;         // reserve log2 statistics
-  float* r_s;
   int32_t map_off;    // head map: offset in the launch's table, or -1 (identity)
 };
 
 struct BwdArgs {
-  const void* x_t;    // own rows (read by the fp32 path)
+  const void* x_t;    // own rows: the caller's tensors (strides below) or dense copies
   const void* x_s;
-  const void* y_t;    // staged rows, fp32 path with x_unit_dense (cross relation: the other
-  const void* y_s;    // matrix; the relation: x)
+  const void* y_t;    // staged rows with x_dense (cross relation: the other matrix; the
+  const void* y_s;    // relation: x)
   int64_t t_sb, t_sh, t_sn;
   int64_t s_sb, s_sh, s_sn;
   int64_t g_sb, g_sh, g_sn;  // gradient strides (elements)
@@ -87,21 +73,17 @@ struct BwdArgs {
   int32_t row_tiles;   // ceil(N / kBRB)
   int32_t key_tiles;   // ceil(N / kBC)
   int32_t splits;      // split-K count over key tiles
-  int32_t npad;
   float scale;
   float c2;
-  const uint16_t* x16_t;  // reserve fp16 copies of the own rows (bf16 path)
-  const uint16_t* x16_s;
-  const uint16_t* y16_t;  // ... and of the staged rows (the same for the relation)
-  const uint16_t* y16_s;
-  const float* r_t;       // log2 statistics of the own rows
-  const float* r_s;
-  const float* rc_t;      // ... and of the staged rows (the same for the relation)
-  const float* rc_s;
+  const float* lse_t;     // the forward's LSE (nats, dense [units][N]) of the own rows
+  const float* lse_s;
+  const float* lc_t;      // ... and of the staged rows (the same for the relation; the
+  const float* lc_s;      // cross relation's query rows in both of its passes)
+  const float* diag_delta;  // R_s(i,i) - R_t(i,i) per own row (relation), or null
   const float* grad_loss;
   const float* rope_cos;  // student RoPE tables [N][d/2] (fused entry points) or null:
   const float* rope_sin;  // the gradient is rotated back before it is written
-  int32_t x_unit_dense;   // fp32 path: x_t / x_s are dense [unit][N][d] copies
+  int32_t x_dense;        // x_* / y_* are dense [unit][N][d] copies (else x_* in place)
   void* dx;            // final gradient (splits == 1)
   float* partial;      // [splits][B*H][row_tiles*kBRB][d] (splits > 1)
   int32_t map_off;
@@ -167,13 +149,15 @@ struct LossOut {
 
 // Each returns a hipError_t value (0 on success).  `in_bf16`: input dtype; `out_f32`:
 // gradient dtype (fp32 or the input dtype).
-// f16_copies: the inputs are the reserve's fp16 copies (RoPE-fused path, bf16 inputs).
+// cross: the cross relation (own rows and key rows from different matrices; no diagonal
+// reference; bf16 inputs arrive as the reserve's fp16 images).
 int launch_fwd(const FwdLaunch& a, bool in_bf16, int d, bool causal, const LossOut& loss,
-               void* stream, bool f16_copies = false);
+               void* stream, bool cross = false);
 // mode: 0 relation gradient, 1 cross dA pass, 2 cross dB pass (see relkl_bwd_kernel).
 int launch_bwd(const BwdLaunch& a, bool in_bf16, int d, bool causal, bool out_f32,
                void* stream, int mode = 0);
 int launch_splitk_reduce(const ReduceLaunch& a, bool out_f32, void* stream);
-int launch_rope_prep(const PrepLaunch& a, bool in_bf16, int d, void* stream);
+// f16_images: write bf16 rows as their fp16 images (cross relation), else in the input dtype.
+int launch_rope_prep(const PrepLaunch& a, bool in_bf16, int d, void* stream, bool f16_images);
 
 }  // namespace lard

@@ -23,15 +23,18 @@
 //    row i and 16 of its columns j: row statistics reduce inside the lane, and the
 //    probability block is already in the A-operand layout of the gradient contraction.
 //  * Forward: one online sweep per row keeps (bias, sum, sum of e_t (S_t - S_s)) for
-//    teacher and student; the two half-waves sharing a row merge at the end.  It also
-//    writes the reserve: fp16 copies of its rows (bf16 inputs) and the row statistics
-//    in log2 units.
+//    teacher and student; the two half-waves sharing a row merge at the end.  For the
+//    relation the diagonal score S_ii = |X_i|^2 is the row's reference: it is computed in
+//    fp64 from the row itself, sets the initial bias and is added to the sums exactly at the
+//    end, so that the KL of nearly equal rows keeps relative precision.  Outputs are per row
+//    only: LSE of both sides, the row KL, and R_s(i,i) - R_t(i,i) for the backward.
 //  * Backward: the owner of a row tile sweeps the whole row (all key tiles), forms
 //    W = dZ + dZ^T block by block (row statistics below the diagonal, column statistics
-//    above it, both on it), carries W * 2^14 as fp16 and accumulates W X_s on
-//    v_mfma_f32_32x32x16_f16, reading X_s transposed from the row-major key tile with
-//    ds_read_b64_tr_b16.  No atomics: every output row has one owner (times an optional
-//    split over key tiles reduced in a fixed order).
+//    above it, both on it; the diagonal entry from the forward), carries W * 2^14 as fp16
+//    and accumulates W X_s on v_mfma_f32_32x32x16_f16, reading X_s transposed from an fp16
+//    image of the staged key tile with ds_read_b64_tr_b16.  The row statistics are the
+//    forward's LSE vectors, staged with each key tile.  No atomics: every output row has
+//    one owner (times an optional split over key tiles reduced in a fixed order).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -64,21 +67,36 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 // ------------------------------------------------------------------ element traits
 // A "fragment" is 8 consecutive elements along d of one row: the k-chunk one lane
-// supplies to a 16-deep step of the score contraction.
-struct Bf16In {  // bf16 inputs as given by the caller (forward)
+// supplies to a 16-deep step of the score contraction.  frag_t is the score operand type,
+// gfrag_t the type of the gradient contraction's operands (the staged student rows and W).
+struct Bf16In {  // bf16 inputs (forward)
   using elem_t = uint16_t;
   using frag_t = bf16x8;
+  using gfrag_t = bf16x8;
   static constexpr int kES = 2;
+  static constexpr bool kConvert = false;
 };
-struct F16Op {   // fp16 reserve copies (backward of bf16 inputs)
+struct Bf16Op {  // bf16 inputs in the backward: scores on the bf16 rows as given, the
+                 // gradient on an IEEE fp16 image of each staged student tile, made in LDS
+  using elem_t = uint16_t;
+  using frag_t = bf16x8;
+  using gfrag_t = f16x8;
+  static constexpr int kES = 2;
+  static constexpr bool kConvert = true;
+};
+struct F16Op {   // fp16 images of bf16 values (the cross relation's reserve copies)
   using elem_t = uint16_t;
   using frag_t = f16x8;
+  using gfrag_t = f16x8;
   static constexpr int kES = 2;
+  static constexpr bool kConvert = false;
 };
 struct F32In {   // fp32 inputs (forward and backward)
   using elem_t = float;
   using frag_t = f32x8;
+  using gfrag_t = f32x8;
   static constexpr int kES = 4;
+  static constexpr bool kConvert = false;
 };
 
 __device__ __forceinline__ f32x16 mma_k16(const bf16x8& a, const bf16x8& b, f32x16 c) {
@@ -172,6 +190,11 @@ __device__ __forceinline__ void lds_copy16(const void* g, uint32_t lds_base) {
 __device__ __forceinline__ void lds_copy16_s(uint32_t voff, const void* sbase, uint32_t lds_base) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
                "{m0}"(lds_base) : "memory");
+}
+
+// LDS copy of 4 bytes per lane (lane l writes lds_base + 4 l), as lds_copy16.
+__device__ __forceinline__ void lds_copy4(const void* g, uint32_t lds_base) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds_base) : "memory");
 }
 
 // Workgroup barrier of the backward's tile pipeline.  It completes this wave's LDS reads
@@ -310,13 +333,15 @@ struct LoadSchedule {
 // ------------------------------------------------------------------ forward
 // Online update of one lane's row statistics with the 16 columns it holds of a 32x32
 // score block (raw scores S; logits z = scale S; c2 = scale log2 e).
-//   b: exponent bias in use, b = -(running max of S) * c2, rounded once;
+//   b: exponent bias in use (fp32), the sums are taken as exp2(S c2 + b);
 //   l: sum of exp2(S c2 + b);  acc_a: sum of exp2(S_t c2 + b_t) (S_t - S_s).
 // The bias is carried as the exact fp32 value that entered every exponent, so the
 // rescale factors (exp2(b_new - b_old)) and the final LSE / KL use exactly the offsets
-// the sums were taken with; a rounded "max * c2" never has to cancel against itself.
-// Masked columns contribute exactly zero (the select is on the exponential itself).
-template <bool MASK, bool CAUSAL>
+// the sums were taken with.  A block keeps the bias in use unless its largest exponent
+// would exceed 2^32; then the bias moves to the block's maximum.  Masked columns contribute
+// exactly zero (the select is on the exponential itself).  REL: the relation, whose
+// diagonal entry j == i is left out of the sums (the kernel adds it exactly at the end).
+template <bool MASK, bool CAUSAL, bool REL>
 __device__ __forceinline__ void online_update(const f32x16& st, const f32x16& ss, int jb0, int i,
                                               int hh, int N, float c2, float& b_t, float& l_t,
                                               float& acc_a, float& b_s, float& l_s) {
@@ -324,7 +349,7 @@ __device__ __forceinline__ void online_update(const f32x16& st, const f32x16& ss
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int j = jb0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-    keep[r] = !MASK || ((j < N) && (!CAUSAL || j <= i));
+    keep[r] = !MASK || ((j < N) && (!CAUSAL || j <= i) && (!REL || j != i));
   }
   float mx_t = kNegBig, mx_s = kNegBig;
 #pragma unroll
@@ -332,7 +357,8 @@ __device__ __forceinline__ void online_update(const f32x16& st, const f32x16& ss
     mx_t = fmaxf(mx_t, keep[r] ? st[r] : kNegBig);
     mx_s = fmaxf(mx_s, keep[r] ? ss[r] : kNegBig);
   }
-  const float bn_t = fminf(b_t, -mx_t * c2), bn_s = fminf(b_s, -mx_s * c2);
+  const float bn_t = fmaf(mx_t, c2, b_t) > 32.f ? -mx_t * c2 : b_t;
+  const float bn_s = fmaf(mx_s, c2, b_s) > 32.f ? -mx_s * c2 : b_s;
   const float alpha_t = fast_exp2(bn_t - b_t);
   const float alpha_s = fast_exp2(bn_s - b_s);
   float e_t[16], e_s[16], dd[16];
@@ -365,9 +391,10 @@ __device__ __forceinline__ void online_update(const f32x16& st, const f32x16& ss
 // the lane's current biases as they are, so no block maximum is formed.  The block is
 // accumulated only if both block sums are at most 2^64, which bounds every exponential
 // (and rules out inf / NaN); then the running sums stay finite and exact in the sense of
-// the bias form above.  Otherwise (a row's first block, whose bias is still the empty-row
-// value, or a row maximum that grew by more than 64 in log2 units) nothing is changed and
-// the caller runs the exact path.  Returns whether the block was accumulated.
+// the bias form above.  Otherwise (a row's first block when the bias is still the
+// empty-row value of the cross relation, or a row maximum that grew by more than 64 in log2
+// units over the bias) nothing is changed and the caller runs the exact path.  Returns
+// whether the block was accumulated.
 __device__ __forceinline__ bool online_update_fast(const f32x16& st, const f32x16& ss, float c2,
                                                    float b_t, float b_s, float& l_t,
                                                    float& acc_a, float& l_s) {
@@ -449,7 +476,33 @@ __device__ __forceinline__ void score_pipeline(const char* tile_t, const char* t
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <class In, int D, bool CAUSAL>
+// Sum of squares of this lane's part of its row (8 elements per fragment), in fp64: the
+// products of bf16 or fp32 values are exact there, and so is, up to 2^-53, their sum.
+template <class In, int D>
+__device__ __forceinline__ double row_sq_sum(const typename In::frag_t (&q)[D / 16]) {
+  double acc = 0.0;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    if constexpr (In::kES == 2) {
+      const u32x4 w = __builtin_bit_cast(u32x4, q[ks]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const double lo = (double)__uint_as_float(w[e] << 16);
+        const double hi = (double)__uint_as_float(w[e] & 0xffff0000u);
+        acc = fma(lo, lo, acc);
+        acc = fma(hi, hi, acc);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = fma((double)q[ks][e], (double)q[ks][e], acc);
+    }
+  }
+  return acc;
+}
+
+// REL: the relation softmax(scale X X^T); its diagonal score S_ii = |X_i|^2 is the row's
+// reference (below).  !REL: the cross relation softmax(scale A B^T), no reference entry.
+template <class In, int D, bool CAUSAL, bool REL>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void relkl_fwd_kernel(const FwdLaunch L) {
   using elem_t = typename In::elem_t;
@@ -508,38 +561,41 @@ void relkl_fwd_kernel(const FwdLaunch L) {
       qs[ks] = frag_t{};
     }
   }
-  if constexpr (std::is_same_v<In, Bf16In>) {
-    // reserve: fp16 copies of this lane's part of its row (inputs that are already fp16
-    // copies, made by rope_prep_kernel, are in the reserve)
-    if (row < N) {
-      const int64_t o = ((int64_t)unit * N + row) * D + 8 * hh;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        *reinterpret_cast<u32x4*>(a.x16_t + o + 16 * ks) = bf16x8_to_f16x8_bits(qt[ks]);
-        *reinterpret_cast<u32x4*>(a.x16_s + o + 16 * ks) = bf16x8_to_f16x8_bits(qs[ks]);
-      }
-    }
-  }
 
   const int fbase = frag_base<In, D>(l32, hh);
   const float c2 = a.c2;
   const float b_init = -kNegBig * c2;  // bias of an empty row: every real bias is below it
   float b_t = b_init, l_t = 0.f, acc_a = 0.f, b_s = b_init, l_s = 0.f;
+  // The relation's diagonal entry carries most of a row's mass (S_ii = |X_i|^2 against
+  // off-diagonal scores of about |X|), so in fp32 its own rounding would dominate the KL
+  // of nearly equal teacher and student rows.  It is therefore left out of the sweep and
+  // added exactly at the end, from S_ii in fp64 (the two half-waves holding the row each
+  // sum their half).  The row's bias starts at -c2 S_ii, which makes the diagonal's own
+  // exponential 2^rho with rho the (tiny) rounding residual of that bias.
+  double sq_t = 0.0, sq_s = 0.0;
+  if constexpr (REL) {
+    sq_t = row_sq_sum<In, D>(qt);
+    sq_s = row_sq_sum<In, D>(qs);
+    sq_t += __shfl_xor(sq_t, 32);
+    sq_s += __shfl_xor(sq_s, 32);
+    b_t = (float)(-(double)c2 * sq_t);
+    b_s = (float)(-(double)c2 * sq_s);
+  }
 
   // Software pipeline over 32-key blocks, which alternate between two score buffers: the
   // exponentials and sums of a block without masked entries run inside the MFMA sequence of
   // the next block (one element of the 16 per MFMA at d = 128), with both at the raised
   // issue priority.  The order of every sum is that of online_update_fast.  A block with
-  // masked entries (the diagonal or the ragged end: always a wave's last) and the exact
-  // fallback run on their own.
+  // masked entries (the diagonal block of the relation, the causal diagonal block, the
+  // ragged end) and the exact fallback run on their own.
   f32x16 stA = f32x16{}, ssA = f32x16{}, stB = f32x16{}, ssB = f32x16{};
   bool have_p = false, p_mask = false;  // a pending block, whether it has masked entries
   int p_jb0 = 0, p_par = 0;             // its first column, its buffer (A: 0, B: 1)
   auto finish = [&](const f32x16& pt, const f32x16& ps) __attribute__((always_inline)) {
     if (p_mask)
-      online_update<true, CAUSAL>(pt, ps, p_jb0, row, hh, N, c2, b_t, l_t, acc_a, b_s, l_s);
+      online_update<true, CAUSAL, REL>(pt, ps, p_jb0, row, hh, N, c2, b_t, l_t, acc_a, b_s, l_s);
     else if (!online_update_fast(pt, ps, c2, b_t, b_s, l_t, acc_a, l_s))
-      online_update<false, CAUSAL>(pt, ps, p_jb0, row, hh, N, c2, b_t, l_t, acc_a, b_s, l_s);
+      online_update<false, CAUSAL, REL>(pt, ps, p_jb0, row, hh, N, c2, b_t, l_t, acc_a, b_s, l_s);
   };
   // Block jb of the tile: scores into (st, ss) while the pending block (pt, ps) is reduced.
   auto block = [&](auto jbc, int kt, const char* tile_t, const char* tile_s, f32x16& st,
@@ -548,7 +604,7 @@ void relkl_fwd_kernel(const FwdLaunch L) {
     const int jb0 = kt * kBC + 32 * jb;
     if (jb0 >= N) return false;
     if (CAUSAL && jb0 > ib0 + 31) return false;  // above every row of the wave
-    const bool need_mask = (CAUSAL && jb0 + 31 > ib0) || (jb0 + 32 > N);
+    const bool need_mask = (CAUSAL && jb0 + 31 > ib0) || (jb0 + 32 > N) || (REL && jb0 == ib0);
     if (have_p && !p_mask) {
       constexpr int NF = 2 * KS, E = (16 + NF - 1) / NF;  // elements per MFMA slot
       float lt[2] = {0.f, 0.f}, ls[2] = {0.f, 0.f}, aa[2] = {0.f, 0.f};
@@ -579,7 +635,7 @@ void relkl_fwd_kernel(const FwdLaunch L) {
       l_s = ok ? l_s + sum_s : l_s;
       acc_a = ok ? acc_a + sum_a : acc_a;
       if (!ok)
-        online_update<false, CAUSAL>(pt, ps, p_jb0, row, hh, N, c2, b_t, l_t, acc_a, b_s, l_s);
+        online_update<false, CAUSAL, REL>(pt, ps, p_jb0, row, hh, N, c2, b_t, l_t, acc_a, b_s, l_s);
     } else {
       if (have_p) finish(pt, ps);
       // the LDS-bound matrix part issues ahead of the partner wave's vector work
@@ -616,10 +672,7 @@ void relkl_fwd_kernel(const FwdLaunch L) {
     else finish(stB, ssB);
   }
 
-  // Merge the two half-waves (lanes l and l ^ 32 hold the same row) and finish, in log2
-  // units:  LSE = ln2 (log2 L - b),
-  //         KL  = ln2 (c2 A_t / L_t + (b_t - b_s) - log2(L_t / L_s))
-  // (KL_i = E_t[z_t - z_s] - (LSE_t - LSE_s), with the LSE difference taken as a ratio).
+  // Merge the two half-waves (lanes l and l ^ 32 hold the same row) onto one bias.
   const float ob_t = __shfl_xor(b_t, 32), ol_t = __shfl_xor(l_t, 32);
   const float oa = __shfl_xor(acc_a, 32);
   const float ob_s = __shfl_xor(b_s, 32), ol_s = __shfl_xor(l_s, 32);
@@ -629,17 +682,51 @@ void relkl_fwd_kernel(const FwdLaunch L) {
   const float L_t = l_t * f1t + ol_t * f2t;
   const float A_t = acc_a * f1t + oa * f2t;
   const float L_s = l_s * f1s + ol_s * f2s;
-  const float lg_t = log2f(L_t), lg_s = log2f(L_s);
-  const float kl = kLn2 * (c2 * (A_t / L_t) + (B_t - B_s) - log2f(L_t / L_s));
+  // Finish the row, in log2 units: with every term exp2(S c2 + B),
+  //   LSE = ln2 (log2 L - B),
+  //   KL  = ln2 (c2 A_t / L_t + (B_t - B_s) - log2(L_t / L_s))
+  // (KL_i = E_t[z_t - z_s] - (LSE_t - LSE_s), with the LSE difference taken as a ratio).
+  float kl, lse_t, lse_s, dd = 0.f;
+  if constexpr (REL) {
+    // The sums hold the off-diagonal terms (L', A'); the diagonal's own term is 2^rho with
+    // rho = c2 S_ii + B, exact in fp64.  With lambda = L' 2^-rho and D = S_t,ii - S_s,ii:
+    //   KL  = scale (A'_t - D L'_t) / L_t - log1p((lambda_t - lambda_s) / (1 + lambda_s)),
+    //   LSE = scale S_ii + log1p(lambda),
+    //   R_s(i,i) - R_t(i,i) = 1 / (1 + lambda_s) - 1 / (1 + lambda_t),
+    // in which the large diagonal terms have cancelled exactly, so that a row whose KL is
+    // tiny against its LSE keeps relative precision, and a row with no off-diagonal entry
+    // gives KL = 0 and R(i,i) = 1 exactly.  When the bias had to move far below the
+    // diagonal's (a row dominated by other entries, rho < -30) the plain form is used with
+    // the diagonal's term added to the sums.
+    const double rho_t = (double)c2 * sq_t + (double)B_t;
+    const double rho_s = (double)c2 * sq_s + (double)B_s;
+    const float dg = (float)(sq_t - sq_s);  // D = S_t,ii - S_s,ii
+    const float e_t = fast_exp2((float)rho_t), e_s = fast_exp2((float)rho_s);
+    if (rho_t >= -30.0 && rho_s >= -30.0) {
+      const float lam_t = L_t / e_t, lam_s = L_s / e_s;
+      kl = a.scale * ((A_t - dg * L_t) / (e_t + L_t)) - log1pf((lam_t - lam_s) / (1.f + lam_s));
+      dd = (lam_t - lam_s) / ((1.f + lam_s) * (1.f + lam_t));
+      lse_t = (float)((double)a.scale * sq_t + (double)log1pf(lam_t));
+      lse_s = (float)((double)a.scale * sq_s + (double)log1pf(lam_s));
+    } else {
+      const float Lt = e_t + L_t, Ls = e_s + L_s, At = fmaf(e_t, dg, A_t);
+      kl = kLn2 * (c2 * (At / Lt) + (B_t - B_s) - log2f(Lt / Ls));
+      dd = e_s / Ls - e_t / Lt;
+      lse_t = (log2f(Lt) - B_t) * kLn2;
+      lse_s = (log2f(Ls) - B_s) * kLn2;
+    }
+  } else {
+    kl = kLn2 * (c2 * (A_t / L_t) + (B_t - B_s) - log2f(L_t / L_s));
+    lse_t = (log2f(L_t) - B_t) * kLn2;
+    lse_s = (log2f(L_s) - B_s) * kLn2;
+  }
   double kl_sum = 0.0;
   if (hh == 0 && row < N) {
     const int64_t o = (int64_t)unit * N + row;
-    a.lse_t[o] = (lg_t - B_t) * kLn2;
-    a.lse_s[o] = (lg_s - B_s) * kLn2;
+    a.lse_t[o] = lse_t;
+    a.lse_s[o] = lse_s;
     if (a.row_kl) a.row_kl[o] = kl;
-    const int64_t ro = (int64_t)unit * a.npad + row;
-    a.r_t[ro] = (lg_t - B_t) - kWScaleLog2;
-    a.r_s[ro] = (lg_s - B_s) - kWScaleLog2;
+    if (REL && a.diag_delta) a.diag_delta[o] = dd;
     kl_sum = (double)kl;
   }
   // Deterministic workgroup sum in fp64.
@@ -685,12 +772,15 @@ __global__ __launch_bounds__(256) void loss_reduce_kernel(const LossOut o) {
 // ROW / COL: which terms the block takes (the symmetric relation: both where the mask keeps
 // them -- the row term below the diagonal, the column term above, both on the diagonal
 // block; the cross relation's dA pass only row terms, its dB pass only column terms);
-// DIAG: the diagonal block, masked per element; TAIL zeroes columns j >= N (their staged
-// rows and statistics are copies of row N-1).
-template <bool ROW, bool COL, bool DIAG, bool TAIL>
+// DIAG: the causal diagonal block, masked per element; TAIL zeroes columns j >= N (their
+// staged rows and statistics are copies of row N-1); SUB: the block holds the relation's
+// diagonal entry (i, i), which takes wd2 = 2 (R_s(i,i) - R_t(i,i)) 2^14 as given by the
+// forward (row and column term) instead of the recomputed difference: with R(i,i) near 1
+// the fp32 statistics cannot resolve it.
+template <bool ROW, bool COL, bool DIAG, bool TAIL, bool SUB = false>
 __device__ __forceinline__ void make_w(const f32x16& st, const f32x16& ss, float rt, float rs,
                                        const float* clt, const float* cls, int hh, int di,
-                                       int n_left, float c2, f32x8 (&w32)[2]) {
+                                       int n_left, float c2, float wd2, f32x8 (&w32)[2]) {
   float wv[16];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -715,6 +805,7 @@ __device__ __forceinline__ void make_w(const f32x16& st, const f32x16& ss, float
         if constexpr (ROW) v += cm;
         else v = cm;
       }
+      if constexpr (SUB) v = dj == di ? wd2 : v;
       if constexpr (TAIL) v = dj < n_left ? v : 0.f;
       wv[r] = v;
     }
@@ -726,7 +817,7 @@ __device__ __forceinline__ void make_w(const f32x16& st, const f32x16& ss, float
 }
 
 template <class Op>
-__device__ __forceinline__ typename Op::frag_t w_frag(const f32x8& w) {
+__device__ __forceinline__ typename Op::gfrag_t w_frag(const f32x8& w) {
   if constexpr (Op::kES == 2) {
     return __builtin_convertvector(w, f16x8);  // round to nearest even, two per instruction
   } else {
@@ -752,8 +843,8 @@ __device__ __forceinline__ int trb_base(int lane, int half) {
 }
 
 template <class Op, int D>
-__device__ __forceinline__ typename Op::frag_t grad_bfrag(const char* tile, int jbase, int mb,
-                                                          int lane, int tb0, int tb1) {
+__device__ __forceinline__ typename Op::gfrag_t grad_bfrag(const char* tile, int jbase, int mb,
+                                                           int lane, int tb0, int tb1) {
   using G = Geo<D, Op::kES>;
   if constexpr (Op::kES == 2) {
     const char* rows = tile + jbase * G::kRowBytes;
@@ -781,8 +872,8 @@ __device__ __forceinline__ typename Op::frag_t grad_bfrag(const char* tile, int 
 
 // Gradient fragment f of a matrix phase: k-half h = f / MB, output block mb = f % MB.
 template <class Op, int D, int F>
-__device__ __forceinline__ typename Op::frag_t grad_frag(const char* gtile, int jbg, int lane,
-                                                         int tb0, int tb1) {
+__device__ __forceinline__ typename Op::gfrag_t grad_frag(const char* gtile, int jbg, int lane,
+                                                          int tb0, int tb1) {
   constexpr int MB = D / 32, mb = F % MB, h = F / MB;
   return grad_bfrag<Op, D>(gtile, jbg + 16 * h, mb, lane, tb0, tb1);
 }
@@ -790,36 +881,36 @@ __device__ __forceinline__ typename Op::frag_t grad_frag(const char* gtile, int 
 template <class Op, int D>
 __device__ __forceinline__ void m_pipeline(const char* gtile, int jbg, const char* stile, int jbs,
                                            int fbase, int lane, int tb0, int tb1,
-                                           const typename Op::frag_t& wf0,
-                                           const typename Op::frag_t& wf1,
+                                           const typename Op::gfrag_t& wf0,
+                                           const typename Op::gfrag_t& wf1,
                                            const typename Op::frag_t (&qt)[D / 16],
                                            const typename Op::frag_t (&qs)[D / 16],
                                            f32x16 (&acc)[D / 32], f32x16& st, f32x16& ss) {
-  using frag_t = typename Op::frag_t;
   using G = Geo<D, Op::kES>;
   constexpr int KS = D / 16, MB = D / 32;
   constexpr int NG = 2 * MB;
   constexpr int NF = NG + 2 * KS;
   using S = LoadSchedule<NG, NF, Op::kES == 2 ? 2 : 8, Op::kES == 2 ? 1 : 2, kBwdLdsOps>;
-  frag_t fr[NF];
+  typename Op::gfrag_t gr[NG];
+  typename Op::frag_t sr[2 * KS];
   auto load = [&](auto fc) __attribute__((always_inline)) {
     constexpr int f = decltype(fc)::value;
     if constexpr (f < NG) {
-      fr[f] = grad_frag<Op, D, f>(gtile, jbg, lane, tb0, tb1);
+      gr[f] = grad_frag<Op, D, f>(gtile, jbg, lane, tb0, tb1);
     } else {
       constexpr int k = f - NG, ks = k / 2, m = k % 2;
-      fr[f] = lds_frag<Op, D>(m ? stile + G::kTileBytes : stile, fbase, jbs, ks);
+      sr[k] = lds_frag<Op, D>(m ? stile + G::kTileBytes : stile, fbase, jbs, ks);
     }
   };
   auto mma = [&](auto fc) __attribute__((always_inline)) {
     constexpr int f = decltype(fc)::value;
     if constexpr (f < NG) {
       constexpr int mb = f % MB, h = f / MB;
-      acc[mb] = mma_k16(h ? wf1 : wf0, fr[f], acc[mb]);
+      acc[mb] = mma_k16(h ? wf1 : wf0, gr[f], acc[mb]);
     } else {
       constexpr int k = f - NG, ks = k / 2, m = k % 2;
-      if constexpr (m == 0) st = mma_k16(fr[f], qt[ks], st);
-      else ss = mma_k16(fr[f], qs[ks], ss);
+      if constexpr (m == 0) st = mma_k16(sr[k], qt[ks], st);
+      else ss = mma_k16(sr[k], qs[ks], ss);
     }
   };
   st = f32x16{};
@@ -850,20 +941,30 @@ __device__ __forceinline__ void m_pipeline(const char* gtile, int jbg, const cha
 //    V(n): W(n) from the scores of block n (exp / VALU work)
 // The waves drift freely between the barriers that separate key tiles, so one wave's
 // vector work overlaps its SIMD partner's matrix work.
+// Bf16Op (bf16 inputs, MODE 0) reads the caller's bf16 rows: the scores contract them as
+// they are (as the forward does), and every staged student tile also gets an IEEE fp16
+// image in LDS (exact for 2^-17 <= |x| < 65504), which the gradient contraction reads with W
+// carried as fp16: each wave converts the 16-byte chunks it copied itself, after its own
+// copies have landed and before the barrier that publishes the tile.
 template <class Op, int D, bool CAUSAL, bool OUT_F32, int MODE>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void relkl_bwd_kernel(const BwdLaunch L) {
   using elem_t = typename Op::elem_t;
   using frag_t = typename Op::frag_t;
+  using gfrag_t = typename Op::gfrag_t;
   using G = Geo<D, Op::kES>;
   constexpr int KS = D / 16;
   constexpr int MB = D / 32;  // 32-wide output blocks over d
   constexpr int kStats = 2 * kBC * 4;
-  constexpr int kStage = 2 * G::kTileBytes + kStats;
+  // stage layout: [teacher tile][student tile]([student fp16 image])[teacher stats][student stats]
+  constexpr int kGradOff = Op::kConvert ? 2 * G::kTileBytes : G::kTileBytes;
+  constexpr int kStatsOff = (Op::kConvert ? 3 : 2) * G::kTileBytes;
+  constexpr int kStage = kStatsOff + kStats;
   constexpr int kDma = kBC * G::kCPR / (kWave * kBWaves);  // DMA instructions per wave per tile
   static_assert(kBC * G::kCPR % (kWave * kBWaves) == 0, "tile must split evenly over 8 waves");
+  static_assert(MODE == 0 || !Op::kConvert, "the cross relation reads fp16 images");
 
-  // Stage buffers: three when they fit in the LDS (bf16 inputs), else two (fp32, d = 128).
+  // Stage buffers: three when they fit in the LDS, else two (fp32, d = 128).
   constexpr int kStages = 3 * kStage <= 160 * 1024 ? 3 : 2;
   __shared__ __attribute__((aligned(1024))) char lds[kStages * kStage];
 
@@ -886,22 +987,15 @@ void relkl_bwd_kernel(const BwdLaunch L) {
   const int b = unit / a.H, h = unit - (unit / a.H) * a.H;
   const int hin = head_of(L, a.map_off, h);
 
-  // Operands: the fp16 reserve copies (dense [unit][N][D]) or the fp32 inputs; own rows
-  // from x, staged key rows from y (the same matrix for the relation).
+  // Operands: the caller's rows in place (through the head map and strides), or dense
+  // [unit][N][D] copies from the reserve; own rows from x, staged key rows from y (the same
+  // matrix for the relation).
   const elem_t* xt;
   const elem_t* xs;
   const elem_t* yt;
   const elem_t* ys;
   int64_t tsn, ssn;
-  if constexpr (Op::kES == 2) {
-    xt = a.x16_t + (int64_t)unit * N * D;
-    xs = a.x16_s + (int64_t)unit * N * D;
-    yt = a.y16_t + (int64_t)unit * N * D;
-    ys = a.y16_s + (int64_t)unit * N * D;
-    tsn = D;
-    ssn = D;
-  } else if (a.x_unit_dense) {
-    // fp32 copies in the reserve (rotated or cross inputs), dense [unit][N][D]
+  if (a.x_dense) {
     xt = reinterpret_cast<const elem_t*>(a.x_t) + (int64_t)unit * N * D;
     xs = reinterpret_cast<const elem_t*>(a.x_s) + (int64_t)unit * N * D;
     yt = reinterpret_cast<const elem_t*>(a.y_t) + (int64_t)unit * N * D;
@@ -919,10 +1013,13 @@ void relkl_bwd_kernel(const BwdLaunch L) {
   const char* yt_c = reinterpret_cast<const char*>(yt);
   const char* ys_c = reinterpret_cast<const char*>(ys);
   const int64_t tsn_b = tsn * Op::kES, ssn_b = ssn * Op::kES;
-  const float* rst_t = a.r_t + (int64_t)unit * a.npad;   // statistics of the own rows
-  const float* rst_s = a.r_s + (int64_t)unit * a.npad;
-  const float* cst_t = a.rc_t + (int64_t)unit * a.npad;  // statistics of the staged rows
-  const float* cst_s = a.rc_s + (int64_t)unit * a.npad;
+  // The forward's LSE vectors (nats); the kernel uses them as log2 statistics
+  // r = LSE log2(e) - 14, for which R(i, j) 2^14 = exp2(S_ij c2 - r_i).
+  const float* own_t = a.lse_t + (int64_t)unit * N;
+  const float* own_s = a.lse_s + (int64_t)unit * N;
+  const float* stg_t = a.lc_t + (int64_t)unit * N;
+  const float* stg_s = a.lc_s + (int64_t)unit * N;
+  constexpr float kLog2e = 1.4426950408889634f;
 
   const int i0 = I * kBRB;
   const int ib0 = i0 + 32 * wave;
@@ -942,9 +1039,9 @@ void relkl_bwd_kernel(const BwdLaunch L) {
   const int kt_end = kt_lo + (int)(((int64_t)(kt_hi - kt_lo) * (split + 1)) / a.splits);
   const int NB = 2 * (kt_end - kt_begin);
 
-  // Stage: [teacher tile][student tile][teacher stats][student stats]; all 8 waves copy
-  // their share of the two tiles, and lanes 0..31 of wave 0 the 2 x 256 bytes of
-  // statistics (the reserve pads each unit's statistics to a multiple of kBC).
+  // Stage: [teacher tile][student tile]([fp16 image])[teacher stats][student stats]; all 8
+  // waves copy their share of the two tiles, and waves 0 and 1 the 64 LSE values of the
+  // teacher and the student (one per lane, rows beyond N read row N-1).
   auto stage_tile = [&](int k, char* st_base) __attribute__((always_inline)) {
     const int j0 = (kt_begin + k) * kBC;
 #pragma unroll
@@ -957,24 +1054,47 @@ void relkl_bwd_kernel(const BwdLaunch L) {
       lds_copy16(yt_c + (int64_t)j * tsn_b + c * 16, lds_addr(st_base + slot0 * 16));
       lds_copy16(ys_c + (int64_t)j * ssn_b + c * 16, lds_addr(st_base + G::kTileBytes + slot0 * 16));
     }
-    if (wave == 0 && lane < 32) {
-      const float* src = (lane < 16 ? cst_t : cst_s) + j0 + 4 * (lane & 15);
-      lds_copy16(src, lds_addr(st_base + 2 * G::kTileBytes));
+    if (wave < 2) {
+      const int j = min(j0 + lane, N - 1);
+      lds_copy4((wave == 0 ? stg_t : stg_s) + j, lds_addr(st_base + kStatsOff + wave * kBC * 4));
+    }
+  };
+  // Once a wave's own copies into a stage buffer have completed (wait_vmem): the fp16 image
+  // of the student chunks it copied (same layout as the tile), and, for waves 0 and 1, its
+  // LSE values turned into log2 statistics (rows beyond N: a huge value, i.e. R = 0).
+  auto convert_tile = [&](int k, char* st_base) __attribute__((always_inline)) {
+    asm volatile("" ::: "memory");  // the reads below follow the completed copies
+    if constexpr (Op::kConvert) {
+#pragma unroll
+      for (int q = 0; q < kDma; ++q) {
+        const int off = ((wave * kDma + q) * kWave + lane) * 16;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(st_base + G::kTileBytes + off);
+        *reinterpret_cast<u32x4*>(st_base + kGradOff + off) =
+            bf16x8_to_f16x8_bits(__builtin_bit_cast(bf16x8, v));
+      }
+    }
+    if (wave < 2) {
+      float* sv = reinterpret_cast<float*>(st_base + kStatsOff) + wave * kBC + lane;
+      const int j = (kt_begin + k) * kBC + lane;
+      *sv = j < N ? fmaf(*sv, kLog2e, -kWScaleLog2) : kPosBig;
     }
   };
   const int ntiles = NB >> 1;
   // stage buffer of tile t (t >= 0)
   auto buf = [&](int t) __attribute__((always_inline)) { return lds + (t % kStages) * kStage; };
   if (ntiles > 0) stage_tile(0, buf(0));
-  // M(0)'s gradient part reads the last buffer's student tile before any copy fills it
+  // M(0)'s gradient part reads the last buffer's gradient tile before any copy fills it
   for (int q = tid; q < G::kTileBytes / 16; q += kBWaves * kWave)
-    *reinterpret_cast<u32x4*>(buf(kStages - 1) + G::kTileBytes + 16 * q) = u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(buf(kStages - 1) + kGradOff + 16 * q) = u32x4{0u, 0u, 0u, 0u};
 
   frag_t qt[KS], qs[KS];
   float rt, rs;  // own row statistics
+  float wd2 = 0.f;  // 2 (R_s(i,i) - R_t(i,i)) 2^14 of the own row (relation)
   if (row < N) {
-    rt = rst_t[row];
-    rs = rst_s[row];
+    rt = fmaf(own_t[row], kLog2e, -kWScaleLog2);
+    rs = fmaf(own_s[row], kLog2e, -kWScaleLog2);
+    if (MODE == 0 && a.diag_delta != nullptr)
+      wd2 = a.diag_delta[(int64_t)unit * N + row] * (2.0f * 16384.0f);
   } else {
     rt = kPosBig;
     rs = kPosBig;
@@ -994,7 +1114,7 @@ void relkl_bwd_kernel(const BwdLaunch L) {
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x16{};
   f32x16 st = f32x16{}, ss = f32x16{};
-  frag_t wf0 = frag_t{}, wf1 = frag_t{};
+  gfrag_t wf0 = gfrag_t{}, wf1 = gfrag_t{};
 
   auto block_j0 = [&](int n) { return (kt_begin + (n >> 1)) * kBC + 32 * (n & 1); };
 
@@ -1005,18 +1125,19 @@ void relkl_bwd_kernel(const BwdLaunch L) {
   //    step t-1) at its start and awaits it at its end;
   //  * two buffers (fp32, d = 128): tile t+1 goes into the buffer of tile t-1, whose last
   //    reads are the gradient MFMAs of M(2t); a barrier after M(2t) precedes the copy.
-  // The barrier ending step t publishes tile t+1 to every wave.  A V(2t-1) that a wave runs
-  // at the start of step t (below) reads tile t-1's statistics before either copy reaches them.
+  // The barrier ending step t publishes tile t+1 (and its fp16 image) to every wave.  A
+  // V(2t-1) that a wave runs at the start of step t (below) reads tile t-1's statistics
+  // before either copy reaches them.
 
   // M(n): gradient of block n-1, scores of block n.  Every M runs the full pipeline: M(0)
-  // contracts the initial zero W with the zero-filled student tile of the last buffer;
+  // contracts the initial zero W with the zero-filled gradient tile of the last buffer;
   // blocks at or beyond N contract a zero W (V leaves zero fragments) with finite copies
   // of row N-1 and their scores are never used; M(NB) computes unused scores from a buffer
   // no copy is writing into.
   auto m_phase = [&](int n) __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(1);  // matrix phases issue ahead of a partner's vector work
     const char* sb = buf(n >> 1);
-    const char* gtile = (n == 0 ? buf(kStages - 1) : buf((n - 1) >> 1)) + G::kTileBytes;
+    const char* gtile = (n == 0 ? buf(kStages - 1) : buf((n - 1) >> 1)) + kGradOff;
     const int jbg = 32 * ((n - 1) & 1), jbs = n & 1;
     m_pipeline<Op, D>(gtile, jbg, sb, jbs, fbase, lane, tb0, tb1, wf0, wf1, qt, qs, acc, st, ss);
   };
@@ -1028,43 +1149,49 @@ void relkl_bwd_kernel(const BwdLaunch L) {
     const int jb0 = block_j0(n);
     if (jb0 < N) {
       const int jb = n & 1;
-      const float* clt = reinterpret_cast<const float*>(sb + 2 * G::kTileBytes) + 32 * jb;
+      const float* clt = reinterpret_cast<const float*>(sb + kStatsOff) + 32 * jb;
       const float* cls = clt + kBC;
       f32x8 w32[2];
       const int di = row - jb0;
       const int nl = N - jb0;
       const bool tail = jb0 + 32 > N;
-      constexpr bool ROW = MODE != 2, COL = MODE != 1;
+      constexpr bool ROW = MODE != 2, COL = MODE != 1, SUB = MODE == 0;
       bool none = false;  // the block holds no entry this pass keeps
       if constexpr (!CAUSAL) {
-        if (tail) make_w<ROW, COL, false, true>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, w32);
-        else make_w<ROW, COL, false, false>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, w32);
+        if (SUB && jb0 == ib0) {  // the wave's diagonal block
+          if (tail) make_w<ROW, COL, false, true, SUB>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, wd2, w32);
+          else make_w<ROW, COL, false, false, SUB>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, wd2, w32);
+        } else if (tail) {
+          make_w<ROW, COL, false, true>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, wd2, w32);
+        } else {
+          make_w<ROW, COL, false, false>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, wd2, w32);
+        }
       } else {
         if (jb0 + 31 < ib0) {  // strictly below the diagonal: row terms
-          if constexpr (ROW) make_w<true, false, false, false>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, w32);
+          if constexpr (ROW) make_w<true, false, false, false>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, wd2, w32);
           else none = true;
         } else if (jb0 > ib0 + 31) {  // strictly above: column terms
           if constexpr (COL) {
-            if (tail) make_w<false, true, false, true>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, w32);
-            else make_w<false, true, false, false>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, w32);
+            if (tail) make_w<false, true, false, true>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, wd2, w32);
+            else make_w<false, true, false, false>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, wd2, w32);
           } else {
             none = true;
           }
         } else {
-          if (tail) make_w<ROW, COL, true, true>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, w32);
-          else make_w<ROW, COL, true, false>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, w32);
+          if (tail) make_w<ROW, COL, true, true, SUB>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, wd2, w32);
+          else make_w<ROW, COL, true, false, SUB>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, wd2, w32);
         }
       }
       if (none) {
-        wf0 = frag_t{};
-        wf1 = frag_t{};
+        wf0 = gfrag_t{};
+        wf1 = gfrag_t{};
       } else {
         wf0 = w_frag<Op>(w32[0]);
         wf1 = w_frag<Op>(w32[1]);
       }
     } else {
-      wf0 = frag_t{};
-      wf1 = frag_t{};
+      wf0 = gfrag_t{};
+      wf1 = gfrag_t{};
     }
   };
 
@@ -1074,6 +1201,7 @@ void relkl_bwd_kernel(const BwdLaunch L) {
   // (each wave's own order of operations is unchanged; its stage buffer is still resident).
   const bool lag = wave >= kBWaves / 2;
   wait_vmem();
+  if (ntiles > 0) convert_tile(0, buf(0));
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     if (kStages == 3 && t + 1 < ntiles) stage_tile(t + 1, buf(t + 1));
@@ -1087,6 +1215,7 @@ void relkl_bwd_kernel(const BwdLaunch L) {
     m_phase(2 * t + 1);
     if (!lag) v_phase(2 * t + 1);
     wait_vmem();
+    if (t + 1 < ntiles) convert_tile(t + 1, buf(t + 1));
     lds_barrier();
   }
   if (lag && ntiles > 0) v_phase(NB - 1);
@@ -1175,16 +1304,30 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const ReduceLaunch L
 }
 
 // ------------------------------------------------------------------ RoPE prep
-// Rotated copies of the teacher and student rows for the RoPE-fused entry points: for
-// token p and frequency k < D/2 (rotate-half pairing of k with k + D/2)
+// Rotated copies of the teacher and student rows for the RoPE-fused and cross entry points:
+// for token p and frequency k < D/2 (rotate-half pairing of k with k + D/2)
 //   y_k = x_k cos[p][k] - x_{k+D/2} sin[p][k],   y_{k+D/2} = x_{k+D/2} cos[p][k] + x_k sin[p][k]
-// each evaluated in fp32 as one fused multiply-add on a rounded product, then rounded to
-// the input dtype, as the rotation inside the model would leave it: bf16 (nearest even),
-// stored as the exactly equal IEEE fp16 value the matrix cores take, or fp32.  Written
-// into the reserve, dense [unit][N][D]; a side without tables is copied unrotated.  One
-// thread per (side, unit, row, group of 4 frequencies): consecutive threads cover
-// consecutive frequencies of one row, so each half-row is read and written in one run.
-template <bool IN_BF16, int D>
+// rounded once to the input dtype (nearest even), as the rotation inside the model would
+// leave it.  Each product of a bf16 or fp32 element with an fp32 table entry is exact in
+// fp64, so the fp64 sum below is the exact rotation rounded once to fp64, and the dtype's
+// rounding is taken from it directly.  F16_IMAGES stores each bf16 value as the exactly
+// equal IEEE fp16 value (the cross relation's matrix-core operands).  Written into the
+// reserve, dense [unit][N][D]; a side without tables is copied unrotated.  One thread per
+// (side, unit, row, group of 4 frequencies): consecutive threads cover consecutive
+// frequencies of one row, so each half-row is read and written in one run.
+
+// Nearest-even bf16 bits of an fp64 value (finite, within the bf16 range): the significand
+// is rounded at bit 45 (7 stored bits remain) on the fp64 bit pattern, after which the
+// value is exact in fp32 and its top half is the bf16 pattern.
+__device__ __forceinline__ uint16_t f64_to_bf16_rne(double v) {
+  uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint64_t low = (1ull << 45) - 1;       // the 45 bits rounded off
+  u += ((1ull << 44) - 1) + ((u >> 45) & 1ull);  // half a unit, ties to the even side
+  u &= ~low;
+  return (uint16_t)(__float_as_uint((float)__longlong_as_double((long long)u)) >> 16);
+}
+
+template <bool IN_BF16, int D, bool F16_IMAGES>
 __global__ __launch_bounds__(256) void rope_prep_kernel(const PrepLaunch L) {
   constexpr int G4 = D / 8;  // groups of 4 frequencies per row
   const int mi = member_of(L, (int)blockIdx.x);
@@ -1220,34 +1363,52 @@ __global__ __launch_bounds__(256) void rope_prep_kernel(const PrepLaunch L) {
     x1 = *reinterpret_cast<const f32x4*>(xp);
     x2 = *reinterpret_cast<const f32x4*>(xp + D / 2);
   }
-  f32x4 y1 = x1, y2 = x2;
+  double y1[4], y2[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    y1[e] = (double)x1[e];
+    y2[e] = (double)x2[e];
+  }
   if (cs != nullptr) {
     const int64_t t = (int64_t)p * (D / 2) + 4 * g;
     const f32x4 c = *reinterpret_cast<const f32x4*>(cs + t);
     const f32x4 sv = *reinterpret_cast<const f32x4*>(sn_tab + t);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      y1[e] = fmaf(x1[e], c[e], -(x2[e] * sv[e]));
-      y2[e] = fmaf(x2[e], c[e], x1[e] * sv[e]);
+      // exact products, one rounding of their difference / sum
+      const double p11 = (double)x1[e] * (double)c[e], p22 = (double)x2[e] * (double)sv[e];
+      const double p21 = (double)x2[e] * (double)c[e], p12 = (double)x1[e] * (double)sv[e];
+      y1[e] = p11 - p22;
+      y2[e] = p21 + p12;
     }
   }
   const int64_t dst = ((int64_t)unit * a.N + p) * D + 4 * g;
   if constexpr (IN_BF16) {
     uint16_t* cp = reinterpret_cast<uint16_t*>(side ? a.c_s : a.c_t) + dst;
-    f32x4 r1, r2;  // the bf16 values, then their fp16 bit patterns (exact below 65504)
+    uint16_t h1[4], h2[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      r1[e] = __uint_as_float((uint32_t)f32_to_bf16_rne(y1[e]) << 16);
-      r2[e] = __uint_as_float((uint32_t)f32_to_bf16_rne(y2[e]) << 16);
+      h1[e] = f64_to_bf16_rne(y1[e]);
+      h2[e] = f64_to_bf16_rne(y2[e]);
     }
-    const f16x4 h1 = __builtin_convertvector(r1, f16x4);
-    const f16x4 h2 = __builtin_convertvector(r2, f16x4);
-    *reinterpret_cast<u32x2*>(cp) = __builtin_bit_cast(u32x2, h1);
-    *reinterpret_cast<u32x2*>(cp + D / 2) = __builtin_bit_cast(u32x2, h2);
+    if constexpr (F16_IMAGES) {  // the bf16 values as fp16 bit patterns (exact below 65504)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float v1 = __uint_as_float((uint32_t)h1[e] << 16);
+        const float v2 = __uint_as_float((uint32_t)h2[e] << 16);
+        h1[e] = __builtin_bit_cast(uint16_t, (_Float16)v1);
+        h2[e] = __builtin_bit_cast(uint16_t, (_Float16)v2);
+      }
+    }
+    *reinterpret_cast<u32x2*>(cp) =
+        u32x2{(uint32_t)h1[0] | ((uint32_t)h1[1] << 16), (uint32_t)h1[2] | ((uint32_t)h1[3] << 16)};
+    *reinterpret_cast<u32x2*>(cp + D / 2) =
+        u32x2{(uint32_t)h2[0] | ((uint32_t)h2[1] << 16), (uint32_t)h2[2] | ((uint32_t)h2[3] << 16)};
   } else {
     float* cp = reinterpret_cast<float*>(side ? a.c_s : a.c_t) + dst;
-    *reinterpret_cast<f32x4*>(cp) = y1;
-    *reinterpret_cast<f32x4*>(cp + D / 2) = y2;
+    *reinterpret_cast<f32x4*>(cp) = f32x4{(float)y1[0], (float)y1[1], (float)y1[2], (float)y1[3]};
+    *reinterpret_cast<f32x4*>(cp + D / 2) =
+        f32x4{(float)y2[0], (float)y2[1], (float)y2[2], (float)y2[3]};
   }
 }
 
@@ -1262,36 +1423,35 @@ static int grid_of(const Launch<M>& L) {
   return L.n >= 1 ? L.end[L.n - 1] : 0;
 }
 
-template <class In, int D, bool CAUSAL>
+template <class In, int D, bool CAUSAL, bool REL>
 static int launch_fwd_t(const FwdLaunch& a, const LossOut& loss, hipStream_t s) {
-  hipLaunchKernelGGL((relkl_fwd_kernel<In, D, CAUSAL>), dim3(grid_of(a)), dim3(kThreads), 0, s,
-                     a);
+  hipLaunchKernelGGL((relkl_fwd_kernel<In, D, CAUSAL, REL>), dim3(grid_of(a)), dim3(kThreads),
+                     0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return (int)e;
   hipLaunchKernelGGL(loss_reduce_kernel, dim3(1 + loss.n), dim3(256), 0, s, loss);
   return (int)hipGetLastError();
 }
 
+template <class In, bool REL>
+static int launch_fwd_d(const FwdLaunch& a, int d, bool causal, const LossOut& loss,
+                        hipStream_t s) {
+  if (d == 128) return causal ? launch_fwd_t<In, 128, true, REL>(a, loss, s)
+                              : launch_fwd_t<In, 128, false, REL>(a, loss, s);
+  return causal ? launch_fwd_t<In, 64, true, REL>(a, loss, s)
+                : launch_fwd_t<In, 64, false, REL>(a, loss, s);
+}
+
 int launch_fwd(const FwdLaunch& a, bool in_bf16, int d, bool causal, const LossOut& loss,
-               void* stream, bool f16_copies) {
+               void* stream, bool cross) {
   if (fault_injected()) return (int)hipErrorLaunchFailure;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (in_bf16 && f16_copies) {
-    if (d == 128) return causal ? launch_fwd_t<F16Op, 128, true>(a, loss, s)
-                                : launch_fwd_t<F16Op, 128, false>(a, loss, s);
-    return causal ? launch_fwd_t<F16Op, 64, true>(a, loss, s)
-                  : launch_fwd_t<F16Op, 64, false>(a, loss, s);
+  if (cross) {
+    return in_bf16 ? launch_fwd_d<F16Op, false>(a, d, causal, loss, s)
+                   : launch_fwd_d<F32In, false>(a, d, causal, loss, s);
   }
-  if (in_bf16) {
-    if (d == 128) return causal ? launch_fwd_t<Bf16In, 128, true>(a, loss, s)
-                                : launch_fwd_t<Bf16In, 128, false>(a, loss, s);
-    return causal ? launch_fwd_t<Bf16In, 64, true>(a, loss, s)
-                  : launch_fwd_t<Bf16In, 64, false>(a, loss, s);
-  }
-  if (d == 128) return causal ? launch_fwd_t<F32In, 128, true>(a, loss, s)
-                              : launch_fwd_t<F32In, 128, false>(a, loss, s);
-  return causal ? launch_fwd_t<F32In, 64, true>(a, loss, s)
-                : launch_fwd_t<F32In, 64, false>(a, loss, s);
+  return in_bf16 ? launch_fwd_d<Bf16In, true>(a, d, causal, loss, s)
+                 : launch_fwd_d<F32In, true>(a, d, causal, loss, s);
 }
 
 template <class Op, int D, bool CAUSAL, bool OUT_F32, int MODE>
@@ -1312,9 +1472,12 @@ static int launch_bwd_d(const BwdLaunch& a, bool causal, bool out_f32, hipStream
 template <int MODE>
 static int launch_bwd_m(const BwdLaunch& a, bool in_bf16, int d, bool causal, bool out_f32,
                         hipStream_t s) {
+  // the relation reads bf16 rows (in place or rotated copies); the cross relation the
+  // reserve's fp16 images
+  using Op16 = std::conditional_t<MODE == 0, Bf16Op, F16Op>;
   if (in_bf16) {
-    return d == 128 ? launch_bwd_d<F16Op, 128, MODE>(a, causal, out_f32, s)
-                    : launch_bwd_d<F16Op, 64, MODE>(a, causal, out_f32, s);
+    return d == 128 ? launch_bwd_d<Op16, 128, MODE>(a, causal, out_f32, s)
+                    : launch_bwd_d<Op16, 64, MODE>(a, causal, out_f32, s);
   }
   // fp32 inputs always give an fp32 gradient
   return d == 128 ? launch_bwd_d<F32In, 128, MODE>(a, causal, true, s)
@@ -1330,19 +1493,23 @@ int launch_bwd(const BwdLaunch& a, bool in_bf16, int d, bool causal, bool out_f3
   return launch_bwd_m<0>(a, in_bf16, d, causal, out_f32, s);
 }
 
-int launch_rope_prep(const PrepLaunch& a, bool in_bf16, int d, void* stream) {
+int launch_rope_prep(const PrepLaunch& a, bool in_bf16, int d, void* stream, bool f16_images) {
   if (fault_injected()) return (int)hipErrorLaunchFailure;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const dim3 grid(grid_of(a));
-  if (in_bf16) {
-    if (d == 128) hipLaunchKernelGGL((rope_prep_kernel<true, 128>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((rope_prep_kernel<true, 64>), grid, dim3(256), 0, s, a);
+  if (in_bf16 && f16_images) {
+    if (d == 128) hipLaunchKernelGGL((rope_prep_kernel<true, 128, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((rope_prep_kernel<true, 64, true>), grid, dim3(256), 0, s, a);
+  } else if (in_bf16) {
+    if (d == 128) hipLaunchKernelGGL((rope_prep_kernel<true, 128, false>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((rope_prep_kernel<true, 64, false>), grid, dim3(256), 0, s, a);
   } else {
-    if (d == 128) hipLaunchKernelGGL((rope_prep_kernel<false, 128>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((rope_prep_kernel<false, 64>), grid, dim3(256), 0, s, a);
+    if (d == 128) hipLaunchKernelGGL((rope_prep_kernel<false, 128, false>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((rope_prep_kernel<false, 64, false>), grid, dim3(256), 0, s, a);
   }
   return (int)hipGetLastError();
 }
+
 
 int launch_splitk_reduce(const ReduceLaunch& a, bool out_f32, void* stream) {
   if (fault_injected()) return (int)hipErrorLaunchFailure;

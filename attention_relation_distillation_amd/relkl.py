@@ -7,6 +7,10 @@ these functions raise.
 
     loss = relation_kl(x_t, x_s, causal=True)          # sum over rows, heads, batch
     loss.backward()                                      # gradient reaches x_s only
+
+Workspaces and outputs are allocated on the stream the call runs on (the ``stream``
+argument, else the current stream), so PyTorch's caching allocator never hands them to
+other work before that stream has finished with them.
 """
 
 from __future__ import annotations
@@ -18,7 +22,7 @@ from typing import Optional, Sequence
 import torch
 
 __all__ = ["LardError", "library_path", "load_library", "relkl_fwd", "relkl_bwd",
-           "relation_kl", "workspace_size", "reserve_size", "rope_reserve_size",
+           "relation_kl", "workspace_size", "rope_reserve_size",
            "rope_relkl_fwd", "rope_relkl_bwd", "rope_relation_kl", "cross_reserve_size",
            "cross_relkl_fwd", "cross_relkl_bwd", "cross_relation_kl", "group_reserve_size",
            "group_workspace_size", "group_relkl_fwd", "group_relkl_bwd", "group_relation_kl",
@@ -76,6 +80,7 @@ class _Member(ctypes.Structure):
         ("desc", _Desc),
         ("x_teacher", ctypes.c_void_p), ("x_student", ctypes.c_void_p),
         ("lse_teacher", ctypes.c_void_p), ("lse_student", ctypes.c_void_p),
+        ("diag_delta", ctypes.c_void_p),
         ("row_kl", ctypes.c_void_p), ("loss", ctypes.c_void_p),
         ("rope", _RopeDesc),
     ]
@@ -110,23 +115,21 @@ def load_library():
     lib.lard_relkl_workspace_size.restype = sz
     lib.lard_relkl_workspace_size.argtypes = [ctypes.POINTER(_Desc), ctypes.c_int,
                                               ctypes.POINTER(ctypes.c_int)]
-    lib.lard_relkl_reserve_size.restype = sz
-    lib.lard_relkl_reserve_size.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(ctypes.c_int)]
     lib.lard_relkl_fwd.restype = ctypes.c_int
-    lib.lard_relkl_fwd.argtypes = [ctypes.POINTER(_Desc), vp, vp, vp, vp, vp, vp, vp, sz, vp, sz,
-                                   vp]
+    lib.lard_relkl_fwd.argtypes = [ctypes.POINTER(_Desc), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.lard_relkl_bwd.restype = ctypes.c_int
-    lib.lard_relkl_bwd.argtypes = [ctypes.POINTER(_Desc), vp, vp, vp, sz, vp,
+    lib.lard_relkl_bwd.argtypes = [ctypes.POINTER(_Desc), vp, vp, vp, vp, vp, vp,
                                    ctypes.POINTER(_GradDesc), vp, vp, sz, vp]
     lib.lard_relkl_rope_reserve_size.restype = sz
     lib.lard_relkl_rope_reserve_size.argtypes = [ctypes.POINTER(_Desc),
                                                  ctypes.POINTER(ctypes.c_int)]
     lib.lard_relkl_rope_fwd.restype = ctypes.c_int
     lib.lard_relkl_rope_fwd.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(_RopeDesc), vp,
-                                        vp, vp, vp, vp, vp, vp, sz, vp, sz, vp]
+                                        vp, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp]
     lib.lard_relkl_rope_bwd.restype = ctypes.c_int
     lib.lard_relkl_rope_bwd.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(_RopeDesc), vp,
-                                        sz, vp, ctypes.POINTER(_GradDesc), vp, vp, sz, vp]
+                                        sz, vp, vp, vp, vp, ctypes.POINTER(_GradDesc), vp, vp,
+                                        sz, vp]
     lib.lard_relkl_cross_reserve_size.restype = sz
     lib.lard_relkl_cross_reserve_size.argtypes = [ctypes.POINTER(_Desc),
                                                   ctypes.POINTER(ctypes.c_int)]
@@ -136,7 +139,7 @@ def load_library():
                                          vp, vp, sz, vp, sz, vp]
     lib.lard_relkl_cross_bwd.restype = ctypes.c_int
     lib.lard_relkl_cross_bwd.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(_RopeDesc), vp,
-                                         sz, vp, ctypes.POINTER(_GradDesc), vp,
+                                         sz, vp, vp, vp, ctypes.POINTER(_GradDesc), vp,
                                          ctypes.POINTER(_GradDesc), vp, vp, sz, vp]
     mp, ci = ctypes.POINTER(_Member), ctypes.c_int
     lib.lard_relkl_group_reserve_size.restype = sz
@@ -199,9 +202,29 @@ def _make_desc(x_t: torch.Tensor, x_s: torch.Tensor, causal: bool, scale: Option
     return desc, keep
 
 
+def _stream_of(dev: torch.device, stream):
+    return torch.cuda.current_stream(dev) if stream is None else stream
+
+
 def _stream_handle(dev: torch.device, stream) -> ctypes.c_void_p:
-    s = torch.cuda.current_stream(dev) if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+    return ctypes.c_void_p(_stream_of(dev, stream).cuda_stream)
+
+
+def _row_vector(b, h, n, dev):
+    return torch.empty((b, h, n), dtype=torch.float32, device=dev)
+
+
+def _check_state(name, t, shape, dev):
+    if (t.dtype != torch.float32 or tuple(t.shape) != tuple(shape) or not t.is_contiguous()
+            or t.device != dev):
+        raise LardError(1, f"{name} must be a contiguous fp32 {tuple(shape)} tensor on the "
+                           "inputs' device, as the forward returned it")
+
+
+def _check_grad_loss(grad_loss, dev):
+    if (grad_loss.dtype != torch.float32 or grad_loss.numel() != 1 or grad_loss.device != dev):
+        raise LardError(1, "grad_loss must be a one-element fp32 tensor on the inputs' device")
+    return grad_loss.contiguous()
 
 
 def _require_gpu(x: torch.Tensor):
@@ -219,50 +242,46 @@ def workspace_size(x_t, x_s, *, causal=True, scale=None, head_map=None, pass_: i
     return int(n)
 
 
-def reserve_size(x_t, x_s, *, causal=True, scale=None, head_map=None) -> int:
-    lib = load_library()
-    desc, _keep = _make_desc(x_t, x_s, causal, scale, head_map)
+def _workspace(lib, desc, pass_, dev):
     st = ctypes.c_int(0)
-    n = lib.lard_relkl_reserve_size(ctypes.byref(desc), ctypes.byref(st))
+    nbytes = lib.lard_relkl_workspace_size(ctypes.byref(desc), pass_, ctypes.byref(st))
     _check(st.value)
-    return int(n)
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
 
 
 def relkl_fwd(x_t: torch.Tensor, x_s: torch.Tensor, *, causal: bool = True,
               scale: Optional[float] = None, head_map: Optional[Sequence[int]] = None,
               want_row_kl: bool = False, stream=None):
-    """Forward: returns dict(loss: 0-d fp32, lse_t, lse_s: fp32 [B, H, N], row_kl or None,
-    reserve: uint8 device buffer the backward needs)."""
+    """Forward: returns dict(loss: 0-d fp32, lse_t, lse_s, diag_delta: fp32 [B, H, N] -- the
+    state the backward takes --, row_kl: fp32 [B, H, N] or None)."""
     lib = load_library()
     desc, keep = _make_desc(x_t, x_s, causal, scale, head_map)
     _require_gpu(x_t)
     b, n = desc.B, desc.N
     dev = x_t.device
-    lse_t = torch.empty((b, desc.H, n), dtype=torch.float32, device=dev)
-    lse_s = torch.empty((b, desc.H, n), dtype=torch.float32, device=dev)
-    row_kl = torch.empty((b, desc.H, n), dtype=torch.float32, device=dev) if want_row_kl else None
-    loss = torch.empty((), dtype=torch.float32, device=dev)
-    st = ctypes.c_int(0)
-    ws_bytes = lib.lard_relkl_workspace_size(ctypes.byref(desc), 0, ctypes.byref(st))
-    _check(st.value)
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
-    rs_bytes = lib.lard_relkl_reserve_size(ctypes.byref(desc), ctypes.byref(st))
-    _check(st.value)
-    reserve = torch.empty(max(rs_bytes, 256), dtype=torch.uint8, device=dev)
-    _check(lib.lard_relkl_fwd(ctypes.byref(desc), x_t.data_ptr(), x_s.data_ptr(),
-                              lse_t.data_ptr(), lse_s.data_ptr(),
-                              row_kl.data_ptr() if row_kl is not None else None,
-                              loss.data_ptr(), reserve.data_ptr(), reserve.numel(),
-                              ws.data_ptr(), ws.numel(), _stream_handle(dev, stream)))
+    with torch.cuda.stream(_stream_of(dev, stream)):
+        lse_t = _row_vector(b, desc.H, n, dev)
+        lse_s = _row_vector(b, desc.H, n, dev)
+        diag = _row_vector(b, desc.H, n, dev)
+        row_kl = _row_vector(b, desc.H, n, dev) if want_row_kl else None
+        loss = torch.empty((), dtype=torch.float32, device=dev)
+        ws = _workspace(lib, desc, 0, dev)
+        _check(lib.lard_relkl_fwd(ctypes.byref(desc), x_t.data_ptr(), x_s.data_ptr(),
+                                  lse_t.data_ptr(), lse_s.data_ptr(), diag.data_ptr(),
+                                  row_kl.data_ptr() if row_kl is not None else None,
+                                  loss.data_ptr(), ws.data_ptr(), ws.numel(),
+                                  _stream_handle(dev, stream)))
     del keep
-    return {"loss": loss, "lse_t": lse_t, "lse_s": lse_s, "row_kl": row_kl, "reserve": reserve}
+    return {"loss": loss, "lse_t": lse_t, "lse_s": lse_s, "diag_delta": diag, "row_kl": row_kl}
 
 
-def relkl_bwd(x_t: torch.Tensor, x_s: torch.Tensor, reserve: torch.Tensor,
-              grad_loss: torch.Tensor, *, causal: bool = True, scale: Optional[float] = None,
-              head_map: Optional[Sequence[int]] = None, dx: Optional[torch.Tensor] = None,
-              dx_dtype: Optional[torch.dtype] = None, stream=None) -> torch.Tensor:
-    """Backward: gradient of grad_loss * loss with respect to x_s (teacher is frozen).
+def relkl_bwd(x_t: torch.Tensor, x_s: torch.Tensor, lse_t: torch.Tensor, lse_s: torch.Tensor,
+              diag_delta: torch.Tensor, grad_loss: torch.Tensor, *, causal: bool = True,
+              scale: Optional[float] = None, head_map: Optional[Sequence[int]] = None,
+              dx: Optional[torch.Tensor] = None, dx_dtype: Optional[torch.dtype] = None,
+              stream=None) -> torch.Tensor:
+    """Backward: gradient of grad_loss * loss with respect to x_s (teacher is frozen), from
+    the inputs and the forward's lse_t, lse_s and diag_delta.
 
     dx (optional) receives the result; heads outside head_map are left untouched.  A new
     dx is zero-filled when head_map selects a subset of heads.
@@ -271,54 +290,58 @@ def relkl_bwd(x_t: torch.Tensor, x_s: torch.Tensor, reserve: torch.Tensor,
     desc, keep = _make_desc(x_t, x_s, causal, scale, head_map)
     _require_gpu(x_t)
     dev = x_t.device
-    if reserve.dtype != torch.uint8 or not reserve.is_contiguous() or reserve.device != dev:
-        raise LardError(1, "reserve must be the uint8 device buffer returned by relkl_fwd")
-    if (grad_loss.dtype != torch.float32 or grad_loss.numel() != 1 or grad_loss.device != dev):
-        raise LardError(1, "grad_loss must be a one-element fp32 tensor on the inputs' device")
-    grad_loss = grad_loss.contiguous()
-    if dx is None:
-        out_dtype = x_s.dtype if dx_dtype is None else dx_dtype
-        subset = head_map is not None and sorted(int(v) for v in head_map) != list(range(desc.H_in))
-        dx = (torch.zeros if subset else torch.empty)(x_s.shape, dtype=out_dtype, device=dev)
-    if dx.shape != x_s.shape or dx.stride(-1) != 1 or dx.device != dev:
-        raise LardError(1, "dx must match x_s in shape, with a contiguous last dimension")
-    gdesc = _GradDesc(dtype=_dtype_code(dx.dtype), reserved=0, stride_b=dx.stride(0),
-                      stride_h=dx.stride(1), stride_n=dx.stride(2))
-    st = ctypes.c_int(0)
-    ws_bytes = lib.lard_relkl_workspace_size(ctypes.byref(desc), 1, ctypes.byref(st))
-    _check(st.value)
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
-    _check(lib.lard_relkl_bwd(ctypes.byref(desc), x_t.data_ptr(), x_s.data_ptr(),
-                              reserve.data_ptr(), reserve.numel(), grad_loss.data_ptr(),
-                              ctypes.byref(gdesc), dx.data_ptr(), ws.data_ptr(), ws.numel(),
-                              _stream_handle(dev, stream)))
+    shape = (desc.B, desc.H, desc.N)
+    for name, t in (("lse_t", lse_t), ("lse_s", lse_s), ("diag_delta", diag_delta)):
+        _check_state(name, t, shape, dev)
+    grad_loss = _check_grad_loss(grad_loss, dev)
+    with torch.cuda.stream(_stream_of(dev, stream)):
+        dx, gdesc = _new_grad(x_s, head_map, desc.H_in, dx, dx_dtype)
+        ws = _workspace(lib, desc, 1, dev)
+        _check(lib.lard_relkl_bwd(ctypes.byref(desc), x_t.data_ptr(), x_s.data_ptr(),
+                                  lse_t.data_ptr(), lse_s.data_ptr(), diag_delta.data_ptr(),
+                                  grad_loss.data_ptr(), ctypes.byref(gdesc), dx.data_ptr(),
+                                  ws.data_ptr(), ws.numel(), _stream_handle(dev, stream)))
     del keep
     return dx
 
 
+def _mean_rows_factor(x: torch.Tensor, reduction: str) -> Optional[float]:
+    if reduction == "sum":
+        return None
+    if reduction == "mean_rows":
+        return 1.0 / x.shape[2]
+    raise LardError(1, f"reduction must be 'sum' or 'mean_rows', not {reduction!r}")
+
+
 class _RelationKL(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, x_t, x_s, causal, scale, head_map):
+    def forward(ctx, x_t, x_s, causal, scale, head_map, factor):
         out = relkl_fwd(x_t, x_s, causal=causal, scale=scale, head_map=head_map)
-        ctx.save_for_backward(x_t, x_s, out["reserve"])
-        ctx.causal, ctx.scale, ctx.head_map = causal, scale, head_map
-        return out["loss"]
+        ctx.save_for_backward(x_t, x_s, out["lse_t"], out["lse_s"], out["diag_delta"])
+        ctx.causal, ctx.scale, ctx.head_map, ctx.factor = causal, scale, head_map, factor
+        return out["loss"] if factor is None else out["loss"] * factor
 
     @staticmethod
     def backward(ctx, grad):
-        x_t, x_s, reserve = ctx.saved_tensors
+        x_t, x_s, lse_t, lse_s, diag = ctx.saved_tensors
         g = grad if grad.dtype == torch.float32 else grad.float()
-        dx = relkl_bwd(x_t, x_s, reserve, g, causal=ctx.causal, scale=ctx.scale,
+        if ctx.factor is not None:
+            g = g * ctx.factor
+        dx = relkl_bwd(x_t, x_s, lse_t, lse_s, diag, g, causal=ctx.causal, scale=ctx.scale,
                        head_map=ctx.head_map)
-        return None, dx, None, None, None
+        return None, dx, None, None, None, None
 
 
 def relation_kl(x_t: torch.Tensor, x_s: torch.Tensor, *, causal: bool = True,
-                scale: Optional[float] = None, head_map: Optional[Sequence[int]] = None):
-    """Sum over batch, relation heads and rows of KL(R_teacher || R_student) (a 0-d fp32
-    tensor).  Differentiable with respect to x_s; the teacher is treated as frozen."""
+                scale: Optional[float] = None, head_map: Optional[Sequence[int]] = None,
+                reduction: str = "sum"):
+    """KL(R_teacher || R_student) summed over batch, relation heads and rows (a 0-d fp32
+    tensor); reduction="mean_rows" divides by N, the pages' mean over the rows of a head
+    (the gradient is scaled alike).  Differentiable with respect to x_s; the teacher is
+    treated as frozen."""
     return _RelationKL.apply(x_t.detach(), x_s, causal, scale,
-                             None if head_map is None else tuple(int(v) for v in head_map))
+                             None if head_map is None else tuple(int(v) for v in head_map),
+                             _mean_rows_factor(x_t, reduction))
 
 
 # ------------------------------------------------------------------ RoPE-fused entry points
@@ -347,39 +370,51 @@ def rope_reserve_size(x_t, x_s, *, causal=True, scale=None, head_map=None) -> in
     return int(n)
 
 
+def _reserve(nbytes, dev):
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+
+
+def _check_reserve(reserve, dev, what):
+    if reserve.dtype != torch.uint8 or not reserve.is_contiguous() or reserve.device != dev:
+        raise LardError(1, f"reserve must be the uint8 device buffer returned by {what}")
+
+
 def rope_relkl_fwd(x_t: torch.Tensor, x_s: torch.Tensor, cos_t=None, sin_t=None, cos_s=None,
                    sin_s=None, *, causal: bool = True, scale: Optional[float] = None,
                    head_map: Optional[Sequence[int]] = None, want_row_kl: bool = False,
                    stream=None):
-    """RoPE-fused forward on pre-rotation inputs; returns the same dict as relkl_fwd (its
-    reserve holds the rotated rows and is what rope_relkl_bwd needs)."""
+    """RoPE-fused forward on pre-rotation inputs; returns the dict of relkl_fwd plus
+    "reserve" (the rotated rows, which rope_relkl_bwd reads)."""
     lib = load_library()
     desc, keep = _make_desc(x_t, x_s, causal, scale, head_map)
     rdesc = _rope_desc(x_t, (cos_t, sin_t, cos_s, sin_s))
     _require_gpu(x_t)
     b, n = desc.B, desc.N
     dev = x_t.device
-    lse_t = torch.empty((b, desc.H, n), dtype=torch.float32, device=dev)
-    lse_s = torch.empty((b, desc.H, n), dtype=torch.float32, device=dev)
-    row_kl = torch.empty((b, desc.H, n), dtype=torch.float32, device=dev) if want_row_kl else None
-    loss = torch.empty((), dtype=torch.float32, device=dev)
     st = ctypes.c_int(0)
-    ws_bytes = lib.lard_relkl_workspace_size(ctypes.byref(desc), 0, ctypes.byref(st))
-    _check(st.value)
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     rs_bytes = lib.lard_relkl_rope_reserve_size(ctypes.byref(desc), ctypes.byref(st))
     _check(st.value)
-    reserve = torch.empty(max(rs_bytes, 256), dtype=torch.uint8, device=dev)
-    _check(lib.lard_relkl_rope_fwd(ctypes.byref(desc), ctypes.byref(rdesc), x_t.data_ptr(),
-                                   x_s.data_ptr(), lse_t.data_ptr(), lse_s.data_ptr(),
-                                   row_kl.data_ptr() if row_kl is not None else None,
-                                   loss.data_ptr(), reserve.data_ptr(), reserve.numel(),
-                                   ws.data_ptr(), ws.numel(), _stream_handle(dev, stream)))
+    with torch.cuda.stream(_stream_of(dev, stream)):
+        lse_t = _row_vector(b, desc.H, n, dev)
+        lse_s = _row_vector(b, desc.H, n, dev)
+        diag = _row_vector(b, desc.H, n, dev)
+        row_kl = _row_vector(b, desc.H, n, dev) if want_row_kl else None
+        loss = torch.empty((), dtype=torch.float32, device=dev)
+        ws = _workspace(lib, desc, 0, dev)
+        reserve = _reserve(rs_bytes, dev)
+        _check(lib.lard_relkl_rope_fwd(ctypes.byref(desc), ctypes.byref(rdesc), x_t.data_ptr(),
+                                       x_s.data_ptr(), lse_t.data_ptr(), lse_s.data_ptr(),
+                                       diag.data_ptr(),
+                                       row_kl.data_ptr() if row_kl is not None else None,
+                                       loss.data_ptr(), reserve.data_ptr(), reserve.numel(),
+                                       ws.data_ptr(), ws.numel(), _stream_handle(dev, stream)))
     del keep
-    return {"loss": loss, "lse_t": lse_t, "lse_s": lse_s, "row_kl": row_kl, "reserve": reserve}
+    return {"loss": loss, "lse_t": lse_t, "lse_s": lse_s, "diag_delta": diag, "row_kl": row_kl,
+            "reserve": reserve}
 
 
-def rope_relkl_bwd(x_s: torch.Tensor, reserve: torch.Tensor, grad_loss: torch.Tensor,
+def rope_relkl_bwd(x_s: torch.Tensor, reserve: torch.Tensor, lse_t: torch.Tensor,
+                   lse_s: torch.Tensor, diag_delta: torch.Tensor, grad_loss: torch.Tensor,
                    cos_t=None, sin_t=None, cos_s=None, sin_s=None, *, causal: bool = True,
                    scale: Optional[float] = None, head_map: Optional[Sequence[int]] = None,
                    dx: Optional[torch.Tensor] = None, dx_dtype: Optional[torch.dtype] = None,
@@ -392,27 +427,20 @@ def rope_relkl_bwd(x_s: torch.Tensor, reserve: torch.Tensor, grad_loss: torch.Te
     rdesc = _rope_desc(x_s, (cos_t, sin_t, cos_s, sin_s))
     _require_gpu(x_s)
     dev = x_s.device
-    if reserve.dtype != torch.uint8 or not reserve.is_contiguous() or reserve.device != dev:
-        raise LardError(1, "reserve must be the uint8 device buffer returned by rope_relkl_fwd")
-    if (grad_loss.dtype != torch.float32 or grad_loss.numel() != 1 or grad_loss.device != dev):
-        raise LardError(1, "grad_loss must be a one-element fp32 tensor on the inputs' device")
-    grad_loss = grad_loss.contiguous()
-    if dx is None:
-        out_dtype = x_s.dtype if dx_dtype is None else dx_dtype
-        subset = head_map is not None and sorted(int(v) for v in head_map) != list(range(desc.H_in))
-        dx = (torch.zeros if subset else torch.empty)(x_s.shape, dtype=out_dtype, device=dev)
-    if dx.shape != x_s.shape or dx.stride(-1) != 1 or dx.device != dev:
-        raise LardError(1, "dx must match x_s in shape, with a contiguous last dimension")
-    gdesc = _GradDesc(dtype=_dtype_code(dx.dtype), reserved=0, stride_b=dx.stride(0),
-                      stride_h=dx.stride(1), stride_n=dx.stride(2))
-    st = ctypes.c_int(0)
-    ws_bytes = lib.lard_relkl_workspace_size(ctypes.byref(desc), 1, ctypes.byref(st))
-    _check(st.value)
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
-    _check(lib.lard_relkl_rope_bwd(ctypes.byref(desc), ctypes.byref(rdesc), reserve.data_ptr(),
-                                   reserve.numel(), grad_loss.data_ptr(), ctypes.byref(gdesc),
-                                   dx.data_ptr(), ws.data_ptr(), ws.numel(),
-                                   _stream_handle(dev, stream)))
+    _check_reserve(reserve, dev, "rope_relkl_fwd")
+    shape = (desc.B, desc.H, desc.N)
+    for name, t in (("lse_t", lse_t), ("lse_s", lse_s), ("diag_delta", diag_delta)):
+        _check_state(name, t, shape, dev)
+    grad_loss = _check_grad_loss(grad_loss, dev)
+    with torch.cuda.stream(_stream_of(dev, stream)):
+        dx, gdesc = _new_grad(x_s, head_map, desc.H_in, dx, dx_dtype)
+        ws = _workspace(lib, desc, 1, dev)
+        _check(lib.lard_relkl_rope_bwd(ctypes.byref(desc), ctypes.byref(rdesc),
+                                       reserve.data_ptr(), reserve.numel(), lse_t.data_ptr(),
+                                       lse_s.data_ptr(), diag_delta.data_ptr(),
+                                       grad_loss.data_ptr(), ctypes.byref(gdesc),
+                                       dx.data_ptr(), ws.data_ptr(), ws.numel(),
+                                       _stream_handle(dev, stream)))
     del keep
     return dx
 
@@ -422,17 +450,18 @@ class _RopeRelationKL(torch.autograd.Function):
     def forward(ctx, x_t, x_s, cos_t, sin_t, cos_s, sin_s, causal, scale, head_map):
         out = rope_relkl_fwd(x_t, x_s, cos_t, sin_t, cos_s, sin_s, causal=causal, scale=scale,
                              head_map=head_map)
-        ctx.save_for_backward(x_s, out["reserve"])
+        ctx.save_for_backward(x_s, out["reserve"], out["lse_t"], out["lse_s"],
+                              out["diag_delta"])
         ctx.tables = (cos_t, sin_t, cos_s, sin_s)
         ctx.causal, ctx.scale, ctx.head_map = causal, scale, head_map
         return out["loss"]
 
     @staticmethod
     def backward(ctx, grad):
-        x_s, reserve = ctx.saved_tensors
+        x_s, reserve, lse_t, lse_s, diag = ctx.saved_tensors
         g = grad if grad.dtype == torch.float32 else grad.float()
-        dx = rope_relkl_bwd(x_s, reserve, g, *ctx.tables, causal=ctx.causal, scale=ctx.scale,
-                            head_map=ctx.head_map)
+        dx = rope_relkl_bwd(x_s, reserve, lse_t, lse_s, diag, g, *ctx.tables,
+                            causal=ctx.causal, scale=ctx.scale, head_map=ctx.head_map)
         return None, dx, None, None, None, None, None, None, None
 
 
@@ -481,8 +510,9 @@ def cross_relkl_fwd(a_t: torch.Tensor, b_t: torch.Tensor, a_s: torch.Tensor, b_s
                     head_map: Optional[Sequence[int]] = None, want_row_kl: bool = False,
                     stream=None):
     """Forward of the cross relation softmax(scale A B^T) per side (A: queries, B: keys);
-    rope: None or (cos_t, sin_t, cos_s, sin_s) rotating each side's A and B.  Returns the
-    same dict as relkl_fwd; its reserve is what cross_relkl_bwd needs."""
+    rope: None or (cos_t, sin_t, cos_s, sin_s) rotating each side's A and B.  Returns
+    dict(loss, lse_t, lse_s, row_kl, reserve); the reserve and the LSE vectors are what
+    cross_relkl_bwd needs."""
     lib = load_library()
     desc, keep = _make_desc(a_t, a_s, causal, scale, head_map)
     kdesc = _cross_desc(a_t, a_s, b_t, b_s)
@@ -490,23 +520,22 @@ def cross_relkl_fwd(a_t: torch.Tensor, b_t: torch.Tensor, a_s: torch.Tensor, b_s
     _require_gpu(a_t)
     b, n = desc.B, desc.N
     dev = a_t.device
-    lse_t = torch.empty((b, desc.H, n), dtype=torch.float32, device=dev)
-    lse_s = torch.empty((b, desc.H, n), dtype=torch.float32, device=dev)
-    row_kl = torch.empty((b, desc.H, n), dtype=torch.float32, device=dev) if want_row_kl else None
-    loss = torch.empty((), dtype=torch.float32, device=dev)
     st = ctypes.c_int(0)
-    ws_bytes = lib.lard_relkl_workspace_size(ctypes.byref(desc), 0, ctypes.byref(st))
-    _check(st.value)
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     rs_bytes = lib.lard_relkl_cross_reserve_size(ctypes.byref(desc), ctypes.byref(st))
     _check(st.value)
-    reserve = torch.empty(max(rs_bytes, 256), dtype=torch.uint8, device=dev)
-    _check(lib.lard_relkl_cross_fwd(ctypes.byref(desc), ctypes.byref(kdesc), rptr,
-                                    a_t.data_ptr(), b_t.data_ptr(), a_s.data_ptr(),
-                                    b_s.data_ptr(), lse_t.data_ptr(), lse_s.data_ptr(),
-                                    row_kl.data_ptr() if row_kl is not None else None,
-                                    loss.data_ptr(), reserve.data_ptr(), reserve.numel(),
-                                    ws.data_ptr(), ws.numel(), _stream_handle(dev, stream)))
+    with torch.cuda.stream(_stream_of(dev, stream)):
+        lse_t = _row_vector(b, desc.H, n, dev)
+        lse_s = _row_vector(b, desc.H, n, dev)
+        row_kl = _row_vector(b, desc.H, n, dev) if want_row_kl else None
+        loss = torch.empty((), dtype=torch.float32, device=dev)
+        ws = _workspace(lib, desc, 0, dev)
+        reserve = _reserve(rs_bytes, dev)
+        _check(lib.lard_relkl_cross_fwd(ctypes.byref(desc), ctypes.byref(kdesc), rptr,
+                                        a_t.data_ptr(), b_t.data_ptr(), a_s.data_ptr(),
+                                        b_s.data_ptr(), lse_t.data_ptr(), lse_s.data_ptr(),
+                                        row_kl.data_ptr() if row_kl is not None else None,
+                                        loss.data_ptr(), reserve.data_ptr(), reserve.numel(),
+                                        ws.data_ptr(), ws.numel(), _stream_handle(dev, stream)))
     del keep
     return {"loss": loss, "lse_t": lse_t, "lse_s": lse_s, "row_kl": row_kl, "reserve": reserve}
 
@@ -524,10 +553,11 @@ def _new_grad(x, head_map, n_in, dx, dx_dtype):
 
 
 def cross_relkl_bwd(a_s: torch.Tensor, b_s: torch.Tensor, reserve: torch.Tensor,
-                    grad_loss: torch.Tensor, *, rope=None, causal: bool = True,
-                    scale: Optional[float] = None, head_map: Optional[Sequence[int]] = None,
-                    da: Optional[torch.Tensor] = None, db: Optional[torch.Tensor] = None,
-                    dx_dtype: Optional[torch.dtype] = None, stream=None):
+                    lse_t: torch.Tensor, lse_s: torch.Tensor, grad_loss: torch.Tensor, *,
+                    rope=None, causal: bool = True, scale: Optional[float] = None,
+                    head_map: Optional[Sequence[int]] = None, da: Optional[torch.Tensor] = None,
+                    db: Optional[torch.Tensor] = None, dx_dtype: Optional[torch.dtype] = None,
+                    stream=None):
     """(dA_s, dB_s) of grad_loss * loss; a_s / b_s give shapes, dtypes and the device (their
     values are not read: the operands come from the reserve)."""
     lib = load_library()
@@ -535,21 +565,20 @@ def cross_relkl_bwd(a_s: torch.Tensor, b_s: torch.Tensor, reserve: torch.Tensor,
     rptr = _rope_ptr(a_s, rope)
     _require_gpu(a_s)
     dev = a_s.device
-    if reserve.dtype != torch.uint8 or not reserve.is_contiguous() or reserve.device != dev:
-        raise LardError(1, "reserve must be the uint8 device buffer returned by cross_relkl_fwd")
-    if (grad_loss.dtype != torch.float32 or grad_loss.numel() != 1 or grad_loss.device != dev):
-        raise LardError(1, "grad_loss must be a one-element fp32 tensor on the inputs' device")
-    grad_loss = grad_loss.contiguous()
-    da, gda = _new_grad(a_s, head_map, desc.H_in, da, dx_dtype)
-    db, gdb = _new_grad(b_s, head_map, desc.H_in, db, dx_dtype)
-    st = ctypes.c_int(0)
-    ws_bytes = lib.lard_relkl_workspace_size(ctypes.byref(desc), 1, ctypes.byref(st))
-    _check(st.value)
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
-    _check(lib.lard_relkl_cross_bwd(ctypes.byref(desc), rptr, reserve.data_ptr(),
-                                    reserve.numel(), grad_loss.data_ptr(), ctypes.byref(gda),
-                                    da.data_ptr(), ctypes.byref(gdb), db.data_ptr(),
-                                    ws.data_ptr(), ws.numel(), _stream_handle(dev, stream)))
+    _check_reserve(reserve, dev, "cross_relkl_fwd")
+    shape = (desc.B, desc.H, desc.N)
+    for name, t in (("lse_t", lse_t), ("lse_s", lse_s)):
+        _check_state(name, t, shape, dev)
+    grad_loss = _check_grad_loss(grad_loss, dev)
+    with torch.cuda.stream(_stream_of(dev, stream)):
+        da, gda = _new_grad(a_s, head_map, desc.H_in, da, dx_dtype)
+        db, gdb = _new_grad(b_s, head_map, desc.H_in, db, dx_dtype)
+        ws = _workspace(lib, desc, 1, dev)
+        _check(lib.lard_relkl_cross_bwd(ctypes.byref(desc), rptr, reserve.data_ptr(),
+                                        reserve.numel(), lse_t.data_ptr(), lse_s.data_ptr(),
+                                        grad_loss.data_ptr(), ctypes.byref(gda), da.data_ptr(),
+                                        ctypes.byref(gdb), db.data_ptr(), ws.data_ptr(),
+                                        ws.numel(), _stream_handle(dev, stream)))
     del keep
     return da, db
 
@@ -559,16 +588,16 @@ class _CrossRelationKL(torch.autograd.Function):
     def forward(ctx, a_t, b_t, a_s, b_s, rope, causal, scale, head_map):
         out = cross_relkl_fwd(a_t, b_t, a_s, b_s, rope=rope, causal=causal, scale=scale,
                               head_map=head_map)
-        ctx.save_for_backward(a_s, b_s, out["reserve"])
+        ctx.save_for_backward(a_s, b_s, out["reserve"], out["lse_t"], out["lse_s"])
         ctx.rope, ctx.causal, ctx.scale, ctx.head_map = rope, causal, scale, head_map
         return out["loss"]
 
     @staticmethod
     def backward(ctx, grad):
-        a_s, b_s, reserve = ctx.saved_tensors
+        a_s, b_s, reserve, lse_t, lse_s = ctx.saved_tensors
         g = grad if grad.dtype == torch.float32 else grad.float()
-        da, db = cross_relkl_bwd(a_s, b_s, reserve, g, rope=ctx.rope, causal=ctx.causal,
-                                 scale=ctx.scale, head_map=ctx.head_map)
+        da, db = cross_relkl_bwd(a_s, b_s, reserve, lse_t, lse_s, g, rope=ctx.rope,
+                                 causal=ctx.causal, scale=ctx.scale, head_map=ctx.head_map)
         return None, None, da, db, None, None, None, None
 
 
@@ -641,86 +670,107 @@ def group_relkl_fwd(pairs, *, causal: bool = True, scale: Optional[float] = None
     None or one head map (or None) per member; rope: None (post-rotation inputs) or one
     entry per member, None or (cos_t, sin_t, cos_s, sin_s), rotating inside the call.
     Returns dict(loss: 0-d fp32 sum over the members, member_loss: list of 0-d fp32,
-    lse_t, lse_s, row_kl: lists per member, reserve).  scale: None (1/sqrt(d)), one value
-    for every member, or one per member."""
+    lse_t, lse_s, diag_delta, row_kl: lists per member, reserve: the rotated rows, or None
+    without rope).  scale: None (1/sqrt(d)), one value for every member, or one per
+    member."""
     lib = load_library()
     members, keep, with_rope = _group(pairs, causal, scale, head_maps, rope)
     _require_gpu(pairs[0][0])
     dev = pairs[0][0].device
-    # one allocation for all members' row vectors and losses; views per member
     n = len(members)
     sizes = [m.desc.B * m.desc.H * m.desc.N for m in members]
-    per = 3 if want_row_kl else 2
-    flat = torch.empty(per * sum(sizes) + n, dtype=torch.float32, device=dev)
-    loss = torch.empty((), dtype=torch.float32, device=dev)
-    out = {"lse_t": [], "lse_s": [], "row_kl": [], "member_loss": []}
-    off = 0
-    for k, m in enumerate(members):
-        shape = (m.desc.B, m.desc.H, m.desc.N)
-        views = []
-        for _ in range(per):
-            views.append(flat[off:off + sizes[k]].view(shape))
-            off += sizes[k]
-        lt, ls = views[0], views[1]
-        kl = views[2] if want_row_kl else None
-        m.lse_teacher, m.lse_student = lt.data_ptr(), ls.data_ptr()
-        m.row_kl = kl.data_ptr() if kl is not None else None
-        out["lse_t"].append(lt)
-        out["lse_s"].append(ls)
-        out["row_kl"].append(kl)
-    for k, m in enumerate(members):
-        ml = flat[off + k]
-        m.loss = ml.data_ptr()
-        out["member_loss"].append(ml)
+    per = 4 if want_row_kl else 3
     st = ctypes.c_int(0)
     ws_bytes = lib.lard_relkl_group_workspace_size(n, members, 0, ctypes.byref(st))
     _check(st.value)
     rs_bytes = lib.lard_relkl_group_reserve_size(n, members, with_rope, ctypes.byref(st))
     _check(st.value)
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
-    reserve = torch.empty(max(rs_bytes, 256), dtype=torch.uint8, device=dev)
-    _check(lib.lard_relkl_group_fwd(n, members, with_rope, loss.data_ptr(), reserve.data_ptr(),
-                                    reserve.numel(), ws.data_ptr(), ws.numel(),
-                                    _stream_handle(dev, stream)))
+    out = {"lse_t": [], "lse_s": [], "diag_delta": [], "row_kl": [], "member_loss": []}
+    with torch.cuda.stream(_stream_of(dev, stream)):
+        # one allocation for all members' row vectors and losses; views per member
+        flat = torch.empty(per * sum(sizes) + n, dtype=torch.float32, device=dev)
+        loss = torch.empty((), dtype=torch.float32, device=dev)
+        off = 0
+        for k, m in enumerate(members):
+            shape = (m.desc.B, m.desc.H, m.desc.N)
+            views = []
+            for _ in range(per):
+                views.append(flat[off:off + sizes[k]].view(shape))
+                off += sizes[k]
+            lt, ls, dg = views[0], views[1], views[2]
+            kl = views[3] if want_row_kl else None
+            m.lse_teacher, m.lse_student = lt.data_ptr(), ls.data_ptr()
+            m.diag_delta = dg.data_ptr()
+            m.row_kl = kl.data_ptr() if kl is not None else None
+            out["lse_t"].append(lt)
+            out["lse_s"].append(ls)
+            out["diag_delta"].append(dg)
+            out["row_kl"].append(kl)
+        for k, m in enumerate(members):
+            ml = flat[off + k]
+            m.loss = ml.data_ptr()
+            out["member_loss"].append(ml)
+        ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+        reserve = _reserve(rs_bytes, dev) if with_rope else None
+        _check(lib.lard_relkl_group_fwd(n, members, with_rope, loss.data_ptr(),
+                                        reserve.data_ptr() if reserve is not None else None,
+                                        reserve.numel() if reserve is not None else 0,
+                                        ws.data_ptr(), ws.numel(),
+                                        _stream_handle(dev, stream)))
     del keep
     out["loss"] = loss
     out["reserve"] = reserve
     return out
 
 
-def group_relkl_bwd(pairs, reserve: torch.Tensor, grad_loss: torch.Tensor, *,
-                    causal: bool = True, scale: Optional[float] = None, head_maps=None,
-                    rope=None, dx=None, dx_dtype: Optional[torch.dtype] = None, stream=None):
-    """Gradients of grad_loss * (group loss) with respect to every member's x_s (a list);
-    arguments as given to group_relkl_fwd.  dx (optional): one output tensor per member."""
+def group_relkl_bwd(pairs, lse_t, lse_s, diag_delta, grad_loss: torch.Tensor, *,
+                    reserve: Optional[torch.Tensor] = None, causal: bool = True,
+                    scale: Optional[float] = None, head_maps=None, rope=None, dx=None,
+                    dx_dtype: Optional[torch.dtype] = None, stream=None):
+    """Gradients of grad_loss * (group loss) with respect to every member's x_s (a list).
+    lse_t, lse_s, diag_delta: the per-member lists group_relkl_fwd returned; reserve: its
+    reserve (with rope); the other arguments as given to group_relkl_fwd.  dx (optional):
+    one output tensor per member."""
     lib = load_library()
     members, keep, with_rope = _group(pairs, causal, scale, head_maps, rope)
     _require_gpu(pairs[0][0])
     dev = pairs[0][0].device
-    if reserve.dtype != torch.uint8 or not reserve.is_contiguous() or reserve.device != dev:
-        raise LardError(1, "reserve must be the uint8 device buffer returned by group_relkl_fwd")
-    if (grad_loss.dtype != torch.float32 or grad_loss.numel() != 1 or grad_loss.device != dev):
-        raise LardError(1, "grad_loss must be a one-element fp32 tensor on the inputs' device")
-    grad_loss = grad_loss.contiguous()
+    if with_rope:
+        if reserve is None:
+            raise LardError(1, "a RoPE-fused group backward needs the forward's reserve")
+        _check_reserve(reserve, dev, "group_relkl_fwd")
+    grad_loss = _check_grad_loss(grad_loss, dev)
     n = len(members)
+    if len(lse_t) != n or len(lse_s) != n or len(diag_delta) != n:
+        raise LardError(1, "lse_t, lse_s and diag_delta need one tensor per member")
     if dx is not None and len(dx) != n:
         raise LardError(1, "dx needs one tensor per member")
-    outs = []
-    gdescs = (_GradDesc * n)()
-    ptrs = (ctypes.c_void_p * n)()
-    for k, (_, x_s) in enumerate(pairs):
-        hm = None if head_maps is None else head_maps[k]
-        g, gd = _new_grad(x_s, hm, members[k].desc.H_in, None if dx is None else dx[k], dx_dtype)
-        outs.append(g)
-        gdescs[k] = gd
-        ptrs[k] = g.data_ptr()
+    for k, m in enumerate(members):
+        shape = (m.desc.B, m.desc.H, m.desc.N)
+        for name, t in (("lse_t", lse_t[k]), ("lse_s", lse_s[k]), ("diag_delta", diag_delta[k])):
+            _check_state(name, t, shape, dev)
+        m.lse_teacher, m.lse_student = lse_t[k].data_ptr(), lse_s[k].data_ptr()
+        m.diag_delta = diag_delta[k].data_ptr()
     st = ctypes.c_int(0)
     ws_bytes = lib.lard_relkl_group_workspace_size(n, members, 1, ctypes.byref(st))
     _check(st.value)
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
-    _check(lib.lard_relkl_group_bwd(n, members, with_rope, reserve.data_ptr(), reserve.numel(),
-                                    grad_loss.data_ptr(), gdescs, ptrs, ws.data_ptr(),
-                                    ws.numel(), _stream_handle(dev, stream)))
+    outs = []
+    gdescs = (_GradDesc * n)()
+    ptrs = (ctypes.c_void_p * n)()
+    with torch.cuda.stream(_stream_of(dev, stream)):
+        for k, (_, x_s) in enumerate(pairs):
+            hm = None if head_maps is None else head_maps[k]
+            g, gd = _new_grad(x_s, hm, members[k].desc.H_in, None if dx is None else dx[k],
+                              dx_dtype)
+            outs.append(g)
+            gdescs[k] = gd
+            ptrs[k] = g.data_ptr()
+        ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+        _check(lib.lard_relkl_group_bwd(n, members, with_rope,
+                                        reserve.data_ptr() if with_rope else None,
+                                        reserve.numel() if with_rope else 0,
+                                        grad_loss.data_ptr(), gdescs, ptrs, ws.data_ptr(),
+                                        ws.numel(), _stream_handle(dev, stream)))
     del keep
     return outs
 
@@ -730,17 +780,27 @@ class _GroupRelationKL(torch.autograd.Function):
     def forward(ctx, causal, scale, head_maps, rope, *xs):
         pairs = [(xs[2 * k], xs[2 * k + 1]) for k in range(len(xs) // 2)]
         out = group_relkl_fwd(pairs, causal=causal, scale=scale, head_maps=head_maps, rope=rope)
-        ctx.save_for_backward(*xs, out["reserve"])
+        n = len(pairs)
+        saved = list(xs) + out["lse_t"] + out["lse_s"] + out["diag_delta"]
+        if out["reserve"] is not None:
+            saved.append(out["reserve"])
+        ctx.save_for_backward(*saved)
+        ctx.n = n
         ctx.causal, ctx.scale, ctx.head_maps, ctx.rope = causal, scale, head_maps, rope
         return out["loss"]
 
     @staticmethod
     def backward(ctx, grad):
-        *xs, reserve = ctx.saved_tensors
-        pairs = [(xs[2 * k], xs[2 * k + 1]) for k in range(len(xs) // 2)]
+        saved = ctx.saved_tensors
+        n = ctx.n
+        xs = saved[:2 * n]
+        lse_t, lse_s = list(saved[2 * n:3 * n]), list(saved[3 * n:4 * n])
+        diag = list(saved[4 * n:5 * n])
+        reserve = saved[5 * n] if len(saved) > 5 * n else None
+        pairs = [(xs[2 * k], xs[2 * k + 1]) for k in range(n)]
         g = grad if grad.dtype == torch.float32 else grad.float()
-        dxs = group_relkl_bwd(pairs, reserve, g, causal=ctx.causal, scale=ctx.scale,
-                              head_maps=ctx.head_maps, rope=ctx.rope)
+        dxs = group_relkl_bwd(pairs, lse_t, lse_s, diag, g, reserve=reserve, causal=ctx.causal,
+                              scale=ctx.scale, head_maps=ctx.head_maps, rope=ctx.rope)
         grads = [None, None, None, None]
         for dx in dxs:
             grads.extend([None, dx])

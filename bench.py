@@ -158,8 +158,9 @@ def host_info(avail):
 
 def mem_sweep(relkl, torch, dev, d=128, H=32, ns=(4096, 8192, 16384, 32768)):
     """Extra device memory of one causal bf16 relation call (fwd + bwd) against N: the peak
-    allocation during the call beyond the inputs and the gradient it returns, next to the
-    library's own reserve/workspace sizes and a materialised fp32 relation (H N^2 4 B)."""
+    allocation during the call beyond the inputs and the gradient it returns (the forward's
+    per-row state, its loss partials and the backward's workspace), next to a materialised
+    fp32 relation (H N^2 4 B)."""
     rows = []
     for n in ns:
         torch.cuda.synchronize()
@@ -172,11 +173,12 @@ def mem_sweep(relkl, torch, dev, d=128, H=32, ns=(4096, 8192, 16384, 32768)):
         base = torch.cuda.memory_allocated(dev)
         torch.cuda.reset_peak_memory_stats(dev)
         f = relkl.relkl_fwd(xt, xs, causal=True)
-        dx = relkl.relkl_bwd(xt, xs, f["reserve"], gl, causal=True)
+        dx = relkl.relkl_bwd(xt, xs, f["lse_t"], f["lse_s"], f["diag_delta"], gl, causal=True)
         torch.cuda.synchronize()
         extra = torch.cuda.max_memory_allocated(dev) - base - dx.numel() * dx.element_size()
+        state = sum(f[k].numel() * 4 for k in ("lse_t", "lse_s", "diag_delta"))
         rows.append({"N": n, "extra_mb": round(extra / 1e6, 2),
-                     "reserve_mb": round(f["reserve"].numel() / 1e6, 2),
+                     "state_mb": round(state / 1e6, 2),
                      "bwd_workspace_mb": round(relkl.workspace_size(xt, xs, pass_=1) / 1e6, 2),
                      "materialised_fp32_gb": round(H * n * n * 4 / 1e9, 2)})
         del xt, xs, f, dx
@@ -212,7 +214,8 @@ def rope_fused_timing(relkl, workloads, wl, dev, causal, steps, tokens, plain_ms
             f = relkl.rope_relkl_fwd(xt, xs, *tabs, causal=causal)
             if record:
                 ev[1].record(stream)
-            relkl.rope_relkl_bwd(xs, f["reserve"], gl, *tabs, causal=causal)
+            relkl.rope_relkl_bwd(xs, f["reserve"], f["lse_t"], f["lse_s"], f["diag_delta"], gl,
+                                 *tabs, causal=causal)
             if record:
                 ev[2].record(stream)
                 log.append(ev)
@@ -257,7 +260,8 @@ def cross_timing(relkl, workloads, wl, dev, causal, steps, tokens):
         f = relkl.cross_relkl_fwd(a_t, b_t, a_s, b_s, rope=tabs, causal=causal)
         if record:
             ev[1].record(stream)
-        relkl.cross_relkl_bwd(a_s, b_s, f["reserve"], gl, rope=tabs, causal=causal)
+        relkl.cross_relkl_bwd(a_s, b_s, f["reserve"], f["lse_t"], f["lse_s"], gl, rope=tabs,
+                              causal=causal)
         if record:
             ev[2].record(stream)
             log.append(ev)
@@ -299,11 +303,13 @@ def group_timing(relkl, workloads, dev, steps):
         def separate():
             for xt, xs in pairs:
                 f = relkl.relkl_fwd(xt, xs, causal=causal)
-                relkl.relkl_bwd(xt, xs, f["reserve"], gl, causal=causal)
+                relkl.relkl_bwd(xt, xs, f["lse_t"], f["lse_s"], f["diag_delta"], gl,
+                                causal=causal)
 
         def grouped():
             f = relkl.group_relkl_fwd(pairs, causal=causal)
-            relkl.group_relkl_bwd(pairs, f["reserve"], gl, causal=causal)
+            relkl.group_relkl_bwd(pairs, f["lse_t"], f["lse_s"], f["diag_delta"], gl,
+                                  causal=causal)
 
         best = {}
         for fn, label in ((separate, "separate"), (grouped, "group")) * 2:
@@ -402,7 +408,7 @@ def main():
             f = relkl.relkl_fwd(xt, xs, causal=causal)
             if record:
                 e1.record(stream)
-            relkl.relkl_bwd(xt, xs, f["reserve"], gl, causal=causal)
+            relkl.relkl_bwd(xt, xs, f["lse_t"], f["lse_s"], f["diag_delta"], gl, causal=causal)
             if record:
                 e2.record(stream)
                 ev_log.append((name, e0, e1, e2))

@@ -13,19 +13,21 @@
  *   and, for an upstream gradient g of the loss,
  *     dZ    = g * (R_s - R_t)  (0 where masked)
  *     dX_s  = scale * (dZ + dZ^T) X_s       (the teacher is frozen: no teacher gradient)
- * "Phase 1" keeps only per-row log-sum-exp statistics; the backward recomputes the logits
- * tile by tile, so no N x N matrix is ever stored.  Between the two calls the library keeps
- * a caller-owned "reserve" buffer (see lard_relkl_reserve_size): the row statistics in
- * log2 units and, for bf16 inputs, IEEE fp16 copies of the teacher and student rows that
- * the backward uses as its matrix-core operands.  Its size is linear in N.
+ * "Phase 1" keeps only per-row statistics; the backward recomputes the logits tile by tile
+ * from them, so no N x N matrix is ever stored.  The forward returns, per row i, the
+ * log-sum-exp LSE_m(i) of both sides and diag_delta(i) = R_s(i,i) - R_t(i,i); the backward
+ * takes exactly these three fp32 vectors (12 bytes per row and head) plus the inputs.  The
+ * diagonal entry Z_m(i,i) = scale |X_m(i)|^2 carries most of a row's mass, so the fp32 LSE
+ * alone cannot resolve R_m(i,i) to the precision a nearly-equal teacher and student need;
+ * the forward computes that entry from |X_m(i)|^2 in fp64 and hands over the difference.
  *
  * Mask: causal = 1 keeps j <= i (the diagonal included); causal = 0 keeps every entry.
  * The returned loss is the plain sum; the pages' mean over rows is loss / N and its
  * gradient is obtained by passing g = 1 / N.
  *
  * Conventions shared by every entry point:
- *  - Pointers named x_*, lse_*, row_kl, loss, reserve, grad_loss, dx_student and
- *    workspace are DEVICE pointers; head_map and the descriptors are HOST pointers.
+ *  - Pointers named x_*, lse_*, diag_delta, row_kl, loss, reserve, grad_loss, dx_student
+ *    and workspace are DEVICE pointers; head_map and the descriptors are HOST pointers.
  *  - All validation happens on the host before any HIP call; a failed validation
  *    returns LARD_ERR_INVALID_ARGUMENT / LARD_ERR_UNSUPPORTED /
  *    LARD_ERR_WORKSPACE_TOO_SMALL and touches no device memory.
@@ -37,10 +39,11 @@
  *    until the enqueued work has completed.
  *  - Results are bitwise reproducible for a fixed shape and split count.
  *  - NaN / Inf inputs are not checked and propagate.
- *  - For bf16 inputs the backward computes in IEEE fp16: the reserve holds fp16 copies
- *    of the inputs (bf16 -> fp16 is exact for 2^-17 <= |x| < 65504; smaller magnitudes
- *    keep an absolute error below 2^-25), and dZ is carried as fp16 scaled by 2^14.
- *    Inputs with |x| >= 65504 are not supported by the bf16 backward.
+ *  - For bf16 inputs the backward recomputes the scores on the bf16 rows as given and
+ *    contracts the gradient in IEEE fp16: each staged student tile is converted on chip
+ *    (bf16 -> fp16 is exact for 2^-17 <= |x| < 65504; smaller magnitudes keep an absolute
+ *    error below 2^-25), and dZ is carried as fp16 scaled by 2^14.  Inputs with
+ *    |x| >= 65504 are not supported by the bf16 backward.
  */
 #ifndef LARD_H
 #define LARD_H
@@ -107,48 +110,46 @@ typedef struct lard_grad_desc {
 
 /*
  * Bytes of device workspace that lard_relkl_fwd (pass = 0) or lard_relkl_bwd (pass = 1)
- * needs for this descriptor (0 is possible).  Returns 0 and sets *status (if non-NULL)
- * on an invalid descriptor.  The backward workspace depends on the split count the
- * library picks for the shape (environment variable LARD_SPLITK overrides it).
+ * needs for this descriptor (the RoPE-fused and cross entry points use the same sizes).
+ * Returns 0 and sets *status (if non-NULL) on an invalid descriptor.  The forward's
+ * workspace holds one fp64 loss partial per workgroup (8 * B * H * ceil(N / 128) bytes,
+ * rounded up to 256); the backward's holds fp32 split-K partials and is 0 bytes unless the
+ * library splits the key range, which it does only when the (batch, head, row tile) work
+ * alone cannot fill the chip (environment variable LARD_SPLITK overrides the split count).
  */
 size_t lard_relkl_workspace_size(const lard_relkl_desc* desc, int pass, lard_status* status);
-
-/*
- * Bytes of the reserve buffer that lard_relkl_fwd writes and lard_relkl_bwd reads for
- * this descriptor: 2 * 4 * B * H * roundup(N, 64) for fp32 inputs, plus
- * 2 * 2 * B * H * N * d for bf16 inputs (each part rounded up to 256 bytes).  Returns 0
- * and sets *status (if non-NULL) on an invalid descriptor.
- */
-size_t lard_relkl_reserve_size(const lard_relkl_desc* desc, lard_status* status);
 
 /*
  * Forward ("phase 1" plus the KL accumulation; key_machinery of the verdict page).
  *   x_teacher, x_student : device, desc layout and dtype, read only.
  *   lse_teacher, lse_student : device fp32 [B, H, N] (dense), written: LSE_m(i) in nats.
+ *   diag_delta : device fp32 [B, H, N] or NULL; written: R_s(i,i) - R_t(i,i).  Required by
+ *            lard_relkl_bwd (a caller that only wants the loss may pass NULL).
  *   row_kl : device fp32 [B, H, N] or NULL; written: KL_i.
  *   loss   : device fp32 scalar, written (not accumulated): sum of KL_i over b, h, i,
  *            reduced in a fixed order in fp64.
- *   reserve : device, >= lard_relkl_reserve_size(desc) bytes, 256-byte aligned; written,
- *            and must be passed unchanged to lard_relkl_bwd for the same inputs.
  *   workspace : device, >= lard_relkl_workspace_size(desc, 0) bytes, 8-byte aligned.
  */
 lard_status lard_relkl_fwd(const lard_relkl_desc* desc, const void* x_teacher,
                            const void* x_student, float* lse_teacher, float* lse_student,
-                           float* row_kl, float* loss, void* reserve, size_t reserve_bytes,
-                           void* workspace, size_t workspace_bytes, void* stream);
+                           float* diag_delta, float* row_kl, float* loss, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /*
  * Backward (logit recomputation fused with the gradient; key_machinery and the gradient
  * identity of core_discovery on the verdict page).
  *   x_teacher, x_student : the inputs given to lard_relkl_fwd.
- *   reserve : device, as written by lard_relkl_fwd for the same inputs and descriptor.
+ *   lse_teacher, lse_student, diag_delta : device fp32 [B, H, N], as written by
+ *            lard_relkl_fwd for the same inputs and descriptor (the only state kept
+ *            between the two passes).
  *   grad_loss : device fp32 scalar g (the upstream gradient of `loss`).
  *   dx_student : device, layout and dtype given by `grad`; see lard_grad_desc.
  *   workspace : device, >= lard_relkl_workspace_size(desc, 1) bytes, 16-byte aligned
  *            (may be NULL when that size is 0).
  */
 lard_status lard_relkl_bwd(const lard_relkl_desc* desc, const void* x_teacher,
-                           const void* x_student, const void* reserve, size_t reserve_bytes,
+                           const void* x_student, const float* lse_teacher,
+                           const float* lse_student, const float* diag_delta,
                            const float* grad_loss, const lard_grad_desc* grad,
                            void* dx_student, void* workspace, size_t workspace_bytes,
                            void* stream);
@@ -173,12 +174,11 @@ lard_status lard_relkl_bwd(const lard_relkl_desc* desc, const void* x_teacher,
  * them), 16-byte aligned.  Each side's pair is either both non-NULL or both NULL (that
  * side is not rotated, e.g. the V relation).  Every relation head uses the same tables.
  *
- * The reserve holds the rotated rows of both sides (IEEE fp16, round to nearest even, for
- * bf16 inputs; fp32 for fp32 inputs) plus the row statistics; size from
- * lard_relkl_rope_reserve_size.  Workspaces are those of lard_relkl_workspace_size.  For
- * bf16 inputs the rotated values must stay below 65504 in magnitude (|x| < 46000 is
- * enough); the matrix work runs on the fp16 copies, so the loss carries the rounding of
- * the rotated rows to fp16 (2^-11 relative per element) on top of the plain path's.
+ * The rotated rows are rounded to the input dtype (bf16: nearest even), as the model would
+ * hand them to the plain operation, and the plain kernels run on them.  The reserve holds
+ * them for the backward (a caller-owned buffer of 2 * e * B * H * N * d bytes, e the
+ * element size, from lard_relkl_rope_reserve_size); the row statistics are the outputs, as
+ * for the plain entry points.  Workspaces are those of lard_relkl_workspace_size.
  * Validation, ownership, stream and error conventions are those of the plain entry points.
  */
 typedef struct lard_rope_desc {
@@ -189,32 +189,34 @@ typedef struct lard_rope_desc {
 } lard_rope_desc;
 
 /* Bytes of the reserve the RoPE-fused forward writes: 2 * c * B * H * N * d (c = 2 for
- * bf16, 4 for fp32 inputs) plus 2 * 4 * B * H * roundup(N, 64), each part rounded up to
- * 256 bytes.  Returns 0 and sets *status on an invalid descriptor. */
+ * bf16, 4 for fp32 inputs), each copy rounded up to 256 bytes.  Returns 0 and sets *status
+ * on an invalid descriptor. */
 size_t lard_relkl_rope_reserve_size(const lard_relkl_desc* desc, lard_status* status);
 
 /*
  * RoPE-fused forward.  x_teacher, x_student: pre-rotation inputs (desc layout and dtype).
- * Outputs, reserve and workspace as for lard_relkl_fwd (reserve sized by
- * lard_relkl_rope_reserve_size).
+ * Outputs and workspace as for lard_relkl_fwd; reserve: device, 256-byte aligned, at least
+ * lard_relkl_rope_reserve_size bytes, written (the rotated rows).
  */
 lard_status lard_relkl_rope_fwd(const lard_relkl_desc* desc, const lard_rope_desc* rope,
                                 const void* x_teacher, const void* x_student,
-                                float* lse_teacher, float* lse_student, float* row_kl,
-                                float* loss, void* reserve, size_t reserve_bytes,
+                                float* lse_teacher, float* lse_student, float* diag_delta,
+                                float* row_kl, float* loss, void* reserve, size_t reserve_bytes,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * RoPE-fused backward: the gradient of g * loss with respect to the student's
  * PRE-rotation input, written like lard_relkl_bwd's (heads outside head_map untouched).
- * Needs only the reserve the fused forward wrote (it holds the rotated operands) and the
- * same `rope` tables (the student's rotate the gradient back).
+ * Needs the reserve the fused forward wrote (it holds the rotated operands), the forward's
+ * lse_teacher, lse_student and diag_delta, and the same `rope` tables (the student's
+ * rotate the gradient back).
  */
 lard_status lard_relkl_rope_bwd(const lard_relkl_desc* desc, const lard_rope_desc* rope,
                                 const void* reserve, size_t reserve_bytes,
-                                const float* grad_loss, const lard_grad_desc* grad,
-                                void* dx_student, void* workspace, size_t workspace_bytes,
-                                void* stream);
+                                const float* lse_teacher, const float* lse_student,
+                                const float* diag_delta, const float* grad_loss,
+                                const lard_grad_desc* grad, void* dx_student, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /*
  * Cross-relation entry points: the same row-wise KL for the relation between two different
@@ -230,8 +232,9 @@ lard_status lard_relkl_rope_bwd(const lard_relkl_desc* desc, const lard_rope_des
  * rotate both its A and its B (as RoPE rotates queries and keys alike; see the RoPE-fused
  * entry points for the rotation, rounding and table layout) and the gradients are returned
  * with respect to the pre-rotation inputs.  The reserve holds copies of all four matrices
- * (fp16 images of bf16 values, or fp32) and the row statistics; size from
- * lard_relkl_cross_reserve_size.  Workspaces are those of lard_relkl_workspace_size.
+ * (fp16 images of bf16 values, or fp32); size from lard_relkl_cross_reserve_size.  The row
+ * statistics are the LSE outputs (no matrix entry is special here, so there is no
+ * diag_delta).  Workspaces are those of lard_relkl_workspace_size.
  * Validation, ownership, stream and error conventions are those of the plain entry points.
  */
 typedef struct lard_cross_desc {
@@ -240,8 +243,8 @@ typedef struct lard_cross_desc {
 } lard_cross_desc;
 
 /* Bytes of the reserve the cross forward writes: 4 * c * B * H * N * d (c = 2 for bf16, 4
- * for fp32 inputs) plus 2 * 4 * B * H * roundup(N, 64), each part rounded up to 256 bytes.
- * Returns 0 and sets *status on an invalid descriptor. */
+ * for fp32 inputs), each copy rounded up to 256 bytes.  Returns 0 and sets *status on an
+ * invalid descriptor. */
 size_t lard_relkl_cross_reserve_size(const lard_relkl_desc* desc, lard_status* status);
 
 /*
@@ -258,11 +261,13 @@ lard_status lard_relkl_cross_fwd(const lard_relkl_desc* desc, const lard_cross_d
 
 /*
  * Cross backward: dA_s and dB_s of g * loss, each written like lard_relkl_bwd's gradient
- * (layout and dtype from grad_a / grad_b; heads outside head_map untouched).  Needs only the
- * reserve the cross forward wrote and the same `rope` (NULL if the forward had none).
+ * (layout and dtype from grad_a / grad_b; heads outside head_map untouched).  Needs the
+ * reserve the cross forward wrote, its lse_teacher and lse_student, and the same `rope`
+ * (NULL if the forward had none).
  */
 lard_status lard_relkl_cross_bwd(const lard_relkl_desc* desc, const lard_rope_desc* rope,
                                  const void* reserve, size_t reserve_bytes,
+                                 const float* lse_teacher, const float* lse_student,
                                  const float* grad_loss, const lard_grad_desc* grad_a,
                                  void* da_student, const lard_grad_desc* grad_b,
                                  void* db_student, void* workspace, size_t workspace_bytes,
@@ -290,8 +295,9 @@ lard_status lard_relkl_cross_bwd(const lard_relkl_desc* desc, const lard_rope_de
  *   `rope` tables (a pair of NULL tables: that side is not rotated, e.g. the V relation),
  *   as lard_relkl_rope_fwd / _bwd; the gradients are with respect to the pre-rotation
  *   inputs.
- * The reserve holds every member's reserve (as sized by the single-problem entry points)
- * back to back; sizes from lard_relkl_group_reserve_size and
+ * With with_rope = 1 the reserve holds every member's rotated rows (as sized by
+ * lard_relkl_rope_reserve_size) back to back; with with_rope = 0 no reserve is needed (it
+ * may be NULL with reserve_bytes 0).  Sizes from lard_relkl_group_reserve_size and
  * lard_relkl_group_workspace_size.  Validation, ownership, stream and error conventions
  * are those of the single-problem entry points.
  */
@@ -299,16 +305,18 @@ typedef struct lard_relkl_member {
   lard_relkl_desc desc;
   const void* x_teacher;    /* device, desc layout and dtype                          */
   const void* x_student;    /* (with_rope = 1: before the rotation)                   */
-  float* lse_teacher;       /* device fp32 [B, H, N], written by the forward          */
-  float* lse_student;
+  float* lse_teacher;       /* device fp32 [B, H, N], written by the forward, read by  */
+  float* lse_student;       /*   the backward                                          */
+  float* diag_delta;        /* device fp32 [B, H, N] (as lard_relkl_fwd's); the forward */
+                            /*   may take NULL, the backward needs it                   */
   float* row_kl;            /* device fp32 [B, H, N] or NULL                          */
   float* loss;              /* device fp32 scalar or NULL: this member's own sum      */
   lard_rope_desc rope;      /* tables of this member (read when with_rope = 1)        */
 } lard_relkl_member;
 
-/* Bytes of the reserve a grouped forward writes: the sum of the members' reserves
- * (lard_relkl_reserve_size, or lard_relkl_rope_reserve_size when with_rope = 1).  Returns
- * 0 and sets *status on an invalid group. */
+/* Bytes of the reserve a grouped forward writes: 0 for with_rope = 0, else the sum of the
+ * members' lard_relkl_rope_reserve_size.  Returns 0 and sets *status on an invalid
+ * group. */
 size_t lard_relkl_group_reserve_size(int n, const lard_relkl_member* members, int with_rope,
                                      lard_status* status);
 
@@ -317,10 +325,10 @@ size_t lard_relkl_group_workspace_size(int n, const lard_relkl_member* members, 
                                        lard_status* status);
 
 /*
- * Grouped forward.  Writes every member's LSE vectors, row KL (if requested) and own loss
- * (if requested), and `loss`: device fp32 scalar = the sum over all members, reduced in a
- * fixed order in fp64.  reserve and workspace as for lard_relkl_fwd, sized by the group
- * functions above.
+ * Grouped forward.  Writes every member's LSE vectors, diag_delta and row KL (if
+ * requested) and own loss (if requested), and `loss`: device fp32 scalar = the sum over all
+ * members, reduced in a fixed order in fp64.  reserve (with_rope = 1) and workspace sized
+ * by the group functions above.
  */
 lard_status lard_relkl_group_fwd(int n, const lard_relkl_member* members, int with_rope,
                                  float* loss, void* reserve, size_t reserve_bytes,
@@ -330,8 +338,9 @@ lard_status lard_relkl_group_fwd(int n, const lard_relkl_member* members, int wi
  * Grouped backward: the gradient of g * loss (g = *grad_loss, loss = the group's sum) with
  * respect to every member's student input, written to dx_student[k] with layout grads[k]
  * (all members' gradients of one dtype; heads outside a member's head map untouched).
- * members, with_rope and reserve: as given to lard_relkl_group_fwd (the members' output
- * pointers are not read; with with_rope = 1 neither are the inputs).
+ * members, with_rope and reserve: as given to lard_relkl_group_fwd; the backward reads the
+ * members' lse_teacher, lse_student and diag_delta as the forward wrote them (row_kl and
+ * loss are not read; with with_rope = 1 neither are the inputs).
  */
 lard_status lard_relkl_group_bwd(int n, const lard_relkl_member* members, int with_rope,
                                  const void* reserve, size_t reserve_bytes,

@@ -20,13 +20,12 @@ part of the operation:
       X[p, k + d/2] = Xpre[p, k + d/2] cos[p, k] + Xpre[p, k] sin[p, k]
   (the complex product (Xpre[p, k] + i Xpre[p, k + d/2]) e^{i angle}).  A side without
   tables is not rotated (the V relation).
-* The rotated rows are the relation inputs in the activations' own dtype, exactly as when
-  the model applies RoPE itself and hands the result to the plain relation KL: each
-  rotated element is evaluated in fp32 as one fused multiply-add on a rounded product
-  (``x_k cos - (x_{k+d/2} sin)``, ``x_{k+d/2} cos + (x_k sin)``), the precision the
-  kernel evaluates it in, so that both sides round the same value, and then rounded to
-  the input dtype (bf16: to nearest, ties to even).  ``dtype=None`` keeps the exact
-  float64 rotation instead (used by the pins that differentiate through it).
+* The rotated rows are the relation inputs in the activations' own dtype, as when the
+  model applies RoPE itself and hands the result to the plain relation KL: the exact
+  rotation (float64 here; the products of a bf16 or fp32 value with an fp32 table entry
+  are exact in float64, and the sum of two of them is off by at most one float64 rounding)
+  rounded once to the input dtype, to nearest with ties to even.  ``dtype=None`` keeps the
+  exact float64 rotation (used by the pins that differentiate through it).
 * The loss is the relation KL of ``oracle.relkl`` on the rotated inputs.
 * The gradient with respect to the student's pre-rotation input is the transposed
   rotation of the gradient with respect to X_s (the rounding to the dtype passes the
@@ -44,7 +43,8 @@ import numpy as np
 
 from . import relkl
 
-__all__ = ["rotate", "rotate_back", "round_bf16", "rotate_in_dtype", "forward", "backward"]
+__all__ = ["rotate", "rotate_back", "round_bf16", "round_fp32", "rotate_in_dtype", "forward",
+           "backward"]
 
 
 def _tab(t):
@@ -81,32 +81,22 @@ def round_bf16(v) -> np.ndarray:
     return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
 
 
-def _f32(v):
+def round_fp32(v) -> np.ndarray:
+    """Round to the nearest fp32 value, ties to even (numpy's float64 -> float32 cast)."""
     return np.asarray(v, dtype=np.float64).astype(np.float32).astype(np.float64)
 
 
 def rotate_in_dtype(x, cos, sin, dtype) -> np.ndarray:
-    """The rotated rows as the operation uses them: every element evaluated in fp32 as one
-    fused multiply-add on a rounded product, then rounded to ``dtype`` ("bf16" or "fp32");
-    dtype None gives the exact rotation.  Inputs and tables must hold values of the given
-    dtype and of fp32 respectively (as the device receives them).
-
-    The fused multiply-add is computed in float64 (the fp32 product is exact there) and
-    rounded to fp32; this double rounding can differ from a true fused one only when the
-    float64 result lands on an fp32 halfway point, about once in 2^29 elements."""
+    """The rotated rows as the operation uses them: the exact rotation rounded once to
+    ``dtype`` ("bf16" or "fp32"); dtype None gives the exact rotation unrounded.  A side
+    without tables is returned as given (its values are already of the dtype)."""
+    y = rotate(x, cos, sin)
     if dtype is None or (cos is None and sin is None):
-        return rotate(x, cos, sin)
-    x = np.asarray(x, dtype=np.float64)
-    cos, sin = _tab(cos), _tab(sin)
-    h = x.shape[-1] // 2
-    x1, x2 = x[..., :h], x[..., h:]
-    y1 = _f32(x1 * cos - _f32(x2 * sin))
-    y2 = _f32(x2 * cos + _f32(x1 * sin))
-    y = np.concatenate((y1, y2), axis=-1)
+        return y
     if dtype == "bf16":
         return round_bf16(y)
     if dtype == "fp32":
-        return y
+        return round_fp32(y)
     raise ValueError(f"unknown dtype {dtype!r}")
 
 

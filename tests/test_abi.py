@@ -22,6 +22,13 @@ def lib():
     return relkl.load_library()
 
 
+@pytest.fixture(autouse=True)
+def no_launch(monkeypatch):
+    """Every call here uses fake device addresses: with the launch wrapper told to fail, a
+    call that passes validation returns LARD_ERR_HIP instead of reaching a GPU."""
+    monkeypatch.setenv("LARD_FAULT_INJECT", "1")
+
+
 def declared_functions():
     src = open(os.path.join(ROOT, "include", "lard.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
@@ -31,7 +38,7 @@ def declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) >= {"lard_relkl_fwd", "lard_relkl_bwd", "lard_relkl_workspace_size",
-                          "lard_relkl_reserve_size", "lard_status_string", "lard_version",
+                          "lard_status_string", "lard_version",
                           "lard_relkl_rope_reserve_size", "lard_relkl_rope_fwd",
                           "lard_relkl_rope_bwd", "lard_relkl_cross_reserve_size",
                           "lard_relkl_cross_fwd", "lard_relkl_cross_bwd",
@@ -39,7 +46,7 @@ def test_exports_every_declared_symbol(lib):
                           "lard_relkl_group_fwd", "lard_relkl_group_bwd"}
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.lard_version() >= 10000
+    assert lib.lard_version() >= 20000
 
 
 def test_status_strings(lib):
@@ -63,17 +70,17 @@ def ws_query(lib, desc, pass_=0):
     return n, st.value
 
 
-def fwd(lib, desc, xt=FAKE, xs=FAKE, lt=FAKE, ls=FAKE, kl=None, loss=FAKE, rs=FAKE,
-        nrs=1 << 30, ws=FAKE, nws=1 << 20):
+def fwd(lib, desc, xt=FAKE, xs=FAKE, lt=FAKE, ls=FAKE, dg=FAKE, kl=None, loss=FAKE, ws=FAKE,
+        nws=1 << 20):
     return lib.lard_relkl_fwd(ctypes.byref(desc) if desc is not None else None, xt, xs, lt, ls,
-                              kl, loss, rs, nrs, ws, nws, None)
+                              dg, kl, loss, ws, nws, None)
 
 
-def bwd(lib, desc, g=None, xt=FAKE, xs=FAKE, rs=FAKE, nrs=1 << 30, dx=FAKE, ws=FAKE,
-        nws=1 << 30):
+def bwd(lib, desc, g=None, xt=FAKE, xs=FAKE, lt=FAKE, ls=FAKE, dg=FAKE, gl=FAKE, dx=FAKE,
+        ws=FAKE, nws=1 << 30):
     g = g or _GradDesc(dtype=1, reserved=0, stride_b=4 * 100 * 128, stride_h=100 * 128,
                        stride_n=128)
-    return lib.lard_relkl_bwd(ctypes.byref(desc), xt, xs, rs, nrs, FAKE, ctypes.byref(g), dx,
+    return lib.lard_relkl_bwd(ctypes.byref(desc), xt, xs, lt, ls, dg, gl, ctypes.byref(g), dx,
                               ws, nws, None)
 
 
@@ -81,13 +88,15 @@ def test_workspace_sizes(lib):
     n0, st = ws_query(lib, good_desc(), 0)
     assert st == OK and n0 >= 8 and n0 % 256 == 0
     n1, st = ws_query(lib, good_desc(), 1)
-    assert st == OK and n1 > 0  # 4 units x 1 row tile: the backward splits its key range
+    # 4 units x 1 row tile: the backward splits its key range (2 tiles) in two
+    assert st == OK and n1 == 2 * 4 * 256 * 128 * 4
     big = good_desc(N=32768, H_in=32, H=32, t_stride_h=32768 * 128, t_stride_b=32 * 32768 * 128,
                     s_stride_h=32768 * 128, s_stride_b=32 * 32768 * 128)
     n1, st = ws_query(lib, big, 1)
-    assert st == OK and n1 == 0  # the grid fills the chip: no split, no workspace
+    # the grid fills the chip: no split, no workspace (the state is the forward's outputs)
+    assert st == OK and n1 == 0
     n0, st = ws_query(lib, big, 0)
-    assert st == OK and n0 < 32 * 32768  # O(B * H * N / 256) partial sums
+    assert st == OK and n0 < 32 * 32768  # O(B * H * N / 128) partial sums
     _, st = ws_query(lib, good_desc(), 2)
     assert st == INVALID
 
@@ -137,27 +146,16 @@ def test_head_map_validation(lib):
     del keep
 
 
-def test_reserve_size(lib):
-    st = ctypes.c_int(-1)
-    d = good_desc()  # bf16, B=1, H=4, N=100, d=128
-    n = lib.lard_relkl_reserve_size(ctypes.byref(d), ctypes.byref(st))
-    assert st.value == OK
-    copies = 2 * (((4 * 100 * 128 * 2) + 255) // 256 * 256)
-    stats = 2 * (((4 * 128 * 4) + 255) // 256 * 256)
-    assert n == copies + stats
-    d32 = good_desc(dtype=0)
-    assert lib.lard_relkl_reserve_size(ctypes.byref(d32), ctypes.byref(st)) == stats
-    assert lib.lard_relkl_reserve_size(ctypes.byref(good_desc(d=32)), ctypes.byref(st)) == 0
-    assert st.value == UNSUPPORTED
-
-
 def test_pointer_and_workspace_validation(lib):
     d = good_desc()
-    assert fwd(lib, d, rs=None) == INVALID
-    assert fwd(lib, d, rs=FAKE + 16) == INVALID    # reserve must be 256-byte aligned
-    assert fwd(lib, d, nrs=16) == WS_SMALL
-    assert bwd(lib, d, rs=None) == INVALID
-    assert bwd(lib, d, nrs=16) == WS_SMALL
+    assert fwd(lib, d, dg=None) == HIP             # diag_delta is optional in the forward
+    assert fwd(lib, d, dg=FAKE + 2) == INVALID     # misaligned state vector
+    assert fwd(lib, d, lt=None) == INVALID
+    assert bwd(lib, d, dg=None) == INVALID         # the backward needs the forward's state
+    assert bwd(lib, d, ls=None) == INVALID
+    assert bwd(lib, d, lt=FAKE + 1) == INVALID
+    assert bwd(lib, d, gl=None) == INVALID
+    assert bwd(lib, d, ws=FAKE + 8) == INVALID     # workspace must be 16-byte aligned
     assert fwd(lib, None) == INVALID
     assert fwd(lib, d, xt=None) == INVALID
     assert fwd(lib, d, loss=None) == INVALID
@@ -198,24 +196,24 @@ def test_python_layer_refuses_cpu_tensors():
 # ------------------------------------------------------------------ RoPE-fused entry points
 def rope_fwd(lib, desc, rope, rs=FAKE, nrs=1 << 30):
     return lib.lard_relkl_rope_fwd(ctypes.byref(desc), ctypes.byref(rope) if rope else None,
-                                   FAKE, FAKE, FAKE, FAKE, None, FAKE, rs, nrs, FAKE, 1 << 20,
-                                   None)
+                                   FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, rs, nrs, FAKE,
+                                   1 << 20, None)
 
 
-def rope_bwd(lib, desc, rope, rs=FAKE, nrs=1 << 30):
+def rope_bwd(lib, desc, rope, rs=FAKE, nrs=1 << 30, dg=FAKE):
     g = _GradDesc(dtype=1, reserved=0, stride_b=4 * 100 * 128, stride_h=100 * 128, stride_n=128)
     return lib.lard_relkl_rope_bwd(ctypes.byref(desc), ctypes.byref(rope) if rope else None,
-                                   rs, nrs, FAKE, ctypes.byref(g), FAKE, FAKE, 1 << 30, None)
+                                   rs, nrs, FAKE, FAKE, dg, FAKE, ctypes.byref(g), FAKE, FAKE,
+                                   1 << 30, None)
 
 
 def test_rope_reserve_size(lib):
     st = ctypes.c_int(-1)
-    stats = 2 * (((4 * 128 * 4) + 255) // 256 * 256)
     n = lib.lard_relkl_rope_reserve_size(ctypes.byref(good_desc()), ctypes.byref(st))
-    assert st.value == OK and n == 2 * (((4 * 100 * 128 * 2) + 255) // 256 * 256) + stats
-    # fp32 inputs keep fp32 rotated copies
+    # the rotated rows of both sides in the input dtype, nothing else
+    assert st.value == OK and n == 2 * (((4 * 100 * 128 * 2) + 255) // 256 * 256)
     n = lib.lard_relkl_rope_reserve_size(ctypes.byref(good_desc(dtype=0)), ctypes.byref(st))
-    assert st.value == OK and n == 2 * (((4 * 100 * 128 * 4) + 255) // 256 * 256) + stats
+    assert st.value == OK and n == 2 * (((4 * 100 * 128 * 4) + 255) // 256 * 256)
     assert lib.lard_relkl_rope_reserve_size(ctypes.byref(good_desc(N=0)), ctypes.byref(st)) == 0
     assert st.value == INVALID
 
@@ -228,15 +226,12 @@ def test_rope_validation(lib):
     assert rope_fwd(lib, d, _RopeDesc(None, None, None, FAKE)) == INVALID
     assert rope_fwd(lib, d, _RopeDesc(FAKE + 4, FAKE, None, None)) == INVALID  # misaligned
     assert rope_bwd(lib, d, _RopeDesc(None, None, FAKE, FAKE + 8)) == INVALID
-    plain = lib.lard_relkl_reserve_size(ctypes.byref(d), None)
     need = lib.lard_relkl_rope_reserve_size(ctypes.byref(d), None)
     assert rope_fwd(lib, d, both, nrs=need - 1) == WS_SMALL
     assert rope_bwd(lib, d, both, nrs=need - 1) == WS_SMALL
     assert rope_fwd(lib, d, both, rs=FAKE + 64) == INVALID            # reserve alignment
-    d32 = good_desc(dtype=0)
-    # the fp32 reserve of the plain path has no copies: too small for the fused path
-    assert rope_fwd(lib, d32, both, nrs=lib.lard_relkl_reserve_size(ctypes.byref(d32), None)) == WS_SMALL
-    assert plain == need  # bf16: the same fp16 copies, rotated
+    assert rope_fwd(lib, d, both, rs=None) == INVALID
+    assert rope_bwd(lib, d, both, dg=None) == INVALID                 # needs the diag state
 
 
 def test_rope_fault_injection_maps_to_hip_error(lib, monkeypatch):
@@ -269,22 +264,22 @@ def cross_fwd(lib, desc, keys, rope=None, rs=FAKE, nrs=1 << 30):
                                     FAKE, FAKE, None, FAKE, rs, nrs, FAKE, 1 << 20, None)
 
 
-def cross_bwd(lib, desc, ga=None, gb=None, rope=None, rs=FAKE, nrs=1 << 30, da=FAKE, db=FAKE):
+def cross_bwd(lib, desc, ga=None, gb=None, rope=None, rs=FAKE, nrs=1 << 30, da=FAKE, db=FAKE,
+              lt=FAKE):
     g = _GradDesc(dtype=1, reserved=0, stride_b=4 * 100 * 128, stride_h=100 * 128, stride_n=128)
     ga = ga or g
     gb = gb or g
     return lib.lard_relkl_cross_bwd(ctypes.byref(desc), ctypes.byref(rope) if rope else None,
-                                    rs, nrs, FAKE, ctypes.byref(ga), da, ctypes.byref(gb), db,
-                                    FAKE, 1 << 30, None)
+                                    rs, nrs, lt, FAKE, FAKE, ctypes.byref(ga), da,
+                                    ctypes.byref(gb), db, FAKE, 1 << 30, None)
 
 
 def test_cross_reserve_size(lib):
     st = ctypes.c_int(-1)
-    stats = 2 * (((4 * 128 * 4) + 255) // 256 * 256)
     n = lib.lard_relkl_cross_reserve_size(ctypes.byref(good_desc()), ctypes.byref(st))
-    assert st.value == OK and n == 4 * (((4 * 100 * 128 * 2) + 255) // 256 * 256) + stats
+    assert st.value == OK and n == 4 * (((4 * 100 * 128 * 2) + 255) // 256 * 256)
     n = lib.lard_relkl_cross_reserve_size(ctypes.byref(good_desc(dtype=0)), ctypes.byref(st))
-    assert st.value == OK and n == 4 * (((4 * 100 * 128 * 4) + 255) // 256 * 256) + stats
+    assert st.value == OK and n == 4 * (((4 * 100 * 128 * 4) + 255) // 256 * 256)
 
 
 def test_cross_validation(lib):
@@ -297,6 +292,7 @@ def test_cross_validation(lib):
     assert cross_fwd(lib, d, good_keys(), nrs=need - 1) == WS_SMALL
     assert cross_bwd(lib, d, nrs=need - 1) == WS_SMALL
     assert cross_bwd(lib, d, db=None) == INVALID
+    assert cross_bwd(lib, d, lt=None) == INVALID                          # needs the LSE state
     assert cross_bwd(lib, d, da=FAKE + 8) == INVALID                      # misaligned gradient
     bad = _GradDesc(dtype=1, reserved=0, stride_b=4 * 100 * 128, stride_h=100 * 128, stride_n=130)
     assert cross_bwd(lib, d, gb=bad) == INVALID
@@ -324,7 +320,7 @@ def members_of(*descs, rope=None):
     for k, d in enumerate(descs):
         ms[k].desc = d
         ms[k].x_teacher = ms[k].x_student = FAKE
-        ms[k].lse_teacher = ms[k].lse_student = ms[k].loss = FAKE
+        ms[k].lse_teacher = ms[k].lse_student = ms[k].diag_delta = ms[k].loss = FAKE
         ms[k].row_kl = None
         if rope is not None:
             ms[k].rope = rope
@@ -349,6 +345,7 @@ def group_fwd(lib, ms, with_rope=0, rs=FAKE, nrs=1 << 30, n=None):
 
 
 def group_bwd(lib, ms, grads=None, with_rope=0, nrs=1 << 30):
+    # (the reserve is read only with with_rope = 1)
     k = len(ms)
     if grads is None:
         grads = [_GradDesc(dtype=1, reserved=0, stride_b=m.desc.t_stride_b,
@@ -363,8 +360,7 @@ def test_group_sizes_are_the_sums_of_the_members(lib):
     q, kv = good_desc(), kv_desc()
     ms = members_of(q, kv, kv)
     n, st = group_query(lib, "lard_relkl_group_reserve_size", ms, 0)
-    one = [lib.lard_relkl_reserve_size(ctypes.byref(d), None) for d in (q, kv, kv)]
-    assert st == OK and n == sum(one)
+    assert st == OK and n == 0  # the plain path keeps no reserve
     n, st = group_query(lib, "lard_relkl_group_reserve_size", ms, 1)
     one = [lib.lard_relkl_rope_reserve_size(ctypes.byref(d), None) for d in (q, kv, kv)]
     assert st == OK and n == sum(one)
@@ -398,8 +394,10 @@ def test_group_validation(lib):
     assert group_fwd(lib, members_of(q, kv), with_rope=2) == INVALID
     # with_rope = 1 checks every member's tables; with_rope = 0 does not read them
     half = _RopeDesc(FAKE, None, None, None)
+    both = _RopeDesc(FAKE, FAKE, FAKE, FAKE)
     assert group_fwd(lib, members_of(q, kv, rope=half), with_rope=1, nrs=16) == INVALID
-    assert group_fwd(lib, members_of(q, kv, rope=half), with_rope=0, nrs=16) == WS_SMALL
+    assert group_fwd(lib, members_of(q, kv, rope=both), with_rope=1, nrs=16) == WS_SMALL
+    assert group_fwd(lib, members_of(q, kv, rope=both), with_rope=1, rs=None) == INVALID
     # head maps of one group: at most 512 entries together
     arr = (ctypes.c_int32 * 200)(*range(200))
     hm = ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32))
@@ -409,20 +407,25 @@ def test_group_validation(lib):
     assert st == OK
     n, st = group_query(lib, "lard_relkl_group_reserve_size", members_of(wide, wide, wide), 0)
     assert st == UNSUPPORTED and n == 0
-    # reserve too small, gradients of two dtypes, missing pointers
-    need, _ = group_query(lib, "lard_relkl_group_reserve_size", members_of(q, kv), 0)
-    assert group_fwd(lib, members_of(q, kv), nrs=need - 1) == WS_SMALL
-    assert group_bwd(lib, members_of(q, kv), nrs=need - 1) == WS_SMALL
+    # reserve too small (with rope), gradients of two dtypes, missing pointers
+    need, _ = group_query(lib, "lard_relkl_group_reserve_size", members_of(q, kv), 1)
+    assert group_bwd(lib, members_of(q, kv, rope=both), with_rope=1, nrs=need - 1) == WS_SMALL
     g16 = _GradDesc(dtype=1, reserved=0, stride_b=4 * 100 * 128, stride_h=100 * 128, stride_n=128)
     g32 = _GradDesc(dtype=0, reserved=0, stride_b=2 * 100 * 128, stride_h=100 * 128, stride_n=128)
     assert group_bwd(lib, members_of(q, kv), grads=[g16, g32]) == INVALID
     ms = members_of(q, kv)
     ms[1].lse_student = None
     assert group_fwd(lib, ms) == INVALID
+    assert group_bwd(lib, ms) == INVALID
+    ms = members_of(q, kv)
+    ms[1].diag_delta = None
+    assert group_bwd(lib, ms) == INVALID         # the backward needs every member's state
     ms = members_of(q, kv)
     ms[0].x_teacher = FAKE + 8
     assert group_fwd(lib, ms) == INVALID
     assert group_bwd(lib, ms) == INVALID         # the plain backward reads the inputs
+    ms = members_of(q, kv, rope=both)
+    ms[0].x_teacher = FAKE + 8
     assert group_bwd(lib, ms, with_rope=1, nrs=16) == WS_SMALL  # the fused one does not
     del arr
 

@@ -36,7 +36,7 @@ def check_workload(name, causal, full_loss=False, grad_units=1):
         xt, xs = rel.x_t.to(dev), rel.x_s.to(dev)
         f = relkl.relkl_fwd(xt, xs, causal=causal, want_row_kl=True)
         gl = torch.ones((), dtype=torch.float32, device=dev)
-        dx = relkl.relkl_bwd(xt, xs, f["reserve"], gl, causal=causal)
+        dx = relkl.relkl_bwd(xt, xs, f["lse_t"], f["lse_s"], f["diag_delta"], gl, causal=causal)
         torch.cuda.synchronize()
         loss = float(f["loss"].item())
         row_kl = np64(f["row_kl"])

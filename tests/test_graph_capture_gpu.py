@@ -25,18 +25,22 @@ def test_capture_and_replay(path):
     def run():
         if path == "plain":
             f = relkl.relkl_fwd(xt, xs, causal=True)
-            return f["loss"], relkl.relkl_bwd(xt, xs, f["reserve"], gl, causal=True)
+            return f["loss"], relkl.relkl_bwd(xt, xs, f["lse_t"], f["lse_s"], f["diag_delta"], gl,
+                                              causal=True)
         if path == "rope":
             f = relkl.rope_relkl_fwd(xt, xs, *tabs, causal=True)
-            return f["loss"], relkl.rope_relkl_bwd(xs, f["reserve"], gl, *tabs, causal=True)
+            return f["loss"], relkl.rope_relkl_bwd(xs, f["reserve"], f["lse_t"], f["lse_s"],
+                                                   f["diag_delta"], gl, *tabs, causal=True)
         if path == "cross":
             f = relkl.cross_relkl_fwd(xt, kt, xs, ks, rope=tabs, causal=True)
-            da, db = relkl.cross_relkl_bwd(xs, ks, f["reserve"], gl, rope=tabs, causal=True)
+            da, db = relkl.cross_relkl_bwd(xs, ks, f["reserve"], f["lse_t"], f["lse_s"], gl,
+                                           rope=tabs, causal=True)
             return f["loss"], torch.cat((da, db), dim=1)
         # grouped: Q/Q on two heads and K/K on one (a head view), both rotated inside the call
         pairs = [(xt, xs), (kt[:, :1], ks[:, :1])]
         f = relkl.group_relkl_fwd(pairs, causal=True, rope=[tabs, tabs])
-        dq, dk = relkl.group_relkl_bwd(pairs, f["reserve"], gl, causal=True, rope=[tabs, tabs])
+        dq, dk = relkl.group_relkl_bwd(pairs, f["lse_t"], f["lse_s"], f["diag_delta"], gl,
+                                       reserve=f["reserve"], causal=True, rope=[tabs, tabs])
         loss = torch.stack((f["loss"], f["member_loss"][0], f["member_loss"][1]))
         return loss, torch.cat((dq, dk), dim=1)
 

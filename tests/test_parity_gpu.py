@@ -11,8 +11,8 @@ import torch
 
 import oracle
 from attention_relation_distillation_amd import relkl, workloads
-from tests._gpu import (GRAD_RL2, LOSS_RTOL, assert_parity, banner, device, fp32_floor,
-                        gpu_fwd_bwd, np64, oracle_fwd_bwd, rel_l2)
+from tests._gpu import (GRAD_RL2, LOSS_RTOL, ROW_KL_RL2, assert_parity, banner, device,
+                        gpu_fwd_bwd, np64, oracle_fwd_bwd, rel_l2, state, tiny_n_floor)
 
 pytestmark = pytest.mark.gpu
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -27,7 +27,8 @@ def test_tiny_workload_full():
     assert_parity(f, dx, fo, dxo, torch.float32, "tiny")
     err = np.abs(np64(f["row_kl"]) - fo["row_kl"])
     print(f"[parity] tiny row_kl max abs err {err.max():.3e}", flush=True)
-    np.testing.assert_allclose(np64(f["row_kl"]), fo["row_kl"], rtol=1e-4, atol=3e-7)
+    np.testing.assert_allclose(np64(f["row_kl"]), fo["row_kl"], rtol=1e-4, atol=1e-7)
+    assert float(f["row_kl"][0, 0, 0].item()) == 0.0  # causal row 0: one entry, KL exactly 0
 
 
 @pytest.mark.parametrize("name,n,hq,hkv,b", [
@@ -57,6 +58,8 @@ def test_workload_recipes_reduced(name, n, hq, hkv, b):
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("n", [1, 2, 3, 5, 63, 64, 65, 255, 256, 257, 513])
 def test_edge_sizes(n, causal, d, dtype):
+    """Ragged and tiny sizes.  N >= 64 is held to the plain gates; below that a row has
+    only a few entries and the named fp32 floor of tiny_n_floor applies."""
     banner(f"edge N={n} d={d} causal={causal} {dtype}")
     g = torch.Generator().manual_seed(n * 7 + d)
     x = torch.randn((1, 2, n, d), generator=g)
@@ -65,9 +68,30 @@ def test_edge_sizes(n, causal, d, dtype):
     f, dx = gpu_fwd_bwd(x_t, x_s, causal, dx_dtype=torch.float32)
     fo, dxo = oracle_fwd_bwd(x_t, x_s, causal)
     scale = oracle.default_scale(d)
-    assert_parity(f, dx, fo, dxo, dtype, f"edge N={n}", x_s=x_s, scale=scale)
-    if n == 1:
-        assert np.all(fo["row_kl"] == 0.0)
+    floor = tiny_n_floor(fo, x_s, scale) if n < 64 else None
+    assert_parity(f, dx, fo, dxo, dtype, f"edge N={n}", floor=floor)
+    if causal:  # row 0 keeps one entry: R_t = R_s = 1, KL exactly 0
+        assert torch.all(f["row_kl"][..., 0] == 0)
+        assert torch.all(f["diag_delta"][..., 0] == 0)
+    if n == 1:  # one entry per row: loss and gradient exactly 0
+        assert np.all(fo["row_kl"] == 0.0) and not np.any(dxo)
+        assert float(f["loss"].item()) == 0.0
+        assert torch.all(f["row_kl"] == 0)
+        assert torch.all(dx == 0)
+
+
+@pytest.mark.parametrize("n", [200, 333, 400, 777])
+def test_vv_small_kl_loss(n):
+    """The V/V relation of the GQA recipe (student V = V + 0.05 noise), whose row KL is
+    about 1e-4 of its LSE, at short lengths where the diagonal carries nearly all of each
+    row's mass: loss and row KL at the plain bf16 gate, five draws each."""
+    for seed in range(5):
+        banner(f"V/V N={n} seed={seed}")
+        (rel,) = workloads.make_inputs("gqa_16k", seed=seed, N=n, Hq=2, Hkv=2,
+                                       relations=("vv",))
+        f, dx = gpu_fwd_bwd(rel.x_t, rel.x_s, True, dx_dtype=torch.float32)
+        fo, dxo = oracle_fwd_bwd(rel.x_t, rel.x_s, True)
+        assert_parity(f, dx, fo, dxo, torch.bfloat16, f"vv N={n} seed={seed}")
 
 
 def test_golden_closed_form():
@@ -88,13 +112,20 @@ def test_golden_closed_form():
                                 scale=case["scale"], g=case["g"])
             np.testing.assert_allclose(np64(f["lse_t"])[0, 0], case["lse_t"], rtol=2e-6, atol=2e-6)
             np.testing.assert_allclose(np64(f["lse_s"])[0, 0], case["lse_s"], rtol=2e-6, atol=2e-6)
-            # every row of these inputs is alike, so per-row fp32 errors add up instead of
-            # averaging out: gate = dtype gate + the fp32 floor of the row formula
-            ref = {k: np.array(case[k]) for k in ("lse_t", "lse_s", "row_kl")}
-            loss_floor, _ = fp32_floor(ref, x_s, case["scale"])
             err = abs(float(f["loss"].item()) - case["loss"])
-            print(f"[parity] golden {case['name']} loss abs err {err:.3e} floor {loss_floor:.3e}")
-            assert err <= LOSS_RTOL[dtype] * case["loss"] + loss_floor
+            # Every row of these structured inputs is alike, so a row's fp32 rounding is
+            # repeated by every row instead of averaging out; where the diagonal carries a
+            # small part of the row (N > d leaves zero rows; non-causal rows of 200
+            # entries) the row KL is a difference of terms of size |LSE|.  For fp32 inputs
+            # the gate therefore adds the per-row fp32 floor of tiny_n_floor (named case:
+            # the closed-form goldens); bf16's gate is far above it.
+            ref = {k: np.array(case[k]) for k in ("lse_t", "lse_s", "row_kl")}
+            floor = tiny_n_floor(ref, x_s, case["scale"])[0] if dtype == torch.float32 else 0.0
+            print(f"[parity] golden {case['name']} loss rel err {err / max(case['loss'], 1e-30):.3e}"
+                  f" floor {floor / max(case['loss'], 1e-30):.3e}")
+            assert err <= LOSS_RTOL[dtype] * case["loss"] + floor
+            np.testing.assert_allclose(np64(f["row_kl"])[0, 0], case["row_kl"],
+                                       rtol=ROW_KL_RL2, atol=floor / n)
             rows = case["dx_rows"]
             got = np64(dx)[0, 0][rows]
             ref = np.array(case["dx"])
@@ -111,6 +142,7 @@ def test_student_equals_teacher_is_exactly_zero(causal, dtype):
     assert float(f["loss"].item()) == 0.0
     assert torch.all(f["row_kl"] == 0)
     assert torch.equal(f["lse_t"], f["lse_s"])
+    assert torch.all(f["diag_delta"] == 0)
     assert torch.all(dx == 0)
 
 
@@ -143,7 +175,7 @@ def test_head_map_and_untouched_heads():
     hm = [0, 4]
     f = relkl.relkl_fwd(rep_t, rep_s, causal=True, head_map=hm, want_row_kl=True)
     sentinel = torch.full(rep_s.shape, 7.0, dtype=torch.float32, device=dev)
-    relkl.relkl_bwd(rep_t, rep_s, f["reserve"], torch.ones((), device=dev),
+    relkl.relkl_bwd(rep_t, rep_s, *state(f), torch.ones((), device=dev),
                     causal=True, head_map=hm, dx=sentinel)
     torch.cuda.synchronize()
     base_t, base_s = k.to(torch.bfloat16), k_s.to(torch.bfloat16)
@@ -167,9 +199,8 @@ def test_strided_inputs_match_contiguous():
     f1 = relkl.relkl_fwd(v_t, v_s, causal=True)
     f2 = relkl.relkl_fwd(v_t.contiguous(), v_s.contiguous(), causal=True)
     gl = torch.ones((), device=dev)
-    d1 = relkl.relkl_bwd(v_t, v_s, f1["reserve"], gl, causal=True)
-    d2 = relkl.relkl_bwd(v_t.contiguous(), v_s.contiguous(), f2["reserve"], gl,
-                         causal=True)
+    d1 = relkl.relkl_bwd(v_t, v_s, *state(f1), gl, causal=True)
+    d2 = relkl.relkl_bwd(v_t.contiguous(), v_s.contiguous(), *state(f2), gl, causal=True)
     torch.cuda.synchronize()
     assert torch.equal(f1["loss"], f2["loss"])
     assert torch.equal(d1.contiguous(), d2)
@@ -186,6 +217,33 @@ def test_autograd_function():
     fo, dxo = oracle_fwd_bwd(x_t.cpu(), x_s.detach().cpu(), True, g=2.5)
     assert float(loss.item()) == pytest.approx(fo["loss"], rel=1e-5)
     assert rel_l2(np64(x_s.grad), dxo) <= GRAD_RL2[torch.float32]
+    # the pages' mean over rows: loss / N, gradient scaled alike
+    x_s.grad = None
+    mean = relkl.relation_kl(x_t, x_s, causal=True, reduction="mean_rows")
+    (2.5 * mean).backward()
+    assert float(mean.item()) == pytest.approx(fo["loss"] / 200, rel=1e-5)
+    assert rel_l2(np64(x_s.grad), dxo / 200) <= GRAD_RL2[torch.float32]
+
+
+def test_side_stream_matches_default_stream():
+    """Forward and backward issued on a side stream (outputs and workspaces allocated on
+    it) give bitwise the results of the default stream."""
+    banner("side stream")
+    dev = device()
+    (rel,) = workloads.make_inputs("llama2_4k", N=600, Hq=2, Hkv=2, relations=("kk",))
+    xt, xs = rel.x_t.to(dev), rel.x_s.to(dev)
+    gl = torch.ones((), device=dev)
+    f0 = relkl.relkl_fwd(xt, xs, causal=True)
+    d0 = relkl.relkl_bwd(xt, xs, *state(f0), gl, causal=True)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    f1 = relkl.relkl_fwd(xt, xs, causal=True, stream=side)
+    d1 = relkl.relkl_bwd(xt, xs, *state(f1), gl, causal=True, stream=side)
+    side.synchronize()
+    assert torch.equal(f0["loss"], f1["loss"]) and torch.equal(f0["lse_t"], f1["lse_t"])
+    assert torch.equal(f0["diag_delta"], f1["diag_delta"])
+    assert torch.equal(d0, d1)
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
@@ -208,7 +266,12 @@ def test_growing_row_maximum(causal, d, dtype):
     x_t, x_s = x_t.to(dtype), x_s.to(dtype)
     f, dx = gpu_fwd_bwd(x_t, x_s, causal)
     fo, dxo = oracle_fwd_bwd(x_t, x_s, causal)
-    assert_parity(f, dx, fo, dxo, dtype, "growing", x_s=x_s, scale=oracle.default_scale(d))
+    # These rows are dominated by entries far above their own diagonal (scores up to
+    # alpha_max^2 ~ 1600, LSE up to ~140 nats), so the row KL (~3e-3) is formed from
+    # quantities of size LSE whose fp32 ulp is ~1e-5: a per-row precision of about
+    # 2^-23 LSE / KL ~ 5e-3 at worst; the row-KL gate here is 1e-3 (the loss and gradient
+    # keep the plain gates).
+    assert_parity(f, dx, fo, dxo, dtype, "growing", row_kl_rl2=1e-3)
 
 
 def test_relations_in_one_call_through_a_fused_qkv_buffer():
@@ -229,13 +292,13 @@ def test_relations_in_one_call_through_a_fused_qkv_buffer():
     assert v_t.stride() == (H * d, d, 3 * H * d, 1)
     gl = torch.ones((), device=dev)
     f = relkl.relkl_fwd(v_t, v_s, causal=True)
-    dx = relkl.relkl_bwd(v_t, v_s, f["reserve"], gl, causal=True, dx_dtype=torch.float32)
+    dx = relkl.relkl_bwd(v_t, v_s, *state(f), gl, causal=True, dx_dtype=torch.float32)
     torch.cuda.synchronize()
     total, parts = 0.0, []
     for k, r in enumerate(rels):
         xt, xs = r.x_t.to(dev), r.x_s.to(dev)
         fk = relkl.relkl_fwd(xt, xs, causal=True)
-        dk = relkl.relkl_bwd(xt, xs, fk["reserve"], gl, causal=True, dx_dtype=torch.float32)
+        dk = relkl.relkl_bwd(xt, xs, *state(fk), gl, causal=True, dx_dtype=torch.float32)
         torch.cuda.synchronize()
         total += float(fk["loss"].item())
         assert torch.equal(dx[k], dk[0]), k

@@ -3,10 +3,12 @@ with the float64 oracle (``oracle.rope``), on the workload recipes handed over b
 rotation: reduced sizes with ragged tails, edge sizes, head maps, the autograd function,
 and the full-size 4K and 32K shapes on sampled rows.
 
-The fused path rotates in fp32 and rounds the rotated rows to the input dtype, as a model
-that applies RoPE itself would; the oracle evaluates the rotation the same way (fp32 fused
-multiply-add, then the dtype's rounding) from the same bytes and tables, so both sides
-multiply the same operands and the gates are those of the plain path."""
+The fused path rounds the rotated rows to the input dtype, as a model that applies RoPE
+itself would; the oracle takes the exact rotation of the same bytes and tables rounded once
+to that dtype.  The kernel evaluates the rotation in fp32 first, so the two roundings can
+differ by one step of the dtype where the exact value lies within an fp32 rounding of a
+rounding boundary (rare; a loss effect of about 1e-7 relative), and the gates are those of
+the plain path."""
 
 import numpy as np
 import pytest
@@ -15,7 +17,8 @@ import torch
 import oracle
 from oracle import rope
 from attention_relation_distillation_amd import relkl, workloads
-from tests._gpu import (GRAD_RL2, LOSS_RTOL, assert_parity, banner, device, np64, rel_l2)
+from tests._gpu import (GRAD_RL2, LOSS_RTOL, assert_parity, banner, device, np64, rel_l2,
+                        state, tiny_n_floor)
 
 pytestmark = pytest.mark.gpu
 
@@ -34,8 +37,8 @@ def gpu_rope(x_t, x_s, tabs, causal, head_map=None, dx_dtype=None, g=1.0, dx=Non
     tg = [None if t is None else t.to(dev).contiguous() for t in tabs]
     f = relkl.rope_relkl_fwd(xt, xs, *tg, causal=causal, head_map=head_map, want_row_kl=True)
     gl = torch.tensor(g, dtype=torch.float32, device=dev)
-    out = relkl.rope_relkl_bwd(xs, f["reserve"], gl, *tg, causal=causal, head_map=head_map,
-                               dx_dtype=dx_dtype, dx=dx)
+    out = relkl.rope_relkl_bwd(xs, f["reserve"], *state(f), gl, *tg, causal=causal,
+                               head_map=head_map, dx_dtype=dx_dtype, dx=dx)
     torch.cuda.synchronize()
     return f, out
 
@@ -93,14 +96,15 @@ def test_rope_edge_sizes(n, causal, d, dtype):
     tabs = (*rand_tables(n, d, 1), *rand_tables(n, d, 2))
     f, dx = gpu_rope(x_t, x_s, tabs, causal, dx_dtype=torch.float32)
     fo, dxo = oracle_rope(x_t, x_s, tabs, causal)
-    assert_parity(f, dx, fo, dxo, dtype, f"rope edge N={n}", x_s=x_s,
-                  scale=oracle.default_scale(d))
+    floor = tiny_n_floor(fo, x_s, oracle.default_scale(d)) if n < 64 else None
+    assert_parity(f, dx, fo, dxo, dtype, f"rope edge N={n}", floor=floor)
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_rope_without_tables_is_plain_path(dtype):
-    """No tables on either side: the fused path computes the plain relation KL.  Identity
-    tables give bitwise the same results as no tables (x cos - y sin = x exactly)."""
+    """No tables on either side: the fused path runs the plain kernels on copies of the
+    inputs, bitwise the plain path.  Identity tables give bitwise the same results as no
+    tables (x cos - y sin = x exactly)."""
     banner(f"rope null tables {dtype}")
     g = torch.Generator().manual_seed(21)
     x = torch.randn((1, 2, 300, 128), generator=g)
@@ -112,11 +116,11 @@ def test_rope_without_tables_is_plain_path(dtype):
     assert torch.equal(f0["loss"], f1["loss"]) and torch.equal(d0, d1)
     dev = device()
     fp = relkl.relkl_fwd(x_t.to(dev), x_s.to(dev), causal=True)
-    dp = relkl.relkl_bwd(x_t.to(dev), x_s.to(dev), fp["reserve"], torch.ones((), device=dev),
+    dp = relkl.relkl_bwd(x_t.to(dev), x_s.to(dev), *state(fp), torch.ones((), device=dev),
                          causal=True, dx_dtype=torch.float32)
     torch.cuda.synchronize()
-    assert abs(float(f0["loss"].item()) - float(fp["loss"].item())) <= 1e-6 * float(fp["loss"].item())
-    assert rel_l2(np64(d0), np64(dp)) <= 1e-6
+    assert torch.equal(f0["loss"], fp["loss"]) and torch.equal(f0["lse_t"], fp["lse_t"])
+    assert torch.equal(d0, dp)
 
 
 def test_rope_head_map_and_untouched_heads():
