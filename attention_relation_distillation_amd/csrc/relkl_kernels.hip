@@ -1125,9 +1125,10 @@ void relkl_bwd_kernel(const BwdLaunch L) {
   //    step t-1) at its start and awaits it at its end;
   //  * two buffers (fp32, d = 128): tile t+1 goes into the buffer of tile t-1, whose last
   //    reads are the gradient MFMAs of M(2t); a barrier after M(2t) precedes the copy.
-  // The barrier ending step t publishes tile t+1 (and its fp16 image) to every wave.  A
-  // V(2t-1) that a wave runs at the start of step t (below) reads tile t-1's statistics
-  // before either copy reaches them.
+  // The barrier ending step t publishes tile t+1 (its fp16 image and statistics made by
+  // each wave after M(2t) from the chunks it copied) to every wave.  A V(2t-1) that a wave
+  // runs at the start of step t (below) reads tile t-1's statistics before either copy
+  // reaches them.
 
   // M(n): gradient of block n-1, scores of block n.  Every M runs the full pipeline: M(0)
   // contracts the initial zero W with the zero-filled gradient tile of the last buffer;
@@ -1211,11 +1212,18 @@ void relkl_bwd_kernel(const BwdLaunch L) {
       lds_barrier();
       if (t + 1 < ntiles) stage_tile(t + 1, buf(t + 1));
     }
+    if (kStages == 3) {
+      // tile t+1's copies, issued at the start of this step, have usually landed by now:
+      // its fp16 image and statistics are made here, beside the partner wave's work, rather
+      // than just before the barrier
+      wait_vmem();
+      if (t + 1 < ntiles) convert_tile(t + 1, buf(t + 1));
+    }
     v_phase(2 * t);
     m_phase(2 * t + 1);
     if (!lag) v_phase(2 * t + 1);
     wait_vmem();
-    if (t + 1 < ntiles) convert_tile(t + 1, buf(t + 1));
+    if (kStages == 2 && t + 1 < ntiles) convert_tile(t + 1, buf(t + 1));
     lds_barrier();
   }
   if (lag && ntiles > 0) v_phase(NB - 1);

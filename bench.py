@@ -92,12 +92,43 @@ def alg_flops(B, H, N, d, causal):
     return B * H * 2 * per, B * H * 4 * per
 
 
-def cpu_baseline(rel, causal, target_s=12.0):
-    """Time the float64 oracle on a bounded sample: forward and gradient of the last `rows`
-    rows of one unit (batch 0, head 0).  For a causal relation these rows are
-    self-contained (their column terms only involve rows j >= i of the same sample).  A
-    512-row probe sizes the sample to about `target_s` seconds of host time; the oracle's
-    cost is proportional to the number of rows it evaluates."""
+_CPU_UNIT = {}
+
+
+def _cpu_init(x_t, x_s, scale, causal):
+    """Pool initializer of cpu_baseline: the unit's inputs, handed to each worker once."""
+    _CPU_UNIT.update(x_t=x_t, x_s=x_s, scale=scale, causal=causal)
+
+
+def _oracle_fwd_rows(rows):
+    """Pool task of cpu_baseline: the oracle's forward of some rows of the unit."""
+    import oracle
+    u = _CPU_UNIT
+    lt, ls, kl = oracle.forward_unit(u["x_t"], u["x_s"], u["scale"], u["causal"], chunk=256,
+                                     rows=rows)
+    return rows, lt, ls
+
+
+def _oracle_bwd_rows(args):
+    """Pool task of cpu_baseline: the oracle's gradient of some rows of the unit."""
+    import oracle
+    lt, ls, rows = args
+    u = _CPU_UNIT
+    oracle.backward_unit(u["x_t"], u["x_s"], u["scale"], u["causal"], 1.0, lse_t=lt, lse_s=ls,
+                         rows=rows, chunk=256)
+    return rows.size
+
+
+def cpu_baseline(rel, causal, bwd_rows=1024):
+    """Time the float64 oracle, as it stands, on the host cores: the forward of one whole
+    unit (batch 0, head 0; every row, so the causal mix of row lengths is the real one) and
+    the gradient of a uniform sample of `bwd_rows` of its rows (evenly spaced over the
+    unit, given the LSE vectors of that forward).  Rows are spread over a process pool
+    (fresh interpreters: nothing of this process's GPU state is inherited) sized by the
+    cores available to this process (at most 16, the box's share of one GPU) and by host
+    RAM, with one BLAS thread per worker.  Returns (unit seconds estimate, details)."""
+    import multiprocessing as mp
+
     import numpy as np
     import oracle
 
@@ -105,33 +136,47 @@ def cpu_baseline(rel, causal, target_s=12.0):
         avail = len(os.sched_getaffinity(0))
     except AttributeError:
         avail = os.cpu_count()
-    try:  # threads the oracle's BLAS calls actually run on
-        from threadpoolctl import threadpool_info
-        blas = [p["num_threads"] for p in threadpool_info() if p.get("user_api") == "blas"]
-        cores = min(max(blas), avail) if blas else 1
-    except ImportError:
-        cores = avail
-    x_t = rel.x_t[0, 0].double().numpy()
-    x_s = rel.x_s[0, 0].double().numpy()
+    host = host_info(avail)
+    mem_gb = host.get("ram_gb", 16.0)
+    x_t = np.ascontiguousarray(rel.x_t[0, 0].double().numpy())
+    x_s = np.ascontiguousarray(rel.x_s[0, 0].double().numpy())
     n = x_t.shape[0]
-    s = oracle.default_scale(x_t.shape[1])
-
-    def run(rows):
-        sel = np.arange(n - rows, n)
-        t0 = time.perf_counter()
-        lt, ls, kl = oracle.forward_unit(x_t, x_s, s, causal, chunk=1024, rows=sel)
-        full_lt = np.full(n, np.nan)
-        full_ls = np.full(n, np.nan)
-        full_lt[sel], full_ls[sel] = lt, ls
-        oracle.backward_unit(x_t, x_s, s, causal, 1.0, lse_t=full_lt, lse_s=full_ls, rows=sel,
-                             chunk=1024)
-        return time.perf_counter() - t0
-
-    probe = min(512, n)
-    t_probe = run(probe)
-    rows = int(min(n, max(probe, round(probe * target_s / max(t_probe, 1e-3) / 512) * 512)))
-    dt = run(rows)
-    return dt, rows, cores, host_info(avail)
+    scale = oracle.default_scale(x_t.shape[1])
+    # ~2 GB per worker at N = 32768 (a few 256 x N float64 blocks plus the inputs)
+    workers = int(max(1, min(avail, 16, mem_gb // 2)))
+    # forward: 256-row blocks dealt round-robin so that every task mixes short and long rows
+    blocks = [np.arange(r0, min(n, r0 + 256)) for r0 in range(0, n, 256)]
+    fwd_tasks = [np.concatenate(blocks[k::workers * 2])
+                 for k in range(min(len(blocks), workers * 2))]
+    sample = np.unique(np.linspace(0, n - 1, min(n, bwd_rows)).round().astype(np.int64))
+    env_keep = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS",
+                                               "MKL_NUM_THREADS")}
+    for k in env_keep:
+        os.environ[k] = "1"
+    try:
+        with mp.get_context("spawn").Pool(workers, initializer=_cpu_init,
+                                          initargs=(x_t, x_s, scale, causal)) as pool:
+            pool.map(_oracle_fwd_rows, [np.arange(4)] * workers)  # start-up, untimed
+            t0 = time.perf_counter()
+            parts = pool.map(_oracle_fwd_rows, fwd_tasks, chunksize=1)
+            t_fwd = time.perf_counter() - t0
+            lt, ls = np.empty(n), np.empty(n)
+            for rows, a, b_ in parts:
+                lt[rows], ls[rows] = a, b_
+            bwd_tasks = [(lt, ls, sample[k::workers]) for k in range(workers)]
+            t0 = time.perf_counter()
+            pool.map(_oracle_bwd_rows, bwd_tasks, chunksize=1)
+            t_bwd = time.perf_counter() - t0
+    finally:
+        for k, v in env_keep.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    unit_s = t_fwd + t_bwd * (n / sample.size)
+    return unit_s, {"workers": workers, "fwd_unit_s": round(t_fwd, 3),
+                    "bwd_sample_rows": int(sample.size), "bwd_sample_s": round(t_bwd, 3),
+                    "bwd_scale": round(n / sample.size, 3), "host": host}
 
 
 def host_info(avail):
@@ -520,21 +565,21 @@ def main():
 
     if not args.no_cpu_baseline:
         rel0 = rels[0]
-        dt, rows, cores, host = cpu_baseline(rel0, causal, args.cpu_seconds)
-        # the oracle's cost is proportional to rows x N (it evaluates full rows), so one
-        # unit costs N / rows samples and the step has sum over relations of B * H units
+        unit_s, det = cpu_baseline(rel0, causal)
         units = sum(wl.B * r.x_t.shape[1] for r in rels)
-        est_step_s = dt * (wl.N / rows) * units
+        est_step_s = unit_s * units
         out["cpu_baseline"] = {
-            "value": round(tokens / est_step_s, 3), "unit": "tokens/s", "cores": cores,
-            "kind": "oracle",
-            "sample": (f"float64 oracle forward+gradient of the last {rows} rows of one "
-                       f"{rel0.name} head at N={wl.N} ({dt:.2f}s), extrapolated (labelled as "
-                       f"such) x{wl.N / rows:.2f} rows x {units} units; host "
-                       f"{platform.processor() or platform.machine()}"),
-            "sample_seconds": round(dt, 3),
+            "value": round(tokens / est_step_s, 3), "unit": "tokens/s",
+            "cores": det["workers"], "kind": "oracle",
+            "sample": (f"float64 oracle on {det['workers']} host processes: forward of one whole "
+                       f"{rel0.name} unit at N={wl.N} ({det['fwd_unit_s']:.2f}s) plus the "
+                       f"gradient of {det['bwd_sample_rows']} evenly spaced rows of it "
+                       f"({det['bwd_sample_s']:.2f}s, x{det['bwd_scale']:.1f} to the unit); "
+                       f"extrapolated (labelled as such) x{units} units of a step"),
+            "unit_seconds": round(unit_s, 3),
             "extrapolated": True,
-            "host": host,
+            "extrapolation_factor": units,
+            "host": det["host"],
         }
     print(json.dumps(out), flush=True)
 
