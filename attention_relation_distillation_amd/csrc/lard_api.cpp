@@ -566,6 +566,23 @@ lard_status lard_relkl_bwd(const lard_relkl_desc* desc, const void* x_teacher,
                        &dx_student, static_cast<float*>(workspace), stream);
 }
 
+lard_status lard_relkl_fwd_noalloc(const lard_relkl_desc* desc, const void* x_teacher,
+                                   const void* x_student, float* lse_teacher,
+                                   float* lse_student, float* diag_delta, float* row_kl,
+                                   float* loss, void* stream) {
+  lard_status s = check_desc(desc);
+  if (s != LARD_OK) return s;
+  if ((s = check_inputs(x_teacher, x_student)) != LARD_OK) return s;
+  if ((s = check_fwd_outputs(lse_teacher, lse_student, diag_delta, row_kl)) != LARD_OK) return s;
+  if (!loss || !aligned(loss, 4)) return LARD_ERR_INVALID_ARGUMENT;
+  if (fwd_partials(desc) > kNoallocMaxPartials) return LARD_ERR_WORKSPACE_TOO_SMALL;
+  void* scratch = nullptr;
+  if (scratch_address(&scratch) != 0) return LARD_ERR_HIP;
+  return run_group_fwd(1, &desc, &x_teacher, &x_student, &lse_teacher, &lse_student,
+                       &diag_delta, &row_kl, nullptr, nullptr, false, loss, nullptr, nullptr,
+                       static_cast<double*>(scratch), stream);
+}
+
 size_t lard_relkl_rope_reserve_size(const lard_relkl_desc* desc, lard_status* status) {
   const lard_status s = check_desc(desc);
   if (status) *status = s;

@@ -160,4 +160,10 @@ int launch_splitk_reduce(const ReduceLaunch& a, bool out_f32, void* stream);
 // f16_images: write bf16 rows as their fp16 images (cross relation), else in the input dtype.
 int launch_rope_prep(const PrepLaunch& a, bool in_bf16, int d, void* stream, bool f16_images);
 
+// Capacity (fp64 loss partials, one per forward workgroup) of the library-owned scratch of
+// the allocation-free forward, and its device address on the current device (a hipError_t
+// value, 0 on success; looked up once per device).
+constexpr int64_t kNoallocMaxPartials = LARD_NOALLOC_MAX_PARTIALS;
+int scratch_address(void** out);
+
 }  // namespace lard

@@ -21,7 +21,8 @@ from typing import Optional, Sequence
 
 import torch
 
-__all__ = ["LardError", "library_path", "load_library", "relkl_fwd", "relkl_bwd",
+__all__ = ["LardError", "library_path", "load_library", "relkl_fwd", "relkl_fwd_noalloc",
+           "relkl_bwd",
            "relation_kl", "workspace_size", "rope_reserve_size",
            "rope_relkl_fwd", "rope_relkl_bwd", "rope_relation_kl", "cross_reserve_size",
            "cross_relkl_fwd", "cross_relkl_bwd", "cross_relation_kl", "group_reserve_size",
@@ -117,6 +118,8 @@ def load_library():
                                               ctypes.POINTER(ctypes.c_int)]
     lib.lard_relkl_fwd.restype = ctypes.c_int
     lib.lard_relkl_fwd.argtypes = [ctypes.POINTER(_Desc), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.lard_relkl_fwd_noalloc.restype = ctypes.c_int
+    lib.lard_relkl_fwd_noalloc.argtypes = [ctypes.POINTER(_Desc), vp, vp, vp, vp, vp, vp, vp, vp]
     lib.lard_relkl_bwd.restype = ctypes.c_int
     lib.lard_relkl_bwd.argtypes = [ctypes.POINTER(_Desc), vp, vp, vp, vp, vp, vp,
                                    ctypes.POINTER(_GradDesc), vp, vp, sz, vp]
@@ -273,6 +276,33 @@ def relkl_fwd(x_t: torch.Tensor, x_s: torch.Tensor, *, causal: bool = True,
                                   _stream_handle(dev, stream)))
     del keep
     return {"loss": loss, "lse_t": lse_t, "lse_s": lse_s, "diag_delta": diag, "row_kl": row_kl}
+
+
+def relkl_fwd_noalloc(x_t: torch.Tensor, x_s: torch.Tensor, lse_t: torch.Tensor,
+                      lse_s: torch.Tensor, diag_delta: Optional[torch.Tensor],
+                      row_kl: Optional[torch.Tensor], loss: torch.Tensor, *,
+                      causal: bool = True, scale: Optional[float] = None,
+                      head_map: Optional[Sequence[int]] = None, stream=None):
+    """The forward into caller-given outputs (fp32 [B, H, N] row vectors, a 0-d fp32 loss)
+    with no allocation by the library or by this binding: the loss partials live in the
+    library's per-GPU scratch.  Calls that overlap on one GPU race on that scratch."""
+    lib = load_library()
+    desc, keep = _make_desc(x_t, x_s, causal, scale, head_map)
+    _require_gpu(x_t)
+    dev = x_t.device
+    shape = (desc.B, desc.H, desc.N)
+    for name, t in (("lse_t", lse_t), ("lse_s", lse_s), ("diag_delta", diag_delta),
+                    ("row_kl", row_kl)):
+        if t is not None:
+            _check_state(name, t, shape, dev)
+    if loss.dtype != torch.float32 or loss.numel() != 1 or loss.device != dev:
+        raise LardError(1, "loss must be a one-element fp32 tensor on the inputs' device")
+    _check(lib.lard_relkl_fwd_noalloc(ctypes.byref(desc), x_t.data_ptr(), x_s.data_ptr(),
+                                      lse_t.data_ptr(), lse_s.data_ptr(),
+                                      diag_delta.data_ptr() if diag_delta is not None else None,
+                                      row_kl.data_ptr() if row_kl is not None else None,
+                                      loss.data_ptr(), _stream_handle(dev, stream)))
+    del keep
 
 
 def relkl_bwd(x_t: torch.Tensor, x_s: torch.Tensor, lse_t: torch.Tensor, lse_s: torch.Tensor,

@@ -348,6 +348,24 @@ lard_status lard_relkl_group_bwd(int n, const lard_relkl_member* members, int wi
                                  void* const* dx_student, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
+/*
+ * Allocation-free forward, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): lard_relkl_fwd
+ * without the workspace argument.  The forward's per-workgroup loss partials go to a
+ * device array the library holds per GPU (LARD_NOALLOC_MAX_PARTIALS fp64 values, 512 KiB,
+ * kept until the process ends); the address is looked up on the first call on each device.
+ * The caller still passes inputs and outputs, as for lard_relkl_fwd.  The call allocates
+ * nothing.  A descriptor needing more than LARD_NOALLOC_MAX_PARTIALS partials
+ * (B * H * ceil(N / 128) of them) returns LARD_ERR_WORKSPACE_TOO_SMALL.  Every call on one
+ * GPU shares the array: calls that overlap on a GPU (e.g. on two streams at once) race.
+ * Results are bitwise those of lard_relkl_fwd.
+ */
+#define LARD_NOALLOC_MAX_PARTIALS 65536
+lard_status lard_relkl_fwd_noalloc(const lard_relkl_desc* desc, const void* x_teacher,
+                                   const void* x_student, float* lse_teacher,
+                                   float* lse_student, float* diag_delta, float* row_kl,
+                                   float* loss, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* lard_status_string(lard_status status);
 

@@ -171,6 +171,22 @@ def test_pointer_and_workspace_validation(lib):
     assert bwd(lib, d32, g=g) == UNSUPPORTED
 
 
+def test_noalloc_forward_validation(lib):
+    def call(desc, lt=FAKE, loss=FAKE):
+        return lib.lard_relkl_fwd_noalloc(ctypes.byref(desc), FAKE, FAKE, lt, FAKE, FAKE, None,
+                                          loss, None)
+    assert call(good_desc(N=0)) == INVALID
+    assert call(good_desc(), lt=None) == INVALID
+    assert call(good_desc(), loss=None) == INVALID
+    # 3 x 86 units x 256 row tiles of 128 = 66048 loss partials > LARD_NOALLOC_MAX_PARTIALS
+    big = good_desc(B=3, H_in=86, H=86, N=32768, d=64, t_stride_n=64, s_stride_n=64,
+                    t_stride_h=32768 * 64, s_stride_h=32768 * 64, t_stride_b=86 * 32768 * 64,
+                    s_stride_b=86 * 32768 * 64)
+    assert call(big) == WS_SMALL
+    # a valid request reaches the device side (no GPU here, or the injected fault)
+    assert call(good_desc()) == HIP
+
+
 def test_fault_injection_maps_to_hip_error(lib, monkeypatch):
     """A failed launch is reported as LARD_ERR_HIP (the launch wrapper is told to fail
     before it calls HIP), and the Python layer turns it into an exception."""
