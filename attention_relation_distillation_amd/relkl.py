@@ -99,7 +99,10 @@ _LIB = None
 
 
 def library_path() -> str:
-    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblard.so")
+    """The in-tree liblard.so (LARD_LIBRARY overrides it, e.g. for a host sanitizer build of
+    the C-ABI layer in the CPU tests)."""
+    return os.environ.get("LARD_LIBRARY") or os.path.join(
+        os.path.dirname(os.path.abspath(__file__)), "liblard.so")
 
 
 def load_library():
