@@ -35,6 +35,9 @@ lard_status check_strides(int dtype, int64_t sb, int64_t sh, int64_t sn) {
   return LARD_OK;
 }
 
+// Row strides (elements) whose byte size stays below 2^24.
+bool row_stride_ok(int dtype, int64_t sn) { return sn * elem_size(dtype) < (int64_t(1) << 24); }
+
 lard_status check_desc(const lard_relkl_desc* d) {
   if (!d) return LARD_ERR_INVALID_ARGUMENT;
   if (d->dtype != LARD_FP32 && d->dtype != LARD_BF16) return LARD_ERR_INVALID_ARGUMENT;
@@ -50,6 +53,9 @@ lard_status check_desc(const lard_relkl_desc* d) {
   if (s != LARD_OK) return s;
   // rows must not overlap inside one head (stride over n at least one row of d)
   if (d->N > 1 && (d->t_stride_n < d->d || d->s_stride_n < d->d)) return LARD_ERR_INVALID_ARGUMENT;
+  // the backward addresses the rows of a key tile as 24-bit offsets from the tile's first row
+  if (d->N > 1 && (!row_stride_ok(d->dtype, d->t_stride_n) || !row_stride_ok(d->dtype, d->s_stride_n)))
+    return LARD_ERR_UNSUPPORTED;
   if (d->head_map == nullptr) {
     if (d->H != d->H_in) return LARD_ERR_INVALID_ARGUMENT;
   } else {
@@ -72,7 +78,8 @@ lard_status check_desc(const lard_relkl_desc* d) {
 }
 
 int row_tiles_of(const lard_relkl_desc* d) { return (d->N + kBR - 1) / kBR; }
-int bwd_row_tiles_of(const lard_relkl_desc* d) { return (d->N + kBRB - 1) / kBRB; }
+int bwd_rows_of(const lard_relkl_desc* d) { return bwd_rows(d->dtype == LARD_FP32); }
+int bwd_row_tiles_of(const lard_relkl_desc* d) { return (d->N + bwd_rows_of(d) - 1) / bwd_rows_of(d); }
 int key_tiles_of(const lard_relkl_desc* d) { return (d->N + kBC - 1) / kBC; }
 int64_t units_of(const lard_relkl_desc* d) { return (int64_t)d->B * d->H; }
 
@@ -109,10 +116,10 @@ size_t fwd_workspace(int n, const lard_relkl_desc* const* d) {
   return round256((size_t)p * sizeof(double));
 }
 
-// Backward workspace: fp32 split-K partials [splits][units][row_tiles * kBRB][d] per member
+// Backward workspace: fp32 split-K partials [splits][units][row_tiles * rows][d] per member
 // when the key range is split, else nothing.
 size_t bwd_partial_floats(const lard_relkl_desc* d) {
-  return (size_t)units_of(d) * bwd_row_tiles_of(d) * kBRB * d->d;
+  return (size_t)units_of(d) * bwd_row_tiles_of(d) * bwd_rows_of(d) * d->d;
 }
 
 size_t bwd_workspace(int n, const lard_relkl_desc* const* d) {
@@ -362,7 +369,7 @@ lard_status run_bwd(const BwdLaunch& L, const lard_relkl_desc* const* d, bool ou
       r.dx = a.dx;
       r.g_sb = a.g_sb; r.g_sh = a.g_sh; r.g_sn = a.g_sn;
       r.B = a.B; r.H = a.H; r.N = a.N; r.d = d[k]->d;
-      r.rows_pad = a.row_tiles * kBRB;
+      r.rows_pad = a.row_tiles * bwd_rows_of(d[k]);
       r.splits = a.splits;
       r.map_off = a.map_off;
     }

@@ -14,9 +14,12 @@ constexpr int kWave = 64;
 constexpr int kWaves = 4;                 // waves per workgroup (two workgroups per CU)
 constexpr int kThreads = kWave * kWaves;  // 256
 constexpr int kBR = kWaves * 32;          // forward rows per workgroup: 32 per wave
-constexpr int kBWaves = 8;                // backward waves per workgroup (two groups of 4)
-constexpr int kBRB = kBWaves * 32;        // backward rows per workgroup
 constexpr int kBC = 64;                   // rows of one key tile staged in LDS
+// Backward workgroup: 8 waves (two per SIMD, 256 rows) for 2-byte operands; 4 waves (one
+// per SIMD, 128 rows) for fp32, whose operands take twice the registers: one wave per SIMD
+// may use 512 (vector and accumulator registers together) instead of 256.
+constexpr int bwd_waves(bool f32) { return f32 ? 4 : 8; }
+constexpr int bwd_rows(bool f32) { return 32 * bwd_waves(f32); }
 
 inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
@@ -70,7 +73,7 @@ struct BwdArgs {
   int64_t s_sb, s_sh, s_sn;
   int64_t g_sb, g_sh, g_sn;  // gradient strides (elements)
   int32_t B, H, N;
-  int32_t row_tiles;   // ceil(N / kBRB)
+  int32_t row_tiles;   // ceil(N / bwd_rows)
   int32_t key_tiles;   // ceil(N / kBC)
   int32_t splits;      // split-K count over key tiles
   float scale;
@@ -85,7 +88,7 @@ struct BwdArgs {
   const float* rope_sin;  // the gradient is rotated back before it is written
   int32_t x_dense;        // x_* / y_* are dense [unit][N][d] copies (else x_* in place)
   void* dx;            // final gradient (splits == 1)
-  float* partial;      // [splits][B*H][row_tiles*kBRB][d] (splits > 1)
+  float* partial;      // [splits][B*H][row_tiles*bwd_rows][d] (splits > 1)
   int32_t map_off;
 };
 
@@ -110,7 +113,7 @@ struct ReduceArgs {
   void* dx;
   int64_t g_sb, g_sh, g_sn;
   int32_t B, H, N, d;
-  int32_t rows_pad;    // row_tiles * kBRB
+  int32_t rows_pad;    // row_tiles * bwd_rows
   int32_t splits;
   int32_t map_off;
 };

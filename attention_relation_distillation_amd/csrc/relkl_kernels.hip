@@ -192,6 +192,12 @@ __device__ __forceinline__ void lds_copy16_s(uint32_t voff, const void* sbase, u
                "{m0}"(lds_base) : "memory");
 }
 
+// LDS copy of 4 bytes per lane from a wave-uniform base plus a per-lane byte offset.
+__device__ __forceinline__ void lds_copy4_s(uint32_t voff, const void* sbase, uint32_t lds_base) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase),
+               "{m0}"(lds_base) : "memory");
+}
+
 // LDS copy of 4 bytes per lane (lane l writes lds_base + 4 l), as lds_copy16.
 __device__ __forceinline__ void lds_copy4(const void* g, uint32_t lds_base) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds_base) : "memory");
@@ -929,8 +935,10 @@ __device__ __forceinline__ void m_pipeline(const char* gtile, int jbg, const cha
   }(std::make_integer_sequence<int, NF>{});
 }
 
-// Backward work decomposition: a workgroup of 8 waves (two per SIMD) owns kBRB = 256 rows,
-// 32 per wave, and sweeps the whole key range in key tiles of 64 rows (two 32-key blocks).
+// Backward work decomposition: a workgroup of 8 waves (two per SIMD) owns 256 rows, 32 per
+// wave, and sweeps the whole key range in key tiles of 64 rows (two 32-key blocks).  fp32
+// operands take twice the registers: there a workgroup is 4 waves (one per SIMD, which may
+// then hold 512 registers) owning 128 rows, and nothing runs beside a wave's phases.
 // MODE 0 is the relation gradient (own rows and staged rows are the same matrix: row and
 // column terms).  The cross relation softmax(A B^T) takes two passes: MODE 1 owns rows of
 // A and stages rows of B (row terms only: dA = scale dZ B_s, keys j <= i when causal);
@@ -947,7 +955,10 @@ __device__ __forceinline__ void m_pipeline(const char* gtile, int jbg, const cha
 // carried as fp16: each wave converts the 16-byte chunks it copied itself, after its own
 // copies have landed and before the barrier that publishes the tile.
 template <class Op, int D, bool CAUSAL, bool OUT_F32, int MODE>
-__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(bwd_waves(Op::kES == 4) * kWave,
+                                                      bwd_waves(Op::kES == 4) * kWave),
+                          amdgpu_waves_per_eu(bwd_waves(Op::kES == 4) / 4,
+                                              bwd_waves(Op::kES == 4) / 4)))
 void relkl_bwd_kernel(const BwdLaunch L) {
   using elem_t = typename Op::elem_t;
   using frag_t = typename Op::frag_t;
@@ -960,8 +971,10 @@ void relkl_bwd_kernel(const BwdLaunch L) {
   constexpr int kGradOff = Op::kConvert ? 2 * G::kTileBytes : G::kTileBytes;
   constexpr int kStatsOff = (Op::kConvert ? 3 : 2) * G::kTileBytes;
   constexpr int kStage = kStatsOff + kStats;
-  constexpr int kDma = kBC * G::kCPR / (kWave * kBWaves);  // DMA instructions per wave per tile
-  static_assert(kBC * G::kCPR % (kWave * kBWaves) == 0, "tile must split evenly over 8 waves");
+  constexpr int kW = bwd_waves(Op::kES == 4);  // waves of the workgroup
+  constexpr int kRowsWG = 32 * kW;               // rows it owns
+  constexpr int kDma = kBC * G::kCPR / (kWave * kW);  // DMA instructions per wave per tile
+  static_assert(kBC * G::kCPR % (kWave * kW) == 0, "tile must split evenly over the waves");
   static_assert(MODE == 0 || !Op::kConvert, "the cross relation reads fp16 images");
 
   // Stage buffers: three when they fit in the LDS, else two (fp32, d = 128).
@@ -1013,6 +1026,12 @@ void relkl_bwd_kernel(const BwdLaunch L) {
   const char* yt_c = reinterpret_cast<const char*>(yt);
   const char* ys_c = reinterpret_cast<const char*>(ys);
   const int64_t tsn_b = tsn * Op::kES, ssn_b = ssn * Op::kES;
+  // row strides in bytes are below 2^24 (checked on the host), so a clamped row (< 64)
+  // times the stride plus a chunk offset is a 24-bit multiply-add
+  const uint32_t tsn_u24 = (uint32_t)tsn_b, ssn_u24 = (uint32_t)ssn_b;
+  constexpr int kRPC = kWave / G::kCPR;  // tile rows per copy instruction
+  const int xr = lane / G::kCPR;
+  const int xc16 = ((lane % G::kCPR) ^ G::swz(xr)) << 4;
   // The forward's LSE vectors (nats); the kernel uses them as log2 statistics
   // r = LSE log2(e) - 14, for which R(i, j) 2^14 = exp2(S_ij c2 - r_i).
   const float* own_t = a.lse_t + (int64_t)unit * N;
@@ -1021,7 +1040,7 @@ void relkl_bwd_kernel(const BwdLaunch L) {
   const float* stg_s = a.lc_s + (int64_t)unit * N;
   constexpr float kLog2e = 1.4426950408889634f;
 
-  const int i0 = I * kBRB;
+  const int i0 = I * kRowsWG;
   const int ib0 = i0 + 32 * wave;
   const int row = ib0 + l32;
   const float c2 = a.c2;
@@ -1033,7 +1052,7 @@ void relkl_bwd_kernel(const BwdLaunch L) {
   // under the causal mask only those holding kept entries (up to the last own row for
   // dA, from the first own row on for dB).  The split divides that range.
   int kt_lo = 0, kt_hi = a.key_tiles;
-  if constexpr (CAUSAL && MODE == 1) kt_hi = min(a.key_tiles, (i0 + kBRB + kBC - 1) / kBC);
+  if constexpr (CAUSAL && MODE == 1) kt_hi = min(a.key_tiles, (i0 + kRowsWG + kBC - 1) / kBC);
   if constexpr (CAUSAL && MODE == 2) kt_lo = i0 / kBC;
   const int kt_begin = kt_lo + (int)(((int64_t)(kt_hi - kt_lo) * split) / a.splits);
   const int kt_end = kt_lo + (int)(((int64_t)(kt_hi - kt_lo) * (split + 1)) / a.splits);
@@ -1044,19 +1063,28 @@ void relkl_bwd_kernel(const BwdLaunch L) {
   // teacher and the student (one per lane, rows beyond N read row N-1).
   auto stage_tile = [&](int k, char* st_base) __attribute__((always_inline)) {
     const int j0 = (kt_begin + k) * kBC;
+    const int lim = N - 1 - j0;  // last row of the unit, relative to the tile (>= 0)
 #pragma unroll
     for (int q = 0; q < kDma; ++q) {
       const int slot0 = (wave * kDma + q) * kWave;
-      const int t = slot0 + lane;
-      const int r = t / G::kCPR;
-      const int c = (t % G::kCPR) ^ G::swz(r);
-      const int j = min(j0 + r, N - 1);
-      lds_copy16(yt_c + (int64_t)j * tsn_b + c * 16, lds_addr(st_base + slot0 * 16));
-      lds_copy16(ys_c + (int64_t)j * ssn_b + c * 16, lds_addr(st_base + G::kTileBytes + slot0 * 16));
+      // copy q covers rows rb .. rb + kRPC - 1 of the tile; lane l takes row rb + l / kCPR
+      // (clamped to the unit's last row) and chunk l % kCPR, stored at the swizzled slot.
+      // For rb a multiple of kRPC, swz(rb + x) = swz(rb) ^ swz(x), so the lane's part is
+      // the loop-invariant xc16 XOR a uniform constant.
+      const int rb = slot0 / G::kCPR;
+      const int rq = min(rb, lim);  // uniform; the lane adds min(l / kCPR, lim - rq) rows
+      int sq = G::swz(rb) << 4;
+      if constexpr (!CAUSAL) asm volatile("" : "+s"(sq));  // formed per copy, not held
+      const uint32_t rr = (uint32_t)min(xr, lim - rq);
+      const uint32_t c16 = (uint32_t)(xc16 ^ sq);
+      lds_copy16_s(__umul24(rr, tsn_u24) + c16, yt_c + (int64_t)(j0 + rq) * tsn_b,
+                   lds_addr(st_base + slot0 * 16));
+      lds_copy16_s(__umul24(rr, ssn_u24) + c16, ys_c + (int64_t)(j0 + rq) * ssn_b,
+                   lds_addr(st_base + G::kTileBytes + slot0 * 16));
     }
     if (wave < 2) {
-      const int j = min(j0 + lane, N - 1);
-      lds_copy4((wave == 0 ? stg_t : stg_s) + j, lds_addr(st_base + kStatsOff + wave * kBC * 4));
+      lds_copy4_s((uint32_t)min(lane, lim) * 4u, (wave == 0 ? stg_t : stg_s) + j0,
+                  lds_addr(st_base + kStatsOff + wave * kBC * 4));
     }
   };
   // Once a wave's own copies into a stage buffer have completed (wait_vmem): the fp16 image
@@ -1084,7 +1112,7 @@ void relkl_bwd_kernel(const BwdLaunch L) {
   auto buf = [&](int t) __attribute__((always_inline)) { return lds + (t % kStages) * kStage; };
   if (ntiles > 0) stage_tile(0, buf(0));
   // M(0)'s gradient part reads the last buffer's gradient tile before any copy fills it
-  for (int q = tid; q < G::kTileBytes / 16; q += kBWaves * kWave)
+  for (int q = tid; q < G::kTileBytes / 16; q += kW * kWave)
     *reinterpret_cast<u32x4*>(buf(kStages - 1) + kGradOff + 16 * q) = u32x4{0u, 0u, 0u, 0u};
 
   frag_t qt[KS], qs[KS];
@@ -1144,7 +1172,8 @@ void relkl_bwd_kernel(const BwdLaunch L) {
   };
 
   // V(n): W(n) from the scores of block n and the column statistics staged with its tile.
-  auto v_phase = [&](int n) __attribute__((always_inline)) {
+  // hh_, row_: the lane's half-wave index and row (passed in: see the last call below)
+  auto v_phase = [&](int n, int hh_, int row_) __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(0);
     const char* sb = buf(n >> 1);
     const int jb0 = block_j0(n);
@@ -1153,34 +1182,34 @@ void relkl_bwd_kernel(const BwdLaunch L) {
       const float* clt = reinterpret_cast<const float*>(sb + kStatsOff) + 32 * jb;
       const float* cls = clt + kBC;
       f32x8 w32[2];
-      const int di = row - jb0;
+      const int di = row_ - jb0;
       const int nl = N - jb0;
       const bool tail = jb0 + 32 > N;
       constexpr bool ROW = MODE != 2, COL = MODE != 1, SUB = MODE == 0;
       bool none = false;  // the block holds no entry this pass keeps
       if constexpr (!CAUSAL) {
         if (SUB && jb0 == ib0) {  // the wave's diagonal block
-          if (tail) make_w<ROW, COL, false, true, SUB>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, wd2, w32);
-          else make_w<ROW, COL, false, false, SUB>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, wd2, w32);
+          if (tail) make_w<ROW, COL, false, true, SUB>(st, ss, rt, rs, clt, cls, hh_, di, nl, c2, wd2, w32);
+          else make_w<ROW, COL, false, false, SUB>(st, ss, rt, rs, clt, cls, hh_, di, nl, c2, wd2, w32);
         } else if (tail) {
-          make_w<ROW, COL, false, true>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, wd2, w32);
+          make_w<ROW, COL, false, true>(st, ss, rt, rs, clt, cls, hh_, di, nl, c2, wd2, w32);
         } else {
-          make_w<ROW, COL, false, false>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, wd2, w32);
+          make_w<ROW, COL, false, false>(st, ss, rt, rs, clt, cls, hh_, di, nl, c2, wd2, w32);
         }
       } else {
         if (jb0 + 31 < ib0) {  // strictly below the diagonal: row terms
-          if constexpr (ROW) make_w<true, false, false, false>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, wd2, w32);
+          if constexpr (ROW) make_w<true, false, false, false>(st, ss, rt, rs, clt, cls, hh_, di, nl, c2, wd2, w32);
           else none = true;
         } else if (jb0 > ib0 + 31) {  // strictly above: column terms
           if constexpr (COL) {
-            if (tail) make_w<false, true, false, true>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, wd2, w32);
-            else make_w<false, true, false, false>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, wd2, w32);
+            if (tail) make_w<false, true, false, true>(st, ss, rt, rs, clt, cls, hh_, di, nl, c2, wd2, w32);
+            else make_w<false, true, false, false>(st, ss, rt, rs, clt, cls, hh_, di, nl, c2, wd2, w32);
           } else {
             none = true;
           }
         } else {
-          if (tail) make_w<ROW, COL, true, true, SUB>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, wd2, w32);
-          else make_w<ROW, COL, true, false, SUB>(st, ss, rt, rs, clt, cls, hh, di, nl, c2, wd2, w32);
+          if (tail) make_w<ROW, COL, true, true, SUB>(st, ss, rt, rs, clt, cls, hh_, di, nl, c2, wd2, w32);
+          else make_w<ROW, COL, true, false, SUB>(st, ss, rt, rs, clt, cls, hh_, di, nl, c2, wd2, w32);
         }
       }
       if (none) {
@@ -1200,13 +1229,13 @@ void relkl_bwd_kernel(const BwdLaunch L) {
   // matrix phases; waves 4-7 instead run V of a tile's last block after the barrier, at the
   // start of the next step, so their matrix phases fall beside the vector phases of waves 0-3
   // (each wave's own order of operations is unchanged; its stage buffer is still resident).
-  const bool lag = wave >= kBWaves / 2;
+  const bool lag = kW == 8 && wave >= 4;
   wait_vmem();
   if (ntiles > 0) convert_tile(0, buf(0));
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     if (kStages == 3 && t + 1 < ntiles) stage_tile(t + 1, buf(t + 1));
-    if (lag && t > 0) v_phase(2 * t - 1);
+    if (lag && t > 0) v_phase(2 * t - 1, hh, row);
     m_phase(2 * t);
     if (kStages == 2) {
       lds_barrier();
@@ -1219,19 +1248,32 @@ void relkl_bwd_kernel(const BwdLaunch L) {
       wait_vmem();
       if (t + 1 < ntiles) convert_tile(t + 1, buf(t + 1));
     }
-    v_phase(2 * t);
+    v_phase(2 * t, hh, row);
     m_phase(2 * t + 1);
-    if (!lag) v_phase(2 * t + 1);
+    if (!lag) v_phase(2 * t + 1, hh, row);
     wait_vmem();
     if (kStages == 2 && t + 1 < ntiles) convert_tile(t + 1, buf(t + 1));
     lds_barrier();
   }
-  if (lag && ntiles > 0) v_phase(NB - 1);
+  if (lag && ntiles > 0) {
+    // the non-causal sweep leaves no register for the lane's indices to survive the loop
+    // in: this last call forms them again (opaque to the compiler)
+    int ln = lane;
+    if constexpr (!CAUSAL)
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+    v_phase(NB - 1, ln >> 5, ib0 + (ln & 31));
+  }
   m_phase(NB);
 
   // Scale and write: acc[mb][r] = dX[i][d] * 2^14 / (scale g) for
   // i = ib0 + 8 (r/4) + 4 hh + (r%4), d = 32 mb + l32.
   const float factor = a.scale * a.grad_loss[0] * (1.0f / 16384.0f);
+  // the lane's indices again, formed here (opaque to the compiler) so that none of the
+  // epilogue's lane-derived values has to be held through the sweep
+  int lne = lane;
+  if constexpr (!CAUSAL)
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lne));
+  const int l32e = lne & 31, hhe = lne >> 5;
   if (a.rope_cos != nullptr) {
     // Gradient before the student's rotation: the transposed rotate-half rotation maps
     // (g_k, g_{k+D/2}) to (g_k c + g_{k+D/2} s, g_{k+D/2} c - g_k s) with the cos / sin of
@@ -1239,11 +1281,11 @@ void relkl_bwd_kernel(const BwdLaunch L) {
     // the same lane.
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int i = ib0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+      const int i = ib0 + 8 * (r >> 2) + 4 * hhe + (r & 3);
       if (i >= N) continue;
 #pragma unroll
       for (int mb = 0; mb < MB / 2; ++mb) {
-        const int64_t t = (int64_t)i * (D / 2) + 32 * mb + l32;
+        const int64_t t = (int64_t)i * (D / 2) + 32 * mb + l32e;
         const float c = a.rope_cos[t], sn = a.rope_sin[t];
         const float g1 = acc[mb][r], g2 = acc[mb + MB / 2][r];
         acc[mb][r] = fmaf(g1, c, g2 * sn);
@@ -1256,11 +1298,11 @@ void relkl_bwd_kernel(const BwdLaunch L) {
     char* gbase = reinterpret_cast<char*>(a.dx) + (b * a.g_sb + hin * a.g_sh) * (OUT_F32 ? 4 : 2);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int i = ib0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+      const int i = ib0 + 8 * (r >> 2) + 4 * hhe + (r & 3);
       if (!full && i >= N) continue;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        const int64_t o = (int64_t)i * a.g_sn + 32 * mb + l32;
+        const int64_t o = (int64_t)i * a.g_sn + 32 * mb + l32e;
         const float v = acc[mb][r] * factor;
         if constexpr (OUT_F32)
           reinterpret_cast<float*>(gbase)[o] = v;
@@ -1269,13 +1311,13 @@ void relkl_bwd_kernel(const BwdLaunch L) {
       }
     }
   } else {
-    const int rows_pad = a.row_tiles * kBRB;
+    const int rows_pad = a.row_tiles * kRowsWG;
     float* dst = a.partial + ((int64_t)split * a.B * a.H + unit) * rows_pad * D;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int i = ib0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+      const int i = ib0 + 8 * (r >> 2) + 4 * hhe + (r & 3);
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) dst[(int64_t)i * D + 32 * mb + l32] = acc[mb][r] * factor;
+      for (int mb = 0; mb < MB; ++mb) dst[(int64_t)i * D + 32 * mb + l32e] = acc[mb][r] * factor;
     }
   }
 }
@@ -1465,7 +1507,7 @@ int launch_fwd(const FwdLaunch& a, bool in_bf16, int d, bool causal, const LossO
 template <class Op, int D, bool CAUSAL, bool OUT_F32, int MODE>
 static int launch_bwd_t(const BwdLaunch& a, hipStream_t s) {
   hipLaunchKernelGGL((relkl_bwd_kernel<Op, D, CAUSAL, OUT_F32, MODE>), dim3(grid_of(a)),
-                     dim3(kBWaves * kWave), 0, s, a);
+                     dim3(bwd_waves(Op::kES == 4) * kWave), 0, s, a);
   return (int)hipGetLastError();
 }
 

@@ -41,8 +41,9 @@
  *  - NaN / Inf inputs are not checked and propagate.
  *  - For bf16 inputs the backward recomputes the scores on the bf16 rows as given and
  *    contracts the gradient in IEEE fp16: each staged student tile is converted on chip
- *    (bf16 -> fp16 is exact for 2^-17 <= |x| < 65504; smaller magnitudes keep an absolute
- *    error below 2^-25), and dZ is carried as fp16 scaled by 2^14.  Inputs with
+ *    (bf16 -> fp16 is exact for 2^-17 <= |x| < 65504; smaller magnitudes are rounded toward
+ *    zero onto the fp16 subnormal grid, an absolute error below 2^-24), and dZ is carried as
+ *    fp16 scaled by 2^14.  Inputs with
  *    |x| >= 65504 are not supported by the bf16 backward.
  */
 #ifndef LARD_H
@@ -78,6 +79,9 @@ typedef enum lard_dtype { LARD_FP32 = 0, LARD_BF16 = 1 } lard_dtype;
  *   B >= 1, H_in >= 1, N >= 1, d in {64, 128};
  *   all strides >= 0 and multiples of 8 (bf16) or 4 (fp32) elements, so that every row
  *   starts on a 16-byte boundary; x pointers 16-byte aligned;
+ *   for N > 1: t_stride_n, s_stride_n >= d, and their byte sizes below 2^24 (16 MiB;
+ *   else LARD_ERR_UNSUPPORTED: the backward addresses the rows of a key tile as 24-bit
+ *   offsets from the tile's first row);
  *   1 <= H <= LARD_MAX_HEADS;
  *   head_map == NULL  -> H == H_in and relation head h reads input head h;
  *   head_map != NULL  -> H entries, each in [0, H_in), pairwise distinct (injective:

@@ -117,10 +117,17 @@ def test_workspace_sizes(lib):
     (dict(t_stride_n=100), INVALID),      # not a multiple of 8 bf16 elements
     (dict(s_stride_h=-128), INVALID),
     (dict(t_stride_n=64), INVALID),       # rows overlap (stride over n < d)
+    (dict(s_stride_n=1 << 23), UNSUPPORTED),  # bf16 row stride of 16 MiB: beyond 24-bit offsets
+    (dict(t_stride_n=(1 << 23) - 8, s_stride_n=128), "ok"),  # just below the limit
 ])
 def test_descriptor_validation(lib, kw, code):
     desc = good_desc(**kw)
     _, st = ws_query(lib, desc, 0)
+    if code == "ok":  # valid: the calls get as far as the (injected) launch failure
+        assert st == OK
+        assert fwd(lib, desc) == HIP
+        assert bwd(lib, desc) == HIP
+        return
     assert st == code
     assert fwd(lib, desc) == code
     assert bwd(lib, desc) == code

@@ -24,7 +24,9 @@ def test_tiny_workload_full():
     (rel,) = workloads.make_inputs("tiny")
     f, dx = gpu_fwd_bwd(rel.x_t, rel.x_s, True)
     fo, dxo = oracle_fwd_bwd(rel.x_t, rel.x_s, True)
-    assert_parity(f, dx, fo, dxo, torch.float32, "tiny")
+    d = assert_parity(f, dx, fo, dxo, torch.float32, "tiny")
+    print(f"[table] tiny/causal qq loss_rel {d['loss_rel']:.2e} max_dlse {d['lse_abs']:.2e} "
+          f"row_kl_rl2 {d['row_kl_rl2']:.2e} grad_rl2 {d['grad_rl2']:.2e}", flush=True)
     err = np.abs(np64(f["row_kl"]) - fo["row_kl"])
     print(f"[parity] tiny row_kl max abs err {err.max():.3e}", flush=True)
     np.testing.assert_allclose(np64(f["row_kl"]), fo["row_kl"], rtol=1e-4, atol=1e-7)
