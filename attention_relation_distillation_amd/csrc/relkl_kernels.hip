@@ -1029,9 +1029,6 @@ void relkl_bwd_kernel(const BwdLaunch L) {
   // row strides in bytes are below 2^24 (checked on the host), so a clamped row (< 64)
   // times the stride plus a chunk offset is a 24-bit multiply-add
   const uint32_t tsn_u24 = (uint32_t)tsn_b, ssn_u24 = (uint32_t)ssn_b;
-  constexpr int kRPC = kWave / G::kCPR;  // tile rows per copy instruction
-  const int xr = lane / G::kCPR;
-  const int xc16 = ((lane % G::kCPR) ^ G::swz(xr)) << 4;
   // The forward's LSE vectors (nats); the kernel uses them as log2 statistics
   // r = LSE log2(e) - 14, for which R(i, j) 2^14 = exp2(S_ij c2 - r_i).
   const float* own_t = a.lse_t + (int64_t)unit * N;
@@ -1063,28 +1060,52 @@ void relkl_bwd_kernel(const BwdLaunch L) {
   // teacher and the student (one per lane, rows beyond N read row N-1).
   auto stage_tile = [&](int k, char* st_base) __attribute__((always_inline)) {
     const int j0 = (kt_begin + k) * kBC;
-    const int lim = N - 1 - j0;  // last row of the unit, relative to the tile (>= 0)
+    if constexpr (CAUSAL) {
+      // the tile's base plus per-lane offsets of the clamped row and chunk, held per copy
+      // (the non-causal form below, which forms them per copy, measured 1% slower here)
+      const int lim = N - 1 - j0;
+      const char* tbt = yt_c + (int64_t)j0 * tsn_b;
+      const char* tbs = ys_c + (int64_t)j0 * ssn_b;
 #pragma unroll
-    for (int q = 0; q < kDma; ++q) {
-      const int slot0 = (wave * kDma + q) * kWave;
-      // copy q covers rows rb .. rb + kRPC - 1 of the tile; lane l takes row rb + l / kCPR
-      // (clamped to the unit's last row) and chunk l % kCPR, stored at the swizzled slot.
-      // For rb a multiple of kRPC, swz(rb + x) = swz(rb) ^ swz(x), so the lane's part is
-      // the loop-invariant xc16 XOR a uniform constant.
-      const int rb = slot0 / G::kCPR;
-      const int rq = min(rb, lim);  // uniform; the lane adds min(l / kCPR, lim - rq) rows
-      int sq = G::swz(rb) << 4;
-      if constexpr (!CAUSAL) asm volatile("" : "+s"(sq));  // formed per copy, not held
-      const uint32_t rr = (uint32_t)min(xr, lim - rq);
-      const uint32_t c16 = (uint32_t)(xc16 ^ sq);
-      lds_copy16_s(__umul24(rr, tsn_u24) + c16, yt_c + (int64_t)(j0 + rq) * tsn_b,
-                   lds_addr(st_base + slot0 * 16));
-      lds_copy16_s(__umul24(rr, ssn_u24) + c16, ys_c + (int64_t)(j0 + rq) * ssn_b,
-                   lds_addr(st_base + G::kTileBytes + slot0 * 16));
-    }
-    if (wave < 2) {
-      lds_copy4_s((uint32_t)min(lane, lim) * 4u, (wave == 0 ? stg_t : stg_s) + j0,
-                  lds_addr(st_base + kStatsOff + wave * kBC * 4));
+      for (int q = 0; q < kDma; ++q) {
+        const int slot0 = (wave * kDma + q) * kWave;
+        const int t = slot0 + lane;
+        const uint32_t r = (uint32_t)min(t / G::kCPR, lim);
+        const uint32_t c16 = (uint32_t)(((t % G::kCPR) ^ G::swz(t / G::kCPR)) * 16);
+        lds_copy16_s(__umul24(r, tsn_u24) + c16, tbt, lds_addr(st_base + slot0 * 16));
+        lds_copy16_s(__umul24(r, ssn_u24) + c16, tbs, lds_addr(st_base + G::kTileBytes + slot0 * 16));
+      }
+      if (wave < 2) {
+        lds_copy4_s((uint32_t)min(lane, lim) * 4u, (wave == 0 ? stg_t : stg_s) + j0,
+                    lds_addr(st_base + kStatsOff + wave * kBC * 4));
+      }
+    } else {
+      const int lim = N - 1 - j0;  // last row of the unit, relative to the tile (>= 0)
+      const int xr = lane / G::kCPR;
+      const int xc16 = ((lane % G::kCPR) ^ G::swz(xr)) << 4;
+#pragma unroll
+      for (int q = 0; q < kDma; ++q) {
+        const int slot0 = (wave * kDma + q) * kWave;
+        // copy q covers rows rb .. rb + 64 / kCPR - 1 of the tile; lane l takes row
+        // rb + l / kCPR (clamped to the unit's last row) and chunk l % kCPR, stored at the
+        // swizzled slot.  For rb a multiple of 64 / kCPR, swz(rb + x) = swz(rb) ^ swz(x), so
+        // the lane's part is the loop-invariant xc16 XOR a uniform constant.
+        const int rb = slot0 / G::kCPR;
+        const int rq = min(rb, lim);  // uniform; the lane adds min(l / kCPR, lim - rq) rows
+        int sq = G::swz(rb) << 4;
+        asm volatile("" : "+s"(sq));  // formed per copy: the non-causal sweep has no register
+                                      // to hold one offset per copy through the loop
+        const uint32_t rr = (uint32_t)min(xr, lim - rq);
+        const uint32_t c16 = (uint32_t)(xc16 ^ sq);
+        lds_copy16_s(__umul24(rr, tsn_u24) + c16, yt_c + (int64_t)(j0 + rq) * tsn_b,
+                     lds_addr(st_base + slot0 * 16));
+        lds_copy16_s(__umul24(rr, ssn_u24) + c16, ys_c + (int64_t)(j0 + rq) * ssn_b,
+                     lds_addr(st_base + G::kTileBytes + slot0 * 16));
+      }
+      if (wave < 2) {
+        lds_copy4_s((uint32_t)min(lane, lim) * 4u, (wave == 0 ? stg_t : stg_s) + j0,
+                    lds_addr(st_base + kStatsOff + wave * kBC * 4));
+      }
     }
   };
   // Once a wave's own copies into a stage buffer have completed (wait_vmem): the fp16 image
@@ -1172,8 +1193,10 @@ void relkl_bwd_kernel(const BwdLaunch L) {
   };
 
   // V(n): W(n) from the scores of block n and the column statistics staged with its tile.
-  // hh_, row_: the lane's half-wave index and row (passed in: see the last call below)
-  auto v_phase = [&](int n, int hh_, int row_) __attribute__((always_inline)) {
+  // hhp, rowp: the lane's half-wave index and row as the non-causal kernel's last call forms
+  // them again (below); the causal kernel uses the values it holds
+  auto v_phase = [&](int n, int hhp, int rowp) __attribute__((always_inline)) {
+    const int hh_ = CAUSAL ? hh : hhp, row_ = CAUSAL ? row : rowp;
     __builtin_amdgcn_s_setprio(0);
     const char* sb = buf(n >> 1);
     const int jb0 = block_j0(n);
@@ -1258,10 +1281,13 @@ void relkl_bwd_kernel(const BwdLaunch L) {
   if (lag && ntiles > 0) {
     // the non-causal sweep leaves no register for the lane's indices to survive the loop
     // in: this last call forms them again (opaque to the compiler)
-    int ln = lane;
-    if constexpr (!CAUSAL)
+    if constexpr (CAUSAL) {
+      v_phase(NB - 1, hh, row);
+    } else {
+      int ln;
       asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
-    v_phase(NB - 1, ln >> 5, ib0 + (ln & 31));
+      v_phase(NB - 1, ln >> 5, ib0 + (ln & 31));
+    }
   }
   m_phase(NB);
 
@@ -1273,7 +1299,7 @@ void relkl_bwd_kernel(const BwdLaunch L) {
   int lne = lane;
   if constexpr (!CAUSAL)
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lne));
-  const int l32e = lne & 31, hhe = lne >> 5;
+  const int l32e = CAUSAL ? l32 : lne & 31, hhe = CAUSAL ? hh : lne >> 5;
   if (a.rope_cos != nullptr) {
     // Gradient before the student's rotation: the transposed rotate-half rotation maps
     // (g_k, g_{k+D/2}) to (g_k c + g_{k+D/2} s, g_{k+D/2} c - g_k s) with the cos / sin of
