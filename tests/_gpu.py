@@ -42,6 +42,16 @@ def banner(msg: str):
     print(f"[case] {msg}", flush=True)
 
 
+TABLE_LINES = []  # repeated at the end of the session by the terminal-summary hook
+
+
+def table(line: str):
+    """Print one per-workload parity line and keep it for the session's closing summary."""
+    line = f"[table] {line}"
+    print(line, flush=True)
+    TABLE_LINES.append(line)
+
+
 def state(f):
     """The forward's per-row state the backward takes: (lse_t, lse_s, diag_delta)."""
     return f["lse_t"], f["lse_s"], f["diag_delta"]

@@ -13,6 +13,17 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "slow: long-running")
 
 
+def pytest_terminal_summary(terminalreporter):
+    """Repeat the per-workload parity lines that tests/_gpu.py::table gathered, so that they
+    appear in quiet runs too."""
+    gpu_helpers = sys.modules.get("tests._gpu")
+    lines = getattr(gpu_helpers, "TABLE_LINES", None)
+    if lines:
+        terminalreporter.section("parity table (error against the float64 oracle)")
+        for line in lines:
+            terminalreporter.write_line(line)
+
+
 @pytest.fixture(scope="session")
 def golden():
     import json

@@ -9,7 +9,7 @@ the sampled rows to the LSE and row-KL gates, and sampled gradient rows of one u
 relation to the gradient gate (computed here by the oracle row by row: O(N d) per row once
 the LSE of the rows they touch is known).  Properties that hold at any size are checked on
 every output: finite values, KL >= 0 up to fp32 noise, loss equal to the sum of the row KLs.
-Each relation prints one "[table]" line: loss error, max |dLSE| and row-KL relative L2 on
+Each relation prints one "[table]" line (repeated in the session summary): loss error, max |dLSE| and row-KL relative L2 on
 the sampled rows, gradient relative L2 on the sampled gradient rows."""
 
 import json
@@ -21,7 +21,7 @@ import torch
 
 import oracle
 from attention_relation_distillation_amd import relkl, workloads
-from tests._gpu import GRAD_RL2, LOSS_RTOL, ROW_KL_RL2, banner, device, np64, rel_l2
+from tests._gpu import GRAD_RL2, LOSS_RTOL, ROW_KL_RL2, banner, device, np64, rel_l2, table
 
 pytestmark = pytest.mark.gpu
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -98,9 +98,9 @@ def check_workload(name, causal):
         g_ref = oracle.backward_unit(ut, us, scale, causal, 1.0, lse_t=flt, lse_s=fls,
                                      rows=rows, chunk=1024)
         g_rl2 = rel_l2(np64(dx[0, 0])[rows], g_ref)
-        print(f"[table] {key} {rel.name} loss_rel {loss_rel:.2e} unit_rel_max "
+        table(f"{key} {rel.name} loss_rel {loss_rel:.2e} unit_rel_max "
               f"{unit_rel.max():.2e} max_dlse {dlse:.2e} row_kl_rl2 {kl_rl2:.2e} "
-              f"grad_rl2 {g_rl2:.2e}", flush=True)
+              f"grad_rl2 {g_rl2:.2e}")
         assert loss_rel <= LOSS_RTOL[torch.bfloat16]
         assert np.all(unit_rel <= LOSS_RTOL[torch.bfloat16]), unit_rel.max()
         assert dlse <= 5e-5 * max(1.0, lse_max)
@@ -136,9 +136,8 @@ def test_llama2_4k_full():
                                          lse_t=fo["lse_t"][0, h], lse_s=fo["lse_s"][0, h],
                                          chunk=1024)
             g_err.append(rel_l2(np64(dx[0, h]), g_ref))
-        print(f"[table] llama2_4k/causal {rel.name} loss_rel {loss_rel:.2e} max_dlse "
-              f"{dlse:.2e} row_kl_rl2 {kl_rl2:.2e} grad_rl2 {max(g_err):.2e} (fp32 output)",
-              flush=True)
+        table(f"llama2_4k/causal {rel.name} loss_rel {loss_rel:.2e} max_dlse "
+              f"{dlse:.2e} row_kl_rl2 {kl_rl2:.2e} grad_rl2 {max(g_err):.2e} (fp32 output)")
         assert loss_rel <= LOSS_RTOL[torch.bfloat16]
         assert dlse <= 5e-5 * max(1.0, float(np.max(np.abs(fo["lse_t"]))))
         assert kl_rl2 <= ROW_KL_RL2

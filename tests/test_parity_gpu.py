@@ -12,7 +12,8 @@ import torch
 import oracle
 from attention_relation_distillation_amd import relkl, workloads
 from tests._gpu import (GRAD_RL2, LOSS_RTOL, ROW_KL_RL2, assert_parity, banner, device,
-                        gpu_fwd_bwd, np64, oracle_fwd_bwd, rel_l2, state, tiny_n_floor)
+                        gpu_fwd_bwd, np64, oracle_fwd_bwd, rel_l2, state, table,
+                        tiny_n_floor)
 
 pytestmark = pytest.mark.gpu
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -25,8 +26,8 @@ def test_tiny_workload_full():
     f, dx = gpu_fwd_bwd(rel.x_t, rel.x_s, True)
     fo, dxo = oracle_fwd_bwd(rel.x_t, rel.x_s, True)
     d = assert_parity(f, dx, fo, dxo, torch.float32, "tiny")
-    print(f"[table] tiny/causal qq loss_rel {d['loss_rel']:.2e} max_dlse {d['lse_abs']:.2e} "
-          f"row_kl_rl2 {d['row_kl_rl2']:.2e} grad_rl2 {d['grad_rl2']:.2e}", flush=True)
+    table(f"tiny/causal qq loss_rel {d['loss_rel']:.2e} max_dlse {d['lse_abs']:.2e} "
+          f"row_kl_rl2 {d['row_kl_rl2']:.2e} grad_rl2 {d['grad_rl2']:.2e}")
     err = np.abs(np64(f["row_kl"]) - fo["row_kl"])
     print(f"[parity] tiny row_kl max abs err {err.max():.3e}", flush=True)
     np.testing.assert_allclose(np64(f["row_kl"]), fo["row_kl"], rtol=1e-4, atol=1e-7)
