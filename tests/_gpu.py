@@ -68,11 +68,35 @@ def gpu_fwd_bwd(x_t, x_s, causal, head_map=None, dx_dtype=None, scale=None, g=1.
     return f, dx
 
 
+def diag_delta_ref(xt, xs, scale, lse_t, lse_s, head_map=None):
+    """R_s(i,i) - R_t(i,i) from its definition: R_m(i,i) = exp(scale |x_m,i|^2 - LSE_m(i)), in
+    float64 on the inputs' exact values and the oracle's LSE vectors ([B, H, N])."""
+    if head_map is not None:
+        xt, xs = xt[:, head_map], xs[:, head_map]
+    zt = scale * np.einsum("bhnd,bhnd->bhn", xt, xt)
+    zs = scale * np.einsum("bhnd,bhnd->bhn", xs, xs)
+    return np.exp(zs - lse_s) - np.exp(zt - lse_t)
+
+
+def diag_delta_tol(xt, xs, scale):
+    """Absolute gate of diag_delta = R_s(i,i) - R_t(i,i) = 1/(1 + lam_s) - 1/(1 + lam_t), lam the
+    row's off-diagonal mass relative to its diagonal.  Every off-diagonal exponential carries the
+    fp32 rounding of its score S, a relative error of about ln2 scale log2(e) 2^-24 |S| (a few
+    times that over the accumulation), and the error of 1/(1 + lam) is at most a quarter of lam's
+    relative error; |S| <= max |x|^2 by Cauchy-Schwarz.  Hence 1e-7 + 4 2^-24 scale max |x|^2:
+    about 4e-6 on the workloads (d = 128, N(0, 1) rows), more where rows carry large norms."""
+    sq = max(float(np.max(np.einsum("...d,...d->...", xt, xt))),
+             float(np.max(np.einsum("...d,...d->...", xs, xs))))
+    return 1e-7 + 4.0 * 2.0 ** -24 * scale * sq
+
+
 def oracle_fwd_bwd(x_t, x_s, causal, head_map=None, scale=None, g=1.0):
     d = x_t.shape[-1]
     s = oracle.default_scale(d) if scale is None else scale
     xt, xs = np64(x_t), np64(x_s)
     f = oracle.forward(xt, xs, s, causal, head_map=head_map)
+    f["diag_delta"] = diag_delta_ref(xt, xs, s, f["lse_t"], f["lse_s"], head_map)
+    f["diag_delta_tol"] = diag_delta_tol(xt, xs, s)
     dx = oracle.backward(xt, xs, s, causal, g, head_map=head_map)
     return f, dx
 
@@ -115,6 +139,8 @@ def assert_parity(f, dx, fo, dxo, dtype, label="", floor=None, row_kl_rl2=ROW_KL
     g_err = rel_l2(np64(dx), dxo)
     diag = dict(loss=loss, loss_ref=fo["loss"], loss_rel=loss_err, lse_abs=lse_err,
                 row_kl_rl2=kl_err, grad_rl2=g_err)
+    if "diag_delta" in fo and "diag_delta" in f:
+        diag["diag_delta_abs"] = float(np.max(np.abs(np64(f["diag_delta"]) - fo["diag_delta"])))
     loss_floor = grad_floor = 0.0
     if floor is not None:
         loss_floor, grad_floor = floor
@@ -124,4 +150,6 @@ def assert_parity(f, dx, fo, dxo, dtype, label="", floor=None, row_kl_rl2=ROW_KL
     assert kl_abs <= row_kl_rl2 * float(np.linalg.norm(fo["row_kl"])) + loss_floor, diag
     assert g_abs <= GRAD_RL2[dtype] * float(np.linalg.norm(dxo)) + grad_floor, diag
     assert lse_err <= 5e-5 * max(1.0, float(np.max(np.abs(fo["lse_t"])))), diag
+    if "diag_delta_abs" in diag:  # gate derived in diag_delta_tol
+        assert diag["diag_delta_abs"] <= fo["diag_delta_tol"], diag
     return diag
