@@ -5,10 +5,10 @@ and the full-size 4K and 32K shapes on sampled rows.
 
 The fused path rounds the rotated rows to the input dtype, as a model that applies RoPE
 itself would; the oracle takes the exact rotation of the same bytes and tables rounded once
-to that dtype.  The kernel evaluates the rotation in fp32 first, so the two roundings can
-differ by one step of the dtype where the exact value lies within an fp32 rounding of a
-rounding boundary (rare; a loss effect of about 1e-7 relative), and the gates are those of
-the plain path."""
+to that dtype.  The kernel forms the same value (exact products in fp64, one rounding of
+their sum or difference, one rounding to the dtype), so the rotated rows it keeps in the
+reserve equal the oracle's bit for bit; the other outputs are held to the plain path's
+gates."""
 
 import numpy as np
 import pytest
@@ -224,3 +224,37 @@ def test_rope_llama2_4k_full():
 
 def test_rope_llama2_32k_sampled():
     check_rope_full("llama2_32k", full_loss=False)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("d", [64, 128])
+def test_rope_reserve_is_the_rounded_rotation_bit_for_bit(d, dtype):
+    """The reserve's rotated rows (dense [units][N][d] per side, each copy starting on a
+    256-byte boundary) against rope.rotate_in_dtype of the same bytes and tables, compared
+    as bit patterns; the teacher side rotated, the student side with other tables, and a
+    head map that picks heads out of order."""
+    n, h_in = 301, 3
+    hm = [2, 0]
+    banner(f"rope reserve bits d={d} {dtype}")
+    g = torch.Generator().manual_seed(40 + d)
+    x = torch.randn((2, h_in, n, d), generator=g) * 3.0
+    x_t = x.to(dtype)
+    x_s = (x + 0.1 * torch.randn((2, h_in, n, d), generator=g)).to(dtype)
+    ct, st = rand_tables(n, d, 1)
+    cs, ss = rand_tables(n, d, 2)
+    f, _ = gpu_rope(x_t, x_s, (ct, st, cs, ss), True, head_map=hm)
+    e = 2 if dtype == torch.bfloat16 else 4
+    units = 2 * len(hm)
+    copy = units * n * d * e
+    stride = (copy + 255) // 256 * 256
+    res = f["reserve"].cpu()
+    view = torch.int16 if dtype == torch.bfloat16 else torch.int32
+    got_t = res[:copy].view(view).reshape(2, len(hm), n, d)
+    got_s = res[stride:stride + copy].view(view).reshape(2, len(hm), n, d)
+    dt = dtype_name(dtype)
+    ref_t = rope.rotate_in_dtype(np64(x_t)[:, hm], ct.double().numpy(), st.double().numpy(), dt)
+    ref_s = rope.rotate_in_dtype(np64(x_s)[:, hm], cs.double().numpy(), ss.double().numpy(), dt)
+    want_t = torch.from_numpy(ref_t).to(dtype).view(view)
+    want_s = torch.from_numpy(ref_s).to(dtype).view(view)
+    assert torch.equal(got_t, want_t), int((got_t != want_t).sum())
+    assert torch.equal(got_s, want_s), int((got_s != want_s).sum())
