@@ -160,3 +160,39 @@ def test_cross_autograd_function():
     assert float(loss.item()) == pytest.approx(fo["loss"], rel=1e-5)
     assert rel_l2(np64(xa.grad), dao) <= GRAD_RL2[torch.float32]
     assert rel_l2(np64(xb.grad), dbo) <= GRAD_RL2[torch.float32]
+
+
+@pytest.mark.parametrize("with_rope", [True, False])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_cross_reserve_is_exact_bit_for_bit(dtype, with_rope):
+    """The cross forward's reserve: A and B of both sides, rotated (or not) and rounded once
+    to the dtype, kept as fp16 images of the bf16 values (fp32 as given), dense
+    [units][N][d] copies in the order A_t, A_s, B_t, B_s, each on a 256-byte boundary.  It
+    must equal the oracle's rounded rotation converted the same way, bit for bit."""
+    n, d, hm = 263, 128, [1, 0]
+    banner(f"cross reserve bits {dtype} rope={with_rope}")
+    a_t, b_t, a_s, b_s = quad(2, 2, n, d, dtype, seed=61)
+    tabs = None
+    if with_rope:
+        gen = torch.Generator().manual_seed(62)
+        ang_t = torch.rand((n, d // 2), generator=gen, dtype=torch.float64) * 6.0 - 3.0
+        ang_s = torch.rand((n, d // 2), generator=gen, dtype=torch.float64) * 6.0 - 3.0
+        tabs = (torch.cos(ang_t).float(), torch.sin(ang_t).float(),
+                torch.cos(ang_s).float(), torch.sin(ang_s).float())
+    f, _, _ = gpu_cross(a_t, b_t, a_s, b_s, True, tabs=tabs, head_map=hm)
+    res = f["reserve"].cpu()
+    e = 2 if dtype == torch.bfloat16 else 4
+    copy = 2 * len(hm) * n * d * e
+    stride = (copy + 255) // 256 * 256
+    view = torch.int16 if dtype == torch.bfloat16 else torch.int32
+    dt = "bf16" if dtype == torch.bfloat16 else "fp32"
+    tab = [None] * 4 if tabs is None else [t.double().numpy() for t in tabs]
+    sides = [(a_t, tab[0], tab[1]), (a_s, tab[2], tab[3]), (b_t, tab[0], tab[1]),
+             (b_s, tab[2], tab[3])]
+    for k, (x, c, s_) in enumerate(sides):
+        got = res[k * stride:k * stride + copy].view(view).reshape(2, len(hm), n, d)
+        ref = torch.from_numpy(rope.rotate_in_dtype(np64(x)[:, hm], c, s_, dt)).to(dtype)
+        if dtype == torch.bfloat16:
+            ref = ref.to(torch.float16)  # the fp16 image of each bf16 value (round to even)
+        want = ref.view(view)
+        assert torch.equal(got, want), (k, int((got != want).sum()))
