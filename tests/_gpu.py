@@ -121,12 +121,14 @@ def tiny_n_floor(fo, x_s, scale):
     return loss_floor, grad_floor
 
 
-def assert_parity(f, dx, fo, dxo, dtype, label="", floor=None, row_kl_rl2=ROW_KL_RL2):
+def assert_parity(f, dx, fo, dxo, dtype, label="", floor=None, row_kl_rl2=ROW_KL_RL2,
+                  grad_dtype=None):
     """Compare GPU outputs with the oracle at the dtype's gates; returns diagnostics.
 
     floor: None, or (loss_floor, grad_floor) from tiny_n_floor for the named tiny-N edge
     cases, added to the gates there.  row_kl_rl2: the row-KL gate (a named case may
-    derive its own)."""
+    derive its own).  grad_dtype: the gradient output's dtype when it differs from the
+    inputs' (its gate is that dtype's)."""
     loss = float(f["loss"].item())
     loss_abs = abs(loss - fo["loss"])
     loss_err = loss_abs / max(abs(fo["loss"]), 1e-30)
@@ -148,7 +150,8 @@ def assert_parity(f, dx, fo, dxo, dtype, label="", floor=None, row_kl_rl2=ROW_KL
     print(f"[parity] {label} {diag}", flush=True)
     assert loss_abs <= LOSS_RTOL[dtype] * abs(fo["loss"]) + loss_floor, diag
     assert kl_abs <= row_kl_rl2 * float(np.linalg.norm(fo["row_kl"])) + loss_floor, diag
-    assert g_abs <= GRAD_RL2[dtype] * float(np.linalg.norm(dxo)) + grad_floor, diag
+    gd = dtype if grad_dtype is None else grad_dtype  # the gradient's output dtype's gate
+    assert g_abs <= GRAD_RL2[gd] * float(np.linalg.norm(dxo)) + grad_floor, diag
     assert lse_err <= 5e-5 * max(1.0, float(np.max(np.abs(fo["lse_t"])))), diag
     if "diag_delta_abs" in diag:  # gate derived in diag_delta_tol
         assert diag["diag_delta_abs"] <= fo["diag_delta_tol"], diag
