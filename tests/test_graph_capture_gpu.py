@@ -1,7 +1,8 @@
 """The library's calls inside a captured HIP graph: the entry points only launch kernels on
 the given stream (no allocation, no memset, no synchronisation), so a forward + backward
 can be captured once and replayed.  Every replay, with eager work and synchronisations in
-between, must match the eager result bitwise."""
+between, must match the eager result bitwise.  The allocation-free forward is captured into
+outputs allocated beforehand, as a caller that cannot allocate would use it."""
 
 import pytest
 import torch
@@ -12,7 +13,7 @@ from tests._gpu import banner, device
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("path", ["plain", "rope", "cross", "group"])
+@pytest.mark.parametrize("path", ["plain", "rope", "cross", "group", "noalloc"])
 def test_capture_and_replay(path):
     banner(f"graph capture {path}")
     dev = device()
@@ -21,8 +22,17 @@ def test_capture_and_replay(path):
     kt, ks = k.x_t.to(dev), k.x_s.to(dev)
     tabs = [t.to(dev) for t in (q.cos_t, q.sin_t, q.cos_s, q.sin_s)]
     gl = torch.ones((), dtype=torch.float32, device=dev)
+    # outputs of the allocation-free forward and its backward, allocated before any capture
+    rows = (xt.shape[0], xt.shape[1], xt.shape[2])
+    na = [torch.empty(rows, dtype=torch.float32, device=dev) for _ in range(3)]
+    na_loss = torch.empty((), dtype=torch.float32, device=dev)
+    na_dx = torch.empty_like(xs)
 
     def run():
+        if path == "noalloc":
+            relkl.relkl_fwd_noalloc(xt, xs, na[0], na[1], na[2], None, na_loss, causal=True)
+            relkl.relkl_bwd(xt, xs, na[0], na[1], na[2], gl, causal=True, dx=na_dx)
+            return na_loss, na_dx
         if path == "plain":
             f = relkl.relkl_fwd(xt, xs, causal=True)
             return f["loss"], relkl.relkl_bwd(xt, xs, f["lse_t"], f["lse_s"], f["diag_delta"], gl,
@@ -59,6 +69,7 @@ def test_capture_and_replay(path):
     for rep in range(3):
         junk = torch.randn((1024, 1024), device=dev) @ torch.randn((1024, 1024), device=dev)
         g_dx.fill_(float("nan"))  # the replay must rewrite everything it returns
+        g_loss.fill_(float("nan"))
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
