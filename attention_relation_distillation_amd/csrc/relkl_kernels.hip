@@ -298,6 +298,30 @@ __device__ __forceinline__ typename In::frag_t lds_frag(const char* tile, int ba
   }
 }
 
+// fp16 image of a staged student tile (backward, bf16 inputs), laid out for the transposed
+// gradient reads: D / 32 blocks of 32 columns, each [kBC rows][64 bytes], blocks kBlkBytes
+// apart; in row r the two 32-byte halves of a block swap when bit 1 of r is set.  A
+// transposed read (per 16-lane group four consecutive rows, 32 bytes each; 512 bytes in all)
+// touches every bank once per 32 lanes, and its rows, halves and block are immediates on one
+// per-lane base.  The 64 bytes between blocks put the 16 chunks of one row, which a group of
+// 16 lanes converts together, on distinct banks.
+template <int D>
+struct ImgGeo {
+  static constexpr int kBlkBytes = kBC * 64 + 64;
+  static constexpr int kBytes = (D / 32) * kBlkBytes;
+  // byte offset of chunk c (columns 8 c .. 8 c + 7) of row r
+  __device__ static __forceinline__ int off(int r, int c) {
+    return (c >> 2) * kBlkBytes + r * 64 + ((((c >> 1) ^ (r >> 1)) & 1) << 5) + ((c & 1) << 4);
+  }
+  // per-lane base of the transposed reads: lane s of 16-lane group g addresses row
+  // 4 hh + s / 4 of an 8-row group, columns 16 (g % 2) + 4 (s % 4) .. +3 of the block
+  __device__ static __forceinline__ int trb_base(int lane) {
+    const int s = lane & 15, g = lane >> 4, hh = lane >> 5;
+    const int r = 4 * hh + (s >> 2);
+    return r * 64 + ((((g & 1) ^ (r >> 1)) & 1) << 5) + 8 * (s & 3);
+  }
+};
+
 // ------------------------------------------------------------------ LDS read pipelines
 // A single wave only sustains about 30 B/clk of LDS reads with a few reads in flight, while
 // its MFMAs consume a 1 KB fragment per 32 cycles; so matrix phases request fragments far
@@ -852,7 +876,13 @@ template <class Op, int D>
 __device__ __forceinline__ typename Op::gfrag_t grad_bfrag(const char* tile, int jbase, int mb,
                                                            int lane, int tb0, int tb1) {
   using G = Geo<D, Op::kES>;
-  if constexpr (Op::kES == 2) {
+  if constexpr (Op::kConvert) {  // the fp16 image (ImgGeo); tb0 from ImgGeo::trb_base
+    const char* p = tile + tb0 + (mb * ImgGeo<D>::kBlkBytes + jbase * 64);
+    const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)p);
+    const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p + 8 * 64));
+    const u32x2 a0 = __builtin_bit_cast(u32x2, v0), a1 = __builtin_bit_cast(u32x2, v1);
+    return __builtin_bit_cast(f16x8, u32x4{a0[0], a0[1], a1[0], a1[1]});
+  } else if constexpr (Op::kES == 2) {
     const char* rows = tile + jbase * G::kRowBytes;
     const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(rows + (tb0 ^ (mb << 6))));
     const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(rows + (tb1 ^ (mb << 6))));
@@ -953,7 +983,8 @@ __device__ __forceinline__ void m_pipeline(const char* gtile, int jbg, const cha
 // they are (as the forward does), and every staged student tile also gets an IEEE fp16
 // image in LDS (exact for 2^-17 <= |x| < 65504), which the gradient contraction reads with W
 // carried as fp16: each wave converts the 16-byte chunks it copied itself, after its own
-// copies have landed and before the barrier that publishes the tile.
+// copies have landed and before the barrier that publishes the tile, into the column-blocked
+// layout of ImgGeo (one address addition per matrix phase for all of its transposed reads).
 template <class Op, int D, bool CAUSAL, bool OUT_F32, int MODE>
 __global__ __attribute__((amdgpu_flat_work_group_size(bwd_waves(Op::kES == 4) * kWave,
                                                       bwd_waves(Op::kES == 4) * kWave),
@@ -966,10 +997,13 @@ void relkl_bwd_kernel(const BwdLaunch L) {
   using G = Geo<D, Op::kES>;
   constexpr int KS = D / 16;
   constexpr int MB = D / 32;  // 32-wide output blocks over d
+  using P = ImgGeo<D>;
   constexpr int kStats = 2 * kBC * 4;
   // stage layout: [teacher tile][student tile]([student fp16 image])[teacher stats][student stats]
-  constexpr int kGradOff = Op::kConvert ? 2 * G::kTileBytes : G::kTileBytes;
-  constexpr int kStatsOff = (Op::kConvert ? 3 : 2) * G::kTileBytes;
+  constexpr int kTileB = G::kTileBytes;
+  constexpr int kImgB = Op::kConvert ? P::kBytes : 0;
+  constexpr int kGradOff = Op::kConvert ? 2 * kTileB : kTileB;
+  constexpr int kStatsOff = 2 * kTileB + kImgB;
   constexpr int kStage = kStatsOff + kStats;
   constexpr int kW = bwd_waves(Op::kES == 4);  // waves of the workgroup
   constexpr int kRowsWG = 32 * kW;               // rows it owns
@@ -1042,8 +1076,8 @@ void relkl_bwd_kernel(const BwdLaunch L) {
   const int row = ib0 + l32;
   const float c2 = a.c2;
   const int fbase = frag_base<Op, D>(l32, hh);
-  const int tb0 = Op::kES == 2 ? trb_base<D>(lane, 0) : 0;
-  const int tb1 = Op::kES == 2 ? trb_base<D>(lane, 1) : 0;
+  const int tb0 = Op::kConvert ? P::trb_base(lane) : Op::kES == 2 ? trb_base<D>(lane, 0) : 0;
+  const int tb1 = !Op::kConvert && Op::kES == 2 ? trb_base<D>(lane, 1) : 0;
 
   // Key tiles this workgroup sweeps: all of them for the relation; for the cross passes
   // under the causal mask only those holding kept entries (up to the last own row for
@@ -1055,6 +1089,16 @@ void relkl_bwd_kernel(const BwdLaunch L) {
   const int kt_end = kt_lo + (int)(((int64_t)(kt_hi - kt_lo) * (split + 1)) / a.splits);
   const int NB = 2 * (kt_end - kt_begin);
 
+  // bf16 inputs: where the chunks this lane copies go in the fp16 image.  Copy qq of a tile
+  // covers rows rq = qq kWave / kCPR .. (a multiple of 4) and the lane takes row rq + l / kCPR,
+  // stored chunk l % kCPR, i.e. column chunk (l % kCPR) ^ swz(row).  With 16 chunks per row
+  // swz(row) = swz(l / kCPR) ^ (qq % 4) and the image offset of that chunk is this lane's
+  // offset for qq = 0, bits 4-5 flipped by qq % 4, plus rq 64; with 8 it is the qq = 0 offset
+  // plus rq 64.
+  auto img_lane_of = [](int l) __attribute__((always_inline)) {
+    return P::off(l / G::kCPR, (l % G::kCPR) ^ G::swz(l / G::kCPR));
+  };
+  const int img_lane = img_lane_of(lane);
   // Stage: [teacher tile][student tile]([fp16 image])[teacher stats][student stats]; all 8
   // waves copy their share of the two tiles, and waves 0 and 1 the 64 LSE values of the
   // teacher and the student (one per lane, rows beyond N read row N-1).
@@ -1109,16 +1153,26 @@ void relkl_bwd_kernel(const BwdLaunch L) {
     }
   };
   // Once a wave's own copies into a stage buffer have completed (wait_vmem): the fp16 image
-  // of the student chunks it copied (same layout as the tile), and, for waves 0 and 1, its
+  // of the student chunks it copied (ImgGeo layout), and, for waves 0 and 1, its
   // LSE values turned into log2 statistics (rows beyond N: a huge value, i.e. R = 0).
   auto convert_tile = [&](int k, char* st_base) __attribute__((always_inline)) {
     asm volatile("" ::: "memory");  // the reads below follow the completed copies
     if constexpr (Op::kConvert) {
+      // the non-causal sweep has no register to hold img_lane through: formed here from the
+      // lane index, opaque to the compiler
+      int il = img_lane;
+      if constexpr (!CAUSAL) {
+        int ln;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+        il = img_lane_of(ln);
+      }
 #pragma unroll
       for (int q = 0; q < kDma; ++q) {
-        const int off = ((wave * kDma + q) * kWave + lane) * 16;
+        const int qq = wave * kDma + q;  // wave-uniform
+        const int off = (qq * kWave + lane) * 16;
+        const int io = (il ^ ((G::kCPR >= 16 ? qq & 3 : 0) << 4)) + qq * (kWave / G::kCPR) * 64;
         const u32x4 v = *reinterpret_cast<const u32x4*>(st_base + G::kTileBytes + off);
-        *reinterpret_cast<u32x4*>(st_base + kGradOff + off) =
+        *reinterpret_cast<u32x4*>(st_base + kGradOff + io) =
             bf16x8_to_f16x8_bits(__builtin_bit_cast(bf16x8, v));
       }
     }
@@ -1133,7 +1187,7 @@ void relkl_bwd_kernel(const BwdLaunch L) {
   auto buf = [&](int t) __attribute__((always_inline)) { return lds + (t % kStages) * kStage; };
   if (ntiles > 0) stage_tile(0, buf(0));
   // M(0)'s gradient part reads the last buffer's gradient tile before any copy fills it
-  for (int q = tid; q < G::kTileBytes / 16; q += kW * kWave)
+  for (int q = tid; q < (Op::kConvert ? kImgB : G::kTileBytes) / 16; q += kW * kWave)
     *reinterpret_cast<u32x4*>(buf(kStages - 1) + kGradOff + 16 * q) = u32x4{0u, 0u, 0u, 0u};
 
   frag_t qt[KS], qs[KS];
