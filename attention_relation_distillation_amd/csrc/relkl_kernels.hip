@@ -179,8 +179,11 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) {
 // picks its stage buffers at run time), and it stops counting LDS reads individually:
 // every read then waits for all earlier ones (lgkmcnt(0)), which breaks the read-ahead of
 // the matrix pipelines.  Completion is awaited explicitly with wait_vmem() before the
-// barrier that publishes a tile.  The s_nop covers the one wait state needed between
-// writing M0 and the copy.
+// barrier that publishes a tile.  The s_nop covers the one wait state needed between a
+// scalar write of M0 and the copy.  A vector instruction that writes a scalar operand of a
+// copy (M0 or the base, e.g. v_readfirstlane) would need five, and the compiler's hazard
+// checks do not look inside the asm: the compiled kernels are checked statically to have no
+// such write that close to a copy (they take their bases and M0 from scalar instructions).
 __device__ __forceinline__ void lds_copy16(const void* g, uint32_t lds_base) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds_base) : "memory");
 }
@@ -860,9 +863,11 @@ __device__ __forceinline__ typename Op::gfrag_t w_frag(const f32x8& w) {
 // row-major key tile.  ds_read_b64_tr_b16: in each 16-lane group, lane s gives the
 // address of row (r0 + s/4), columns c0 + 4 (s%4) .. +3, and lane q receives column
 // c0 + q of rows r0 .. r0 + 3.  Here r0 = jbase + 8 half + 4 hh and c0 = 32 mb + 16 (g%2)
-// for lane group g; the row swizzle does not depend on jb or kb (multiples of 16 rows),
-// and mb only flips chunk bits 2-3, so the address is a per-lane base for each half,
-// XOR (mb << 6), plus the immediate jbase rows.
+// for lane group g.  In the swizzled key tile (fp16 reserve copies of the cross relation)
+// the row swizzle does not depend on jb or kb (multiples of 16 rows), and mb only flips chunk
+// bits 2-3, so the address is a per-lane base for each half, XOR (mb << 6), plus the
+// immediate jbase rows; in the fp16 image of bf16 inputs (ImgGeo) the whole offset past one
+// per-lane base is an immediate.
 template <int D>
 __device__ __forceinline__ int trb_base(int lane, int half) {
   using G = Geo<D, 2>;
