@@ -330,9 +330,10 @@ struct ImgGeo {
 // its MFMAs consume a 1 KB fragment per 32 cycles; so matrix phases request fragments far
 // ahead of their MFMAs: before each MFMA, further fragments are requested while at most
 // MAXOPS reads are outstanding (the LGKM counter tracks 15).  Measured best at 32 heads x
-// 32K: 12 in the forward (2% faster than 6 or 8, 14 no better) and 6 in the backward, whose
-// phases hold more registers (0.4% faster than 8; 12 was 2% slower).
-constexpr int kFwdLdsOps = 12;
+// 32K: 10 in the forward (1% faster than 8, 11 or 12, which the registers of its current
+// pipeline only just hold) and 6 in the backward, whose phases hold more registers (7 and 8 no
+// better; 12 was 2% slower).
+constexpr int kFwdLdsOps = 10;
 constexpr int kBwdLdsOps = 6;
 
 template <int NG, int NF, int OPS_G, int OPS_S, int MAXOPS>
@@ -643,23 +644,41 @@ void relkl_fwd_kernel(const FwdLaunch L) {
       float lt[2] = {0.f, 0.f}, ls[2] = {0.f, 0.f}, aa[2] = {0.f, 0.f};
       const float bt = b_t, bs = b_s;
       __builtin_amdgcn_s_setprio(1);
+      // Element r's exponent arguments and exponentials go into one MFMA slot and its sums
+      // into the next, so that no slot waits on an exponential it has just issued; the sums
+      // keep their order, so the result is the same bit for bit.
+      float ut[16], us[16], xt[16], xs[16];
+      auto pre = [&](int r) __attribute__((always_inline)) {
+        ut[r] = fmaf(pt[r], c2, bt);
+        us[r] = fmaf(ps[r], c2, bs);
+      };
+      auto ex = [&](int r) __attribute__((always_inline)) {
+        xt[r] = fast_exp2(ut[r]);
+        xs[r] = fast_exp2(us[r]);
+      };
+      auto add = [&](int r) __attribute__((always_inline)) {
+        if (r < 2) {  // exponentials are never -0, so these equal 0 + et and 0 + es bitwise
+          lt[r] = xt[r];
+          ls[r] = xs[r];
+        } else {
+          lt[r & 1] += xt[r];
+          ls[r & 1] += xs[r];
+        }
+        aa[r & 1] = fmaf(xt[r], pt[r] - ps[r], aa[r & 1]);
+      };
       score_pipeline<In, D>(tile_t, tile_s, fbase, jb, qt, qs, st, ss,
                             [&](auto ic) __attribute__((always_inline)) {
         constexpr int I = decltype(ic)::value;
+        constexpr int lo = I * E < 16 ? I * E : 16, hi = (I + 1) * E < 16 ? (I + 1) * E : 16;
 #pragma unroll
-        for (int r = I * E; r < (I + 1) * E && r < 16; ++r) {
-          const float et = fast_exp2(fmaf(pt[r], c2, bt));
-          const float es = fast_exp2(fmaf(ps[r], c2, bs));
-          if (r < 2) {  // exponentials are never -0, so these equal 0 + et and 0 + es bitwise
-            lt[r] = et;
-            ls[r] = es;
-          } else {
-            lt[r & 1] += et;
-            ls[r & 1] += es;
-          }
-          aa[r & 1] = fmaf(et, pt[r] - ps[r], aa[r & 1]);
-        }
+        for (int r = lo; r < hi; ++r) pre(r);
+#pragma unroll
+        for (int r = lo; r < hi; ++r) ex(r);
+#pragma unroll
+        for (int r = (lo >= E ? lo - E : 0); r < (lo >= E ? lo : 0); ++r) add(r);
       });
+#pragma unroll
+      for (int r = 16 - E; r < 16; ++r) add(r);
       __builtin_amdgcn_s_setprio(0);
       const float sum_t = lt[0] + lt[1], sum_s = ls[0] + ls[1], sum_a = aa[0] + aa[1];
       const bool ok = sum_t <= 0x1p64f && sum_s <= 0x1p64f;
