@@ -657,7 +657,7 @@ void relkl_fwd_kernel(const FwdLaunch L) {
         xs[r] = fast_exp2(us[r]);
       };
       auto add = [&](int r) __attribute__((always_inline)) {
-        if (r < 2) {  // exponentials are never -0, so these equal 0 + et and 0 + es bitwise
+        if (r < 2) {  // an exponential is never -0, so this equals 0 + the exponential bitwise
           lt[r] = xt[r];
           ls[r] = xs[r];
         } else {
