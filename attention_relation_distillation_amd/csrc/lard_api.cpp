@@ -530,6 +530,16 @@ const char* lard_status_string(lard_status status) {
 
 int lard_version(void) { return kVersion; }
 
+lard_status lard_probe_mfma(int vector_work, int iters, int workgroups, float* sink,
+                            void* stream) {
+  if (!sink || !aligned(sink, 4) || iters < 1 || iters > (1 << 20) || workgroups < 1 ||
+      workgroups > (1 << 16) || (vector_work != 0 && vector_work != 1))
+    return LARD_ERR_INVALID_ARGUMENT;
+  return launch_probe_mfma(vector_work == 1, iters, workgroups, sink, stream) == 0
+             ? LARD_OK
+             : LARD_ERR_HIP;
+}
+
 size_t lard_relkl_workspace_size(const lard_relkl_desc* desc, int pass, lard_status* status) {
   lard_status s = check_desc(desc);
   if (s == LARD_OK && pass != 0 && pass != 1) s = LARD_ERR_INVALID_ARGUMENT;

@@ -121,6 +121,8 @@ def load_library():
                                               ctypes.POINTER(ctypes.c_int)]
     lib.lard_relkl_fwd.restype = ctypes.c_int
     lib.lard_relkl_fwd.argtypes = [ctypes.POINTER(_Desc), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.lard_probe_mfma.restype = ctypes.c_int
+    lib.lard_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp]
     lib.lard_relkl_fwd_noalloc.restype = ctypes.c_int
     lib.lard_relkl_fwd_noalloc.argtypes = [ctypes.POINTER(_Desc), vp, vp, vp, vp, vp, vp, vp, vp]
     lib.lard_relkl_bwd.restype = ctypes.c_int
@@ -336,6 +338,25 @@ def relkl_bwd(x_t: torch.Tensor, x_s: torch.Tensor, lse_t: torch.Tensor, lse_s: 
                                   ws.data_ptr(), ws.numel(), _stream_handle(dev, stream)))
     del keep
     return dx
+
+
+PROBE_THREADS = 512       # LARD_PROBE_THREADS
+PROBE_MFMA_PER_ITER = 24  # LARD_PROBE_MFMA_PER_ITER
+PROBE_FLOPS_PER_MFMA = 2 * 32 * 32 * 16
+
+
+def probe_mfma(vector_work: bool, iters: int, workgroups: int, sink: torch.Tensor, stream=None):
+    """Enqueue the matrix-core throughput probe (lard_probe_mfma; measurement only).  It
+    issues workgroups * 8 waves * iters * PROBE_MFMA_PER_ITER bf16 MFMAs; sink: fp32 device
+    tensor of at least workgroups * PROBE_THREADS elements."""
+    lib = load_library()
+    _require_gpu(sink)
+    if sink.dtype != torch.float32 or not sink.is_contiguous() or \
+            sink.numel() < workgroups * PROBE_THREADS:
+        raise ValueError("sink: contiguous fp32 tensor of workgroups * PROBE_THREADS elements")
+    _check(lib.lard_probe_mfma(1 if vector_work else 0, int(iters), int(workgroups),
+                               ctypes.c_void_p(sink.data_ptr()),
+                               _stream_handle(sink.device, stream)))
 
 
 def _mean_rows_factor(x: torch.Tensor, reduction: str) -> Optional[float]:

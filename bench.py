@@ -92,6 +92,41 @@ def alg_flops(B, H, N, d, causal):
     return B * H * 2 * per, B * H * 4 * per
 
 
+def executed_bwd_flops(B, H, N, d):
+    """MFMA flops the backward kernel executes per launch (2-byte inputs): every workgroup of 8
+    waves owns 256 rows and runs one matrix phase per 32-key block of the whole key range plus
+    one (2 key_tiles + 1); a wave's phase issues d/8 score MFMAs (teacher and student) and d/16
+    gradient MFMAs of 32x32x16.  Full-row ownership scores every (row, key) pair of the causal
+    relation twice, so this is 6/4 of the algorithmic count."""
+    row_tiles = -(-N // 256)
+    key_tiles = -(-N // 64)
+    per_phase = d // 8 + d // 16
+    return B * H * row_tiles * (2 * key_tiles + 1) * 8 * per_phase * 2.0 * 32 * 32 * 16
+
+
+def mfma_ceiling(relkl, torch, dev, iters=2000, reps=5):
+    """Dense bf16 MFMA rate the part sustains under a full matrix load (lard_probe_mfma), with
+    and without the backward's vector work beside it: TFLOP/s over `reps` timed launches."""
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.empty(cus * relkl.PROBE_THREADS, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    flops = cus * 8 * iters * relkl.PROBE_MFMA_PER_ITER * relkl.PROBE_FLOPS_PER_MFMA
+    out = {}
+    for vec in (False, True):
+        relkl.probe_mfma(vec, iters, cus, sink)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            relkl.probe_mfma(vec, iters, cus, sink)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        s = e0.elapsed_time(e1) / reps / 1e3
+        out["with_vector_work_tflops" if vec else "pure_tflops"] = round(flops / s / 1e12, 1)
+    out["workgroups"] = cus
+    return out
+
+
 _CPU_UNIT = {}
 
 
@@ -530,6 +565,7 @@ def main():
                      "alg_flops_per_launch": mean_bwd_flops,
                      "mean_launch_ms": round(mean_bwd_s * 1e3, 3)},
         "executed_counters": counters,
+        "mfma_ceiling": None,
         "alg_tflops_total": round(total_tflops, 1),
         "frac_of_bf16_peak_total": round(total_tflops / PEAK_BF16_TFLOPS, 4),
         "fwd_ms": round(fwd_ms, 3),
@@ -543,6 +579,15 @@ def main():
         "kernel_sources": kernel_source_digest(),
         "cpu_baseline": None,
     }
+
+    # the dense bf16 rate the part sustains beside the published peak, and the backward's
+    # executed MFMA rate against it (full-row ownership executes 6/4 of the algorithmic work)
+    ceil = mfma_ceiling(relkl, torch, dev)
+    ex_b = sum(executed_bwd_flops(wl.B, r.x_t.shape[1], wl.N, wl.d) for r in rels) / n_rel
+    ceil["bwd_executed_tflops"] = round(ex_b / mean_bwd_s / 1e12, 1)
+    ceil["bwd_executed_frac_of_pure"] = round(ex_b / mean_bwd_s / 1e12 / ceil["pure_tflops"], 4)
+    out["mfma_ceiling"] = ceil
+    print("[bench] MFMA ceiling probe done", file=sys.stderr, flush=True)
 
     if args.rope_steps > 0:
         out["next_rows"] = {"rope_fused": rope_fused_timing(relkl, workloads, wl, dev, causal,

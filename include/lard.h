@@ -370,6 +370,24 @@ lard_status lard_relkl_fwd_noalloc(const lard_relkl_desc* desc, const void* x_te
                                    float* lse_student, float* diag_delta, float* row_kl,
                                    float* loss, void* stream);
 
+/*
+ * Matrix-core throughput probe (measurement, not part of the relation KL): enqueues one
+ * kernel of `workgroups` workgroups of LARD_PROBE_THREADS threads (two waves per SIMD when
+ * one workgroup runs per CU, the relation backward's occupancy), in which every wave issues
+ * iters * LARD_PROBE_MFMA_PER_ITER independent v_mfma_f32_32x32x16_bf16 (32768 flops each)
+ * with register operands.  vector_work = 1 adds, per four MFMAs, the vector work of four
+ * backward probability differences (two FMAs, two exp2 and a subtraction each).  Timing the
+ * launch gives the dense bf16 rate the part sustains under that load, beside the published
+ * peak the roofline is quoted against.  sink: device buffer of workgroups *
+ * LARD_PROBE_THREADS floats, written with values that depend on every result.  Returns
+ * LARD_ERR_INVALID_ARGUMENT for a null sink, iters outside [1, 2^20], workgroups outside
+ * [1, 2^16] or vector_work other than 0 or 1; LARD_ERR_HIP if the launch fails.
+ */
+#define LARD_PROBE_THREADS 512
+#define LARD_PROBE_MFMA_PER_ITER 24
+lard_status lard_probe_mfma(int vector_work, int iters, int workgroups, float* sink,
+                            void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* lard_status_string(lard_status status);
 

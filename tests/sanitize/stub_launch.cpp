@@ -9,6 +9,7 @@ int launch_fwd(const FwdLaunch&, bool, int, bool, const LossOut&, void*, bool) {
 int launch_bwd(const BwdLaunch&, bool, int, bool, bool, void*, int) { return 1; }
 int launch_splitk_reduce(const ReduceLaunch&, bool, void*) { return 1; }
 int launch_rope_prep(const PrepLaunch&, bool, int, void*, bool) { return 1; }
+int launch_probe_mfma(bool, int, int, float*, void*) { return 1; }
 int scratch_address(void** out) {
   *out = nullptr;
   return 1;

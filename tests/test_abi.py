@@ -205,6 +205,22 @@ def test_fault_injection_maps_to_hip_error(lib, monkeypatch):
     assert ei.value.status == HIP
 
 
+def test_mfma_probe_validation(lib):
+    """The throughput probe checks its arguments on the host; a valid request reaches the
+    launch wrapper, which the fixture tells to fail."""
+    assert lib.lard_probe_mfma(0, 10, 256, None, None) == INVALID
+    assert lib.lard_probe_mfma(2, 10, 256, FAKE, None) == INVALID
+    assert lib.lard_probe_mfma(0, 0, 256, FAKE, None) == INVALID
+    assert lib.lard_probe_mfma(0, (1 << 20) + 1, 256, FAKE, None) == INVALID
+    assert lib.lard_probe_mfma(1, 10, 0, FAKE, None) == INVALID
+    assert lib.lard_probe_mfma(1, 10, (1 << 16) + 1, FAKE, None) == INVALID
+    assert lib.lard_probe_mfma(0, 10, 256, FAKE + 2, None) == INVALID  # misaligned sink
+    assert lib.lard_probe_mfma(0, 10, 256, FAKE, None) == HIP
+    assert lib.lard_probe_mfma(1, 1 << 20, 1 << 16, FAKE, None) == HIP
+    with pytest.raises(RuntimeError, match="GPU"):
+        relkl.probe_mfma(False, 10, 1, torch.zeros(512))
+
+
 def test_python_layer_refuses_cpu_tensors():
     x = torch.zeros(1, 1, 8, 64)
     with pytest.raises(RuntimeError, match="GPU"):

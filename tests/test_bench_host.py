@@ -32,6 +32,15 @@ def test_alg_flops_counts_kept_entries(bench, causal, N, d):
     assert bwd == 2 * fwd
 
 
+def test_executed_backward_flops_match_the_counted_mfmas(bench):
+    # SQ_INSTS_MFMA of one backward dispatch at 32 heads x 32K (the committed counter run):
+    # 8.056e8 wave-level MFMAs of 32x32x16 (32768 flops each)
+    ex = bench.executed_bwd_flops(1, 32, 32768, 128)
+    assert abs(ex / 32768 - 8.056e8) / 8.056e8 < 1e-3
+    _, alg = bench.alg_flops(1, 32, 32768, 128, True)
+    assert 1.49 < ex / alg < 1.51  # full-row ownership: 6 units executed for 4 algorithmic
+
+
 def _recorded_digest(path, key):
     with open(os.path.join(ROOT, path)) as f:
         m = re.search(key + r".*source_sha256=([0-9a-f]+)", f.read())
