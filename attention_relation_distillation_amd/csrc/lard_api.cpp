@@ -11,6 +11,7 @@
 #include <string.h>
 
 #include "lard.h"
+#include "probe_internal.h"
 #include "relkl_internal.h"
 
 namespace {

@@ -13,7 +13,8 @@
 #include <hip/hip_runtime.h>
 #include <stdlib.h>
 
-#include "relkl_internal.h"
+#include "lard.h"
+#include "probe_internal.h"
 
 namespace lard {
 namespace {

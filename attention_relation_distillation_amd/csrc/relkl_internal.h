@@ -169,7 +169,4 @@ int launch_rope_prep(const PrepLaunch& a, bool in_bf16, int d, void* stream, boo
 constexpr int64_t kNoallocMaxPartials = LARD_NOALLOC_MAX_PARTIALS;
 int scratch_address(void** out);
 
-// Matrix-core throughput probe (mfma_probe.hip): a hipError_t value, 0 on success.
-int launch_probe_mfma(bool vector_work, int iters, int workgroups, float* sink, void* stream);
-
 }  // namespace lard

@@ -1,6 +1,7 @@
 // Host-only stand-ins for the device launchers of liblard.so, for a sanitizer build of the
 // C-ABI layer (lard_api.cpp) on a machine without a GPU: every launch reports a failure,
 // which the entry points map to LARD_ERR_HIP.  Test infrastructure only.
+#include "probe_internal.h"
 #include "relkl_internal.h"
 
 namespace lard {
