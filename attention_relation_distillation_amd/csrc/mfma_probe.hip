@@ -5,12 +5,14 @@
 // hold 2.4 GHz, so the rate a perfect kernel could reach on the box is lower.  This probe
 // measures it: every SIMD runs two waves (the relation backward's occupancy), each issuing
 // independent v_mfma_f32_32x32x16_bf16 on four accumulator chains with operands in
-// registers.  With vector_work = 1 each group of four MFMAs also carries the vector work of
+// registers, cycled through eight pseudo-random fragments so that the matrix cores switch as
+// they do on real data (the part is power-limited: constant operands would run faster).  With vector_work = 1 each group of four MFMAs also carries the vector work of
 // one backward probability step per element (two FMAs, two exp2, a subtraction) for four
 // elements, as in the backward's W tiles, so the figure includes the power drawn by that
 // work beside the matrix cores.  The result is written to `sink` so that nothing is elided.
 
 #include <hip/hip_runtime.h>
+#include <stdint.h>
 #include <stdlib.h>
 
 #include "lard.h"
@@ -25,6 +27,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kProbeThreads = LARD_PROBE_THREADS;           // 8 waves: two per SIMD
 constexpr int kProbeGroups = LARD_PROBE_MFMA_PER_ITER / 4;  // groups of four MFMAs per iteration
 constexpr int kProbeLdsFloats = 96 * 1024 / 4;
+constexpr int kProbeFrags = 8;  // operand fragments cycled through
 
 template <bool VEC>
 __global__ __launch_bounds__(kProbeThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -33,11 +36,25 @@ void mfma_probe_kernel(float* sink, int iters, float c) {
   __shared__ float occupancy[kProbeLdsFloats];
   const int lane = threadIdx.x & 63;
   occupancy[threadIdx.x] = c;
-  bf16x8 a, b;
+  // eight A and eight B fragments of pseudo-random N(0,1)-like bf16 values, cycled so that
+  // consecutive MFMAs see different operands (the multipliers switch as with real data)
+  bf16x8 a[kProbeFrags], b[kProbeFrags];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    a[e] = (__bf16)(0.001f * (float)(lane + e));
-    b[e] = (__bf16)(0.002f * (float)(lane - e));
+  for (int f = 0; f < kProbeFrags; ++f) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint32_t h = (uint32_t)(threadIdx.x * 131 + f * 17 + e) * 2654435761u;
+      h ^= h >> 15;
+      h *= 2246822519u;
+      h ^= h >> 13;
+      // sum of four uniform bytes, centred: roughly normal with unit variance
+      const float u = (float)((h & 255) + ((h >> 8) & 255) + ((h >> 16) & 255) + (h >> 24));
+      a[f][e] = (__bf16)((u - 510.0f) * (1.0f / 147.8f));
+      h = h * 2654435761u + 12345u;
+      h ^= h >> 16;
+      const float w = (float)((h & 255) + ((h >> 8) & 255) + ((h >> 16) & 255) + (h >> 24));
+      b[f][e] = (__bf16)((w - 510.0f) * (1.0f / 147.8f));
+    }
   }
   f32x16 acc0 = {}, acc1 = {}, acc2 = {}, acc3 = {};
   float v[16];
@@ -46,10 +63,10 @@ void mfma_probe_kernel(float* sink, int iters, float c) {
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
     for (int k = 0; k < kProbeGroups; ++k) {
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, acc1, 0, 0, 0);
-      acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, a, acc2, 0, 0, 0);
-      acc3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, b, acc3, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[(4 * k) % kProbeFrags], b[(4 * k + 1) % kProbeFrags], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[(4 * k + 1) % kProbeFrags], b[(4 * k + 3) % kProbeFrags], acc1, 0, 0, 0);
+      acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[(4 * k + 2) % kProbeFrags], b[(4 * k + 5) % kProbeFrags], acc2, 0, 0, 0);
+      acc3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[(4 * k + 3) % kProbeFrags], b[(4 * k + 7) % kProbeFrags], acc3, 0, 0, 0);
       if constexpr (VEC) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {

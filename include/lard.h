@@ -375,7 +375,7 @@ lard_status lard_relkl_fwd_noalloc(const lard_relkl_desc* desc, const void* x_te
  * kernel of `workgroups` workgroups of LARD_PROBE_THREADS threads (two waves per SIMD when
  * one workgroup runs per CU, the relation backward's occupancy), in which every wave issues
  * iters * LARD_PROBE_MFMA_PER_ITER independent v_mfma_f32_32x32x16_bf16 (32768 flops each)
- * with register operands.  vector_work = 1 adds, per four MFMAs, the vector work of four
+ * with register operands that change from one MFMA to the next (pseudo-random bf16 values).  vector_work = 1 adds, per four MFMAs, the vector work of four
  * backward probability differences (two FMAs, two exp2 and a subtraction each).  Timing the
  * launch gives the dense bf16 rate the part sustains under that load, beside the published
  * peak the roofline is quoted against.  sink: device buffer of workgroups *
