@@ -44,6 +44,8 @@ lard_status check_desc(const lard_relkl_desc* d) {
   if (d->dtype != LARD_FP32 && d->dtype != LARD_BF16) return LARD_ERR_INVALID_ARGUMENT;
   if (d->B < 1 || d->H_in < 1 || d->N < 1 || d->d < 1) return LARD_ERR_INVALID_ARGUMENT;
   if (d->d != 64 && d->d != 128) return LARD_ERR_UNSUPPORTED;
+  // row and key indices are 32-bit in the kernels, with a tile's width added to them
+  if (d->N > LARD_MAX_N) return LARD_ERR_UNSUPPORTED;
   if (d->causal != 0 && d->causal != 1) return LARD_ERR_INVALID_ARGUMENT;
   if (!(d->scale > 0.0f) || !isfinite(d->scale)) return LARD_ERR_INVALID_ARGUMENT;
   if (d->H < 1) return LARD_ERR_INVALID_ARGUMENT;
@@ -72,16 +74,18 @@ lard_status check_desc(const lard_relkl_desc* d) {
   }
   // 32-bit work indices
   const int64_t units = (int64_t)d->B * d->H;
-  const int64_t row_tiles = (d->N + kBR - 1) / kBR;
+  const int64_t row_tiles = ((int64_t)d->N + kBR - 1) / kBR;
   if (units * row_tiles * kMaxSplits > 0x7fffffffLL) return LARD_ERR_UNSUPPORTED;
   if ((int64_t)units * d->N > 0x7fffffffLL * 4LL) return LARD_ERR_UNSUPPORTED;
   return LARD_OK;
 }
 
-int row_tiles_of(const lard_relkl_desc* d) { return (d->N + kBR - 1) / kBR; }
+int row_tiles_of(const lard_relkl_desc* d) { return (int)(((int64_t)d->N + kBR - 1) / kBR); }
 int bwd_rows_of(const lard_relkl_desc* d) { return bwd_rows(d->dtype == LARD_FP32); }
-int bwd_row_tiles_of(const lard_relkl_desc* d) { return (d->N + bwd_rows_of(d) - 1) / bwd_rows_of(d); }
-int key_tiles_of(const lard_relkl_desc* d) { return (d->N + kBC - 1) / kBC; }
+int bwd_row_tiles_of(const lard_relkl_desc* d) {
+  return (int)(((int64_t)d->N + bwd_rows_of(d) - 1) / bwd_rows_of(d));
+}
+int key_tiles_of(const lard_relkl_desc* d) { return (int)(((int64_t)d->N + kBC - 1) / kBC); }
 int64_t units_of(const lard_relkl_desc* d) { return (int64_t)d->B * d->H; }
 
 // Split the key range of the backward when the (unit, row tile) workgroups of a launch

@@ -66,6 +66,9 @@ typedef enum lard_status {
 
 typedef enum lard_dtype { LARD_FP32 = 0, LARD_BF16 = 1 } lard_dtype;
 
+/* Largest sequence length N (rows per head); longer descriptors return LARD_ERR_UNSUPPORTED. */
+#define LARD_MAX_N (1 << 30)
+
 /* Largest number of relation heads one call may compute (length of head_map). */
 #define LARD_MAX_HEADS 256
 
@@ -76,7 +79,7 @@ typedef enum lard_dtype { LARD_FP32 = 0, LARD_BF16 = 1 } lard_dtype;
  * Problem descriptor.  Teacher and student are [B, H_in, N, d] tensors of the same dtype
  * with element strides (stride over d must be 1, i.e. each row of d elements is
  * contiguous).  Requirements checked by every entry point:
- *   B >= 1, H_in >= 1, N >= 1, d in {64, 128};
+ *   B >= 1, H_in >= 1, 1 <= N <= LARD_MAX_N, d in {64, 128};
  *   all strides >= 0 and multiples of 8 (bf16) or 4 (fp32) elements, so that every row
  *   starts on a 16-byte boundary; x pointers 16-byte aligned;
  *   for N > 1: t_stride_n, s_stride_n >= d, and their byte sizes below 2^24 (16 MiB;

@@ -119,6 +119,8 @@ def test_workspace_sizes(lib):
     (dict(t_stride_n=64), INVALID),       # rows overlap (stride over n < d)
     (dict(s_stride_n=1 << 23), UNSUPPORTED),  # bf16 row stride of 16 MiB: beyond 24-bit offsets
     (dict(t_stride_n=(1 << 23) - 8, s_stride_n=128), "ok"),  # just below the limit
+    (dict(N=(1 << 30) + 1), UNSUPPORTED),  # beyond LARD_MAX_N (32-bit row indices in the kernels)
+    (dict(N=0x7fffffff), UNSUPPORTED),     # no overflow in the sizing of the largest int32 N
 ])
 def test_descriptor_validation(lib, kw, code):
     desc = good_desc(**kw)
@@ -131,6 +133,15 @@ def test_descriptor_validation(lib, kw, code):
     assert st == code
     assert fwd(lib, desc) == code
     assert bwd(lib, desc) == code
+
+
+def test_longest_sequence_is_sized_without_overflow(lib):
+    n = 1 << 30  # LARD_MAX_N
+    desc = good_desc(N=n, H_in=1, H=1, t_stride_h=n * 128, s_stride_h=n * 128,
+                     t_stride_b=n * 128, s_stride_b=n * 128)
+    ws, st = ws_query(lib, desc, 0)
+    assert st == OK
+    assert ws == 8 * (n // 128)  # one fp64 loss partial per 128-row forward workgroup
 
 
 def test_head_map_validation(lib):
