@@ -194,7 +194,11 @@ def _make_desc(x_t: torch.Tensor, x_s: torch.Tensor, causal: bool, scale: Option
     b, h_in, n, d = x_t.shape
     keep = []
     if head_map is not None:
-        arr = (ctypes.c_int32 * len(head_map))(*[int(v) for v in head_map])
+        vals = [int(v) for v in head_map]
+        if any(v < 0 or v >= h_in for v in vals):
+            # checked here too: ctypes would wrap values beyond int32 into valid head indices
+            raise LardError(1, f"head_map entries must lie in [0, {h_in})")
+        arr = (ctypes.c_int32 * len(vals))(*vals)
         keep.append(arr)
         hm_ptr = ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32))
         h = len(head_map)

@@ -232,6 +232,17 @@ def test_mfma_probe_validation(lib):
         relkl.probe_mfma(False, 10, 1, torch.zeros(512))
 
 
+def test_python_layer_range_checks_head_map():
+    """Head indices beyond int32 would wrap into valid ones in the ctypes array: the binding
+    rejects every entry outside [0, H_in) itself."""
+    x = torch.zeros(1, 4, 8, 64)
+    for bad in ([2 ** 32], [-1], [4], [0, 2 ** 33 + 1]):
+        with pytest.raises(relkl.LardError):
+            relkl._make_desc(x, x, True, None, bad)
+    desc, keep = relkl._make_desc(x, x, True, None, [3, 1])
+    assert desc.H == 2 and desc.head_map[0] == 3 and desc.head_map[1] == 1
+
+
 def test_python_layer_refuses_cpu_tensors():
     x = torch.zeros(1, 1, 8, 64)
     with pytest.raises(RuntimeError, match="GPU"):
